@@ -1,0 +1,105 @@
+"""CPU oracle for the Lightning Indexer (score + top-k), loaded through ctypes.
+
+TEST INFRASTRUCTURE: only the test suite, the smoke check and the benchmark's
+CPU-baseline leg may import this package. It shares no code with the HIP
+library; the two meet only in the seeded inputs of ``workloads``.
+
+The arithmetic lives in ``ds4idx_oracle.c`` (plain C, fp64, OpenMP over rows
+and key blocks); this wrapper only builds it with gcc and marshals arrays.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ds4idx_oracle.c")
+_LIB = os.path.join(_HERE, "libds4idx_oracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (-O2, OpenMP)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-std=c11",
+                               "-Wall", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build(force=False)
+        lib = ctypes.CDLL(_LIB)
+        p, i, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+        lib.ds4o_e4m3_decode.argtypes = [i]
+        lib.ds4o_e4m3_decode.restype = ctypes.c_double
+        lib.ds4o_select.argtypes = [p, i, p, i, p, p, i, i, i, i, i, i64, i,
+                                    p, i, p, p, p, p, i]
+        lib.ds4o_select.restype = i
+        lib.ds4o_score_pairs.argtypes = [p, i, p, i, p, p, i, i, i, i, i, i64,
+                                         p, p, i64, p, i]
+        lib.ds4o_score_pairs.restype = i
+        _lib = lib
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def e4m3_decode(code: int) -> float:
+    return _load().ds4o_e4m3_decode(int(code))
+
+
+def _problem_args(wl):
+    q = np.ascontiguousarray(wl.q)
+    k = np.ascontiguousarray(wl.k)
+    ks = None if wl.k_scale is None else np.ascontiguousarray(wl.k_scale, dtype=np.float32)
+    w = np.ascontiguousarray(wl.w, dtype=np.float32)
+    keep = (q, k, ks, w)
+    args = [_ptr(q), wl.q_dtype, _ptr(k), wl.k_dtype, _ptr(ks), _ptr(w),
+            wl.B, wl.T, wl.S, wl.H, wl.D, wl.offset]
+    return keep, args
+
+
+def select(wl, rows=None, topk=None, nthreads: int = 0):
+    """Oracle top-k for flat rows (b*T + t) of a workload.
+
+    Returns (idx int32 [n, k] ascending/-1 padded, val float64 [n, k],
+    kth float64 [n], rms float64 [n], threads_used).
+    """
+    lib = _load()
+    topk = wl.topk if topk is None else topk
+    rows = np.arange(wl.B * wl.T, dtype=np.int64) if rows is None else \
+        np.ascontiguousarray(rows, dtype=np.int64)
+    n = len(rows)
+    idx = np.empty((n, topk), dtype=np.int32)
+    val = np.empty((n, topk), dtype=np.float64)
+    kth = np.empty(n, dtype=np.float64)
+    rms = np.empty(n, dtype=np.float64)
+    keep, args = _problem_args(wl)
+    used = lib.ds4o_select(*args, topk, _ptr(rows), n, _ptr(idx), _ptr(val), _ptr(kth),
+                           _ptr(rms), nthreads)
+    if used < 0:
+        raise ValueError("oracle rejected the problem shape")
+    del keep
+    return idx, val, kth, rms, used
+
+
+def score_pairs(wl, rows, keys, nthreads: int = 0) -> np.ndarray:
+    """Oracle scores at (row, key) pairs; NaN where the key is not visible."""
+    lib = _load()
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    keys = np.ascontiguousarray(keys, dtype=np.int64)
+    out = np.empty(len(rows), dtype=np.float64)
+    keep, args = _problem_args(wl)
+    if lib.ds4o_score_pairs(*args, _ptr(rows), _ptr(keys), len(rows), _ptr(out), nthreads) < 0:
+        raise ValueError("oracle rejected the problem shape")
+    del keep
+    return out

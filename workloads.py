@@ -1,0 +1,240 @@
+"""Seeded synthetic inputs for the Lightning Indexer (score + top-k) workloads.
+
+This module is the only code shared by the HIP path's tests/bench and the CPU
+oracle. It generates input bytes and nothing else: it holds none of the
+indexer's arithmetic (no scoring, no selection). The one transformation it
+applies is the storage encoding of the inputs themselves:
+
+* bf16 tensors are float32 draws rounded to nearest-even bf16 (torch's cast);
+* fp8 key caches are OCP E4M3FN codes with one positive fp32 scale per key
+  token: scale[s] = max(amax_s, 2^-126) / 448 and code = E4M3(RNE(clamp(k /
+  scale, -448, 448))), the cast done by torch's ``float8_e4m3fn``.  The FP8
+  format is OCP E4M3 (bias 7, max 448, NaN = S.1111.111), never the FNUZ
+  variant whose reading of the same bits is off by 2x (the MI300X write-up,
+  section on the FP8 format mismatch of the indexer cache).
+
+The five workloads follow the shapes the pages' measurements revolve around
+(64k cold prefill, 256k decode, the 1M window; first page, TL;DR and section
+details; fourth page, performance table):
+
+=========  ==========================================================================
+tiny       T=S=1024, H=4, D=64, k=512; fp32 Q/K integers uniform in [-3,3];
+           head weights in {0.5, 1, 2}. Every fp32 sum is exact.
+8k         T=S=8192, H=64, D=128, k=512; bf16 Q/K = bf16(N(0,1)*0.25);
+           w = N(0,1)*H^-0.5 (fp32).
+8k-int     as 8k, Q/K integers uniform in [-4,4] (bf16, exact); w in {0.5,1,2}.
+64k        T=S=65536 in 16 chunks of 4096 queries (chunk c: offset 4096c, S=4096(c+1));
+           Q bf16(N(0,1)); K fp8 E4M3 + per-token scale of N(0,1) rows;
+           w = N(0,1)*H^-0.5.
+decode     8 independent streams, T=1, S=262144, offset 262143; Q/K/w as 64k.
+1m         T=2048 after 1,046,528 cached tokens (S=1,048,576, offset=1,046,528).
+=========  ==========================================================================
+
+Random numbers: numpy ``Generator(PCG64(SeedSequence(seed)))`` with one
+spawned child stream per tensor, so every tensor is reproducible on its own.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import List, Optional, Tuple
+
+import numpy as np
+import torch
+
+F32, BF16, FP8 = 0, 1, 2
+DTYPE_NAMES = {F32: "f32", BF16: "bf16", FP8: "fp8_e4m3"}
+
+E4M3_MAX = 448.0
+
+
+@dataclasses.dataclass
+class Workload:
+    """Host arrays for one indexer problem (row-major, contiguous).
+
+    q:       [B, T, H, D]  float32, or uint16 holding bf16 bits
+    k:       [B, S, D]     float32, uint16 (bf16 bits) or uint8 (E4M3 codes)
+    k_scale: [B, S]        float32 (fp8 keys only) else None
+    w:       [B, T, H]     float32
+    Query t of batch b sees keys s <= offset + t.
+    """
+    name: str
+    q: np.ndarray
+    k: np.ndarray
+    k_scale: Optional[np.ndarray]
+    w: np.ndarray
+    B: int
+    T: int
+    S: int
+    H: int
+    D: int
+    offset: int
+    topk: int
+    q_dtype: int
+    k_dtype: int
+    # Calls that make up one pass: (t0, T_c, S_c, offset_c). Chunk c sees the
+    # cache filled so far, S_c = offset_c + T_c.
+    chunks: List[Tuple[int, int, int, int]]
+    integer_valued: bool = False
+
+    def nbytes(self) -> int:
+        n = self.q.nbytes + self.k.nbytes + self.w.nbytes
+        if self.k_scale is not None:
+            n += self.k_scale.nbytes
+        return n
+
+
+def _streams(seed: int, n: int):
+    ss = np.random.SeedSequence(seed)
+    return [np.random.Generator(np.random.PCG64(c)) for c in ss.spawn(n)]
+
+
+def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 to bf16 (nearest-even, torch's cast); return the uint16 bits."""
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Widen bf16 bits to float32 (exact)."""
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+def quantize_e4m3_per_token(x: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Per-token OCP E4M3 encoding of a key cache x[..., S, D] (float32).
+
+    Returns (codes uint8 [..., S, D], scale float32 [..., S]) with
+    scale = max(amax, 2^-126) / 448 and codes = E4M3(clamp(x / scale)).
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    amax = np.abs(x).max(axis=-1)
+    scale = (np.maximum(amax, np.float32(2.0 ** -126)) / np.float32(E4M3_MAX)).astype(np.float32)
+    t = torch.from_numpy(x) / torch.from_numpy(scale)[..., None]
+    t = t.clamp_(-E4M3_MAX, E4M3_MAX)
+    codes = t.to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
+    return codes, scale
+
+
+def _int_uniform(g, shape, lo, hi):
+    return g.integers(lo, hi + 1, size=shape, dtype=np.int64).astype(np.float32)
+
+
+def _pick_weights(g, shape):
+    return np.array([0.5, 1.0, 2.0], dtype=np.float32)[g.integers(0, 3, size=shape)]
+
+
+def tiny(seed: int = 1, T: int = 1024, S: int = 1024, H: int = 4, D: int = 64,
+         topk: int = 512, offset: int = 0) -> Workload:
+    gq, gk, gw = _streams(seed, 3)
+    q = _int_uniform(gq, (1, T, H, D), -3, 3)
+    k = _int_uniform(gk, (1, S, D), -3, 3)
+    w = _pick_weights(gw, (1, T, H))
+    return Workload("tiny", q, k, None, w, 1, T, S, H, D, offset, topk, F32, F32,
+                    [(0, T, S, offset)], integer_valued=True)
+
+
+def prefill_bf16(seed: int = 2, T: int = 8192, S: int = 8192, H: int = 64, D: int = 128,
+                 topk: int = 512, offset: int = 0, B: int = 1, name: str = "8k") -> Workload:
+    gq, gk, gw = _streams(seed, 3)
+    q = to_bf16_bits(gq.standard_normal((B, T, H, D), dtype=np.float32) * np.float32(0.25))
+    k = to_bf16_bits(gk.standard_normal((B, S, D), dtype=np.float32) * np.float32(0.25))
+    w = gw.standard_normal((B, T, H), dtype=np.float32) * np.float32(H ** -0.5)
+    return Workload(name, q, k, None, w, B, T, S, H, D, offset, topk, BF16, BF16,
+                    [(0, T, S, offset)])
+
+
+def prefill_bf16_int(seed: int = 102, T: int = 8192, S: int = 8192, H: int = 64, D: int = 128,
+                     topk: int = 512, offset: int = 0, B: int = 1,
+                     name: str = "8k-int") -> Workload:
+    gq, gk, gw = _streams(seed, 3)
+    q = to_bf16_bits(_int_uniform(gq, (B, T, H, D), -4, 4))
+    k = to_bf16_bits(_int_uniform(gk, (B, S, D), -4, 4))
+    w = _pick_weights(gw, (B, T, H))
+    return Workload(name, q, k, None, w, B, T, S, H, D, offset, topk, BF16, BF16,
+                    [(0, T, S, offset)], integer_valued=True)
+
+
+def _fp8_cache(gk, B, S, D, block=1 << 20):
+    codes = np.empty((B, S, D), dtype=np.uint8)
+    scale = np.empty((B, S), dtype=np.float32)
+    for b in range(B):
+        for s0 in range(0, S, block):
+            s1 = min(S, s0 + block)
+            x = gk.standard_normal((s1 - s0, D), dtype=np.float32)
+            codes[b, s0:s1], scale[b, s0:s1] = quantize_e4m3_per_token(x)
+    return codes, scale
+
+
+def prefill_fp8(seed: int = 3, T: int = 65536, S: int = 65536, H: int = 64, D: int = 128,
+                topk: int = 512, offset: int = 0, B: int = 1, chunk: int = 4096,
+                name: str = "64k") -> Workload:
+    """Causal prefill of T queries in chunks against an fp8 cache that already
+    holds the offset earlier tokens; chunk c covers queries [c*chunk, (c+1)*chunk)."""
+    gq, gk, gw = _streams(seed, 3)
+    q = to_bf16_bits(gq.standard_normal((B, T, H, D), dtype=np.float32))
+    codes, scale = _fp8_cache(gk, B, S, D)
+    w = gw.standard_normal((B, T, H), dtype=np.float32) * np.float32(H ** -0.5)
+    chunks = []
+    for t0 in range(0, T, chunk):
+        tc = min(chunk, T - t0)
+        chunks.append((t0, tc, offset + t0 + tc, offset + t0))
+    return Workload(name, q, codes, scale, w, B, T, S, H, D, offset, topk, BF16, FP8, chunks)
+
+
+def decode(seed: int = 4, B: int = 8, S: int = 262144, H: int = 64, D: int = 128,
+           topk: int = 512, T: int = 1, name: str = "decode") -> Workload:
+    gq, gk, gw = _streams(seed, 3)
+    q = to_bf16_bits(gq.standard_normal((B, T, H, D), dtype=np.float32))
+    codes, scale = _fp8_cache(gk, B, S, D)
+    w = gw.standard_normal((B, T, H), dtype=np.float32) * np.float32(H ** -0.5)
+    off = S - T
+    return Workload(name, q, codes, scale, w, B, T, S, H, D, off, topk, BF16, FP8,
+                    [(0, T, S, off)])
+
+
+def long_prefill(seed: int = 5, T: int = 2048, S: int = 1048576, H: int = 64, D: int = 128,
+                 topk: int = 512, name: str = "1m") -> Workload:
+    gq, gk, gw = _streams(seed, 3)
+    q = to_bf16_bits(gq.standard_normal((1, T, H, D), dtype=np.float32))
+    codes, scale = _fp8_cache(gk, 1, S, D)
+    w = gw.standard_normal((1, T, H), dtype=np.float32) * np.float32(H ** -0.5)
+    off = S - T
+    return Workload(name, q, codes, scale, w, 1, T, S, H, D, off, topk, BF16, FP8,
+                    [(0, T, S, off)])
+
+
+CONFIGS = {
+    "tiny": tiny,
+    "8k": prefill_bf16,
+    "8k-int": prefill_bf16_int,
+    "64k": prefill_fp8,
+    "decode": decode,
+    "1m": long_prefill,
+}
+
+
+def make(name: str, **kw) -> Workload:
+    return CONFIGS[name](**kw)
+
+
+def sample_rows(wl: Workload, n: int, seed: int = 7) -> np.ndarray:
+    """A bounded, seeded set of flat row ids (b*T + t) that always contains the
+    first and last query of every chunk, the short rows around t = k-1 when the
+    first chunk starts at offset 0, and the rest drawn uniformly."""
+    fixed = set()
+    for b in range(wl.B):
+        for (t0, tc, _s, _o) in wl.chunks:
+            fixed.add(b * wl.T + t0)
+            fixed.add(b * wl.T + t0 + tc - 1)
+        if wl.offset == 0:
+            for t in (wl.topk - 2, wl.topk - 1, wl.topk):
+                if 0 <= t < wl.T:
+                    fixed.add(b * wl.T + t)
+    rows = sorted(fixed)
+    g = np.random.Generator(np.random.PCG64(seed))
+    total = wl.B * wl.T
+    while len(rows) < min(n, total):
+        r = int(g.integers(0, total))
+        if r not in fixed:
+            fixed.add(r)
+            rows.append(r)
+    return np.array(sorted(rows), dtype=np.int64)
