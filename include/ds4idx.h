@@ -1,0 +1,135 @@
+/*
+ * ds4idx — the Lightning Indexer of DeepSeek V4's sparse attention, as a C-ABI
+ * library of hand-written HIP kernels for AMD MI355X (gfx950).
+ *
+ * What it computes. For every query token the indexer scores all causally
+ * visible cached keys and keeps the positions worth attending to; the pages
+ * describe it as the step that dominates long-context prefill, made of a
+ * scorer and a top-512 selection (first page, "DeepSeek V4 Flash 추론을 1.6초로
+ * 줄인 ds4 최적화": glossary entry "Lightning Indexer"; section details, second
+ * paragraph). The score is the indexer's published form
+ *
+ *     score(t, s) = sum_h W[t,h] * max(0, sum_d Q[t,h,d] * K[s,d] * K_scale[s])
+ *
+ * and query t of a call, whose absolute position is causal_offset + t, sees the
+ * keys s <= causal_offset + t. The selection keeps the min(k, L) visible keys
+ * (L = causal_offset + t + 1) that come first in the strict order (score
+ * descending, index ascending): equal scores go to the lower index. Because the
+ * order is total, the answer is unique, as the pages' byte-identical outputs
+ * across kernel rewrites require (first page, TL;DR).
+ *
+ * Layouts (row-major, contiguous, device memory owned by the caller):
+ *   Q        [B, T, H, D]  fp32 or bf16                       16-byte aligned
+ *   K        [B, S, D]     fp32, bf16, or OCP E4M3FN codes    16-byte aligned
+ *   K_scale  [B, S]        fp32, positive finite; required for E4M3 keys
+ *                          (ignored, may be NULL, otherwise)
+ *   W        [B, T, H]     fp32 head weights
+ *   scores   [B, T, S]     fp32 (ds4idx_score output; -inf where s is masked)
+ *   idx      [B, T, k]     int32: selected key indices in ascending order,
+ *                          then -1 padding after min(k, L) entries
+ *   vals     [B, T, k]     fp32 scores of idx (-inf in padding); may be NULL
+ *
+ * FP8 keys are OCP E4M3FN (bias 7, max 448, NaN = S.1111.111, no infinities),
+ * never the FNUZ variant: the MI300X write-up ("DeepSeek V4 Flash는 단일 AMD
+ * MI300X에서 실행됩니다", section on the indexer cache's FP8 format mismatch)
+ * shows that mixing the two readings scales every key by 2.
+ *
+ * Calls are asynchronous on the HIP stream passed as `stream` (a hipStream_t;
+ * NULL = the default stream). The return value reports argument validation
+ * and launch errors only; device faults surface at the caller's next
+ * synchronisation. Every argument is validated before any HIP call is made.
+ * The library never allocates, frees or synchronises in these calls, keeps no
+ * pointer after returning, and is safe to call from several threads on
+ * different streams. Non-finite Q, K or W values give undefined (but
+ * memory-safe) results.
+ */
+#ifndef DS4IDX_H
+#define DS4IDX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DS4IDX_ABI_VERSION 1
+#define DS4IDX_MAX_TOPK 2048
+
+typedef enum {
+    DS4IDX_OK = 0,
+    DS4IDX_ERR_INVALID_ARG = 1, /* null pointer, bad size, misalignment, bad k */
+    DS4IDX_ERR_UNSUPPORTED = 2, /* shape/dtype with no kernel under the forced implementation */
+    DS4IDX_ERR_WORKSPACE = 3,   /* workspace NULL or smaller than ds4idx_workspace_bytes */
+    DS4IDX_ERR_HIP = 4          /* a HIP launch or query failed */
+} ds4idx_status;
+
+typedef enum {
+    DS4IDX_F32 = 0,
+    DS4IDX_BF16 = 1,
+    DS4IDX_FP8_E4M3 = 2 /* OCP E4M3FN codes, one byte each; keys only */
+} ds4idx_dtype;
+
+/* Problem shape shared by every entry point. All sizes >= 1, causal_offset
+ * >= 0 and causal_offset + T <= S (the cache already holds the new tokens).
+ * Key indices are int32, so S <= 2^31 - 1; internal offsets are 64-bit. */
+typedef struct {
+    int32_t B, T, S, H, D;
+    int64_t causal_offset;
+    int32_t q_dtype; /* ds4idx_dtype: F32 or BF16 */
+    int32_t k_dtype; /* ds4idx_dtype: F32, BF16 or FP8_E4M3 */
+} ds4idx_problem;
+
+enum { DS4IDX_OP_SCORE = 0, DS4IDX_OP_TOPK = 1, DS4IDX_OP_SELECT = 2 };
+
+/* Kernel family. AUTO: the MFMA kernels where the shape allows, the plain
+ * kernels otherwise. REF: the plain kernels for every shape. OPT: the MFMA
+ * kernels only; shapes they do not cover return DS4IDX_ERR_UNSUPPORTED.
+ * The pages keep each new kernel behind a rollback switch so the old path
+ * stays comparable (first page, practical advice, third paragraph); this is
+ * that switch. Its initial value comes from the environment variable
+ * DS4IDX_IMPL ("auto", "ref" or "opt"; default "auto"). */
+enum { DS4IDX_IMPL_AUTO = 0, DS4IDX_IMPL_REF = 1, DS4IDX_IMPL_OPT = 2 };
+
+/* ABI version of the loaded library (DS4IDX_ABI_VERSION). */
+int ds4idx_abi_version(void);
+
+/* Static, NUL-terminated description of a status code. Never NULL. */
+const char *ds4idx_status_string(int status);
+
+/* Select the kernel family for later calls in this process; returns the
+ * previous value, or -1 for an unknown value (then nothing changes). */
+int ds4idx_set_impl(int impl);
+int ds4idx_get_impl(void);
+
+/* Bytes of device workspace that `op` (DS4IDX_OP_*) needs for this problem
+ * and k under the current kernel family, or 0 if it needs none. Returns
+ * (size_t)-1 for an invalid problem. The workspace for DS4IDX_OP_SELECT must
+ * be zero-filled before its first use (it holds per-row arrival counters that
+ * every completed call leaves at zero again); 256-byte alignment required. */
+size_t ds4idx_workspace_bytes(const ds4idx_problem *p, int32_t k, int32_t op);
+
+/* Scorer only: scores[b,t,s] for every s in [0, S): the score of visible keys
+ * (s <= causal_offset + t) and -inf for the rest. */
+int ds4idx_score(const ds4idx_problem *p, const void *Q, const void *K, const float *K_scale,
+                 const float *W, float *scores, void *stream);
+
+/* Top-k over materialised scores [B,T,S] (only the visible prefix of each row,
+ * s <= causal_offset + t, is read). 1 <= k <= DS4IDX_MAX_TOPK. Uses no
+ * workspace (workspace may be NULL). */
+int ds4idx_topk(const ds4idx_problem *p, const float *scores, int32_t k, int32_t *idx,
+                float *vals, void *workspace, size_t ws_bytes, void *stream);
+
+/* Fused scorer + top-k: the indexer's hot path. Same outputs as
+ * ds4idx_score followed by ds4idx_topk, without materialising the scores
+ * when the MFMA kernels apply (H = 64, D = 128, bf16 Q, bf16 or E4M3 K,
+ * k <= 512). 1 <= k <= DS4IDX_MAX_TOPK. */
+int ds4idx_select(const ds4idx_problem *p, const void *Q, const void *K, const float *K_scale,
+                  const float *W, int32_t k, int32_t *idx, float *vals, void *workspace,
+                  size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DS4IDX_H */

@@ -1,0 +1,207 @@
+"""Python binding of libds4idx, the Lightning Indexer (score + top-k) for MI355X.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI of ``include/ds4idx.h``. PyTorch provides device
+memory and the current stream. There is no CPU fallback: if the library is
+not built, every call raises.
+
+    idx, vals = select(q, k, k_scale, w, causal_offset, topk=512)
+
+q [B,T,H,D] bf16/fp32, k [B,S,D] bf16/fp32 or uint8 OCP E4M3 codes (or
+torch.float8_e4m3fn), k_scale [B,S] fp32 for fp8 keys, w [B,T,H] fp32.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libds4idx.so")
+
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
+F32, BF16, FP8_E4M3 = 0, 1, 2
+OP_SCORE, OP_TOPK, OP_SELECT = 0, 1, 2
+IMPL_AUTO, IMPL_REF, IMPL_OPT = 0, 1, 2
+MAX_TOPK = 2048
+ABI_VERSION = 1
+
+# Every symbol include/ds4idx.h declares.
+EXPORTS = ("ds4idx_abi_version", "ds4idx_status_string", "ds4idx_set_impl", "ds4idx_get_impl",
+           "ds4idx_workspace_bytes", "ds4idx_score", "ds4idx_topk", "ds4idx_select")
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("T", ctypes.c_int32), ("S", ctypes.c_int32),
+                ("H", ctypes.c_int32), ("D", ctypes.c_int32), ("causal_offset", ctypes.c_int64),
+                ("q_dtype", ctypes.c_int32), ("k_dtype", ctypes.c_int32)]
+
+
+class Ds4idxError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C-ABI library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m sparse_attention_token_lightning_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, vp, i32, sz = ctypes.POINTER(Problem), ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        L.ds4idx_abi_version.argtypes = []
+        L.ds4idx_abi_version.restype = ctypes.c_int
+        L.ds4idx_status_string.argtypes = [ctypes.c_int]
+        L.ds4idx_status_string.restype = ctypes.c_char_p
+        L.ds4idx_set_impl.argtypes = [ctypes.c_int]
+        L.ds4idx_set_impl.restype = ctypes.c_int
+        L.ds4idx_get_impl.argtypes = []
+        L.ds4idx_get_impl.restype = ctypes.c_int
+        L.ds4idx_workspace_bytes.argtypes = [P, i32, i32]
+        L.ds4idx_workspace_bytes.restype = sz
+        L.ds4idx_score.argtypes = [P, vp, vp, vp, vp, vp, vp]
+        L.ds4idx_score.restype = ctypes.c_int
+        L.ds4idx_topk.argtypes = [P, vp, i32, vp, vp, vp, sz, vp]
+        L.ds4idx_topk.restype = ctypes.c_int
+        L.ds4idx_select.argtypes = [P, vp, vp, vp, vp, i32, vp, vp, vp, sz, vp]
+        L.ds4idx_select.restype = ctypes.c_int
+        if L.ds4idx_abi_version() != ABI_VERSION:
+            raise RuntimeError("libds4idx ABI version mismatch; rebuild the library")
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().ds4idx_status_string(int(status)).decode()
+
+
+def set_impl(impl) -> int:
+    """Select the kernel family ('auto', 'ref', 'opt' or IMPL_*); returns the previous one."""
+    if isinstance(impl, str):
+        impl = {"auto": IMPL_AUTO, "ref": IMPL_REF, "opt": IMPL_OPT}[impl]
+    prev = lib().ds4idx_set_impl(int(impl))
+    if prev < 0:
+        raise ValueError(f"unknown kernel family {impl}")
+    return prev
+
+
+def get_impl() -> int:
+    return lib().ds4idx_get_impl()
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _dtype_code(t: torch.Tensor, key: bool) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if key and t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return FP8_E4M3
+    raise TypeError(f"unsupported {'key' if key else 'query'} dtype {t.dtype}")
+
+
+def make_problem(q: torch.Tensor, k: torch.Tensor, causal_offset: int) -> Problem:
+    if q.dim() != 4 or k.dim() != 3:
+        raise ValueError("q must be [B,T,H,D] and k [B,S,D]")
+    B, T, H, D = q.shape
+    if k.shape[0] != B or k.shape[2] != D:
+        raise ValueError(f"k shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
+    return Problem(B, T, k.shape[1], H, D, int(causal_offset), _dtype_code(q, False),
+                   _dtype_code(k, True))
+
+
+def _check_inputs(q, k, k_scale, w):
+    for name, t in (("q", q), ("k", k), ("w", w)) + ((("k_scale", k_scale),) if k_scale is not None else ()):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    B, T, H, _ = q.shape
+    if w.dtype != torch.float32 or tuple(w.shape) != (B, T, H):
+        raise ValueError("w must be float32 [B,T,H]")
+    if k_scale is not None and (k_scale.dtype != torch.float32 or tuple(k_scale.shape) != tuple(k.shape[:2])):
+        raise ValueError("k_scale must be float32 [B,S]")
+
+
+def workspace_bytes(problem: Problem, k: int, op: int = OP_SELECT) -> int:
+    n = lib().ds4idx_workspace_bytes(ctypes.byref(problem), int(k), int(op))
+    if n == ctypes.c_size_t(-1).value:
+        raise Ds4idxError(ERR_INVALID_ARG, "ds4idx_workspace_bytes")
+    return n
+
+
+def new_workspace(problem: Problem, k: int, device=None) -> Optional[torch.Tensor]:
+    """A zero-filled device workspace big enough for ds4idx_select (or None)."""
+    n = workspace_bytes(problem, k, OP_SELECT)
+    if n == 0:
+        return None
+    return torch.zeros(n, dtype=torch.uint8, device=device or "cuda")
+
+
+def score(q, k, k_scale, w, causal_offset: int, out: Optional[torch.Tensor] = None,
+          stream=None) -> torch.Tensor:
+    """scores [B,T,S] fp32: the indexer score of every visible key, -inf elsewhere."""
+    _check_inputs(q, k, k_scale, w)
+    p = make_problem(q, k, causal_offset)
+    if out is None:
+        out = torch.empty((p.B, p.T, p.S), dtype=torch.float32, device=q.device)
+    st = lib().ds4idx_score(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(k_scale), _ptr(w), _ptr(out),
+                            _stream(stream))
+    if st != OK:
+        raise Ds4idxError(st, "ds4idx_score")
+    return out
+
+
+def topk(scores: torch.Tensor, k: int, causal_offset: int, idx: Optional[torch.Tensor] = None,
+         vals: Optional[torch.Tensor] = None, with_vals: bool = True,
+         stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Top-k (ascending indices, -1 padded) of materialised scores [B,T,S]."""
+    if scores.dtype != torch.float32 or scores.dim() != 3 or not scores.is_contiguous():
+        raise ValueError("scores must be contiguous float32 [B,T,S]")
+    B, T, S = scores.shape
+    p = Problem(B, T, S, 1, 1, int(causal_offset), F32, F32)
+    if idx is None:
+        idx = torch.empty((B, T, k), dtype=torch.int32, device=scores.device)
+    if vals is None and with_vals:
+        vals = torch.empty((B, T, k), dtype=torch.float32, device=scores.device)
+    st = lib().ds4idx_topk(ctypes.byref(p), _ptr(scores), int(k), _ptr(idx), _ptr(vals), None, 0,
+                           _stream(stream))
+    if st != OK:
+        raise Ds4idxError(st, "ds4idx_topk")
+    return idx, vals
+
+
+def select(q, k, k_scale, w, causal_offset: int, topk: int = 512,
+           idx: Optional[torch.Tensor] = None, vals: Optional[torch.Tensor] = None,
+           workspace: Optional[torch.Tensor] = None, with_vals: bool = True,
+           stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Fused indexer: (idx [B,T,topk] int32 ascending/-1 padded, vals fp32 or None)."""
+    _check_inputs(q, k, k_scale, w)
+    p = make_problem(q, k, causal_offset)
+    if idx is None:
+        idx = torch.empty((p.B, p.T, topk), dtype=torch.int32, device=q.device)
+    if vals is None and with_vals:
+        vals = torch.empty((p.B, p.T, topk), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = new_workspace(p, topk, q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().ds4idx_select(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(k_scale), _ptr(w), int(topk),
+                             _ptr(idx), _ptr(vals), _ptr(workspace), ws_bytes, _stream(stream))
+    if st != OK:
+        raise Ds4idxError(st, "ds4idx_select")
+    return idx, vals

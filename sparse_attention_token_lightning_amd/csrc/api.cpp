@@ -1,0 +1,190 @@
+// C-ABI entry points of libds4idx (declared in include/ds4idx.h): argument
+// validation (always before any HIP call), workspace sizing, and dispatch to
+// the MFMA kernels or the plain kernels.
+#include "../../include/ds4idx.h"
+
+#include <atomic>
+#include <cstdlib>
+#include <cstring>
+
+#include "kernels.h"
+
+using ds4idx::Problem;
+
+namespace {
+
+std::atomic<int> g_impl{-1};
+
+int impl_now()
+{
+    int v = g_impl.load(std::memory_order_relaxed);
+    if (v >= 0) return v;
+    int init = DS4IDX_IMPL_AUTO;
+    if (const char *e = std::getenv("DS4IDX_IMPL")) {
+        if (!std::strcmp(e, "ref")) init = DS4IDX_IMPL_REF;
+        else if (!std::strcmp(e, "opt")) init = DS4IDX_IMPL_OPT;
+    }
+    int expected = -1;
+    g_impl.compare_exchange_strong(expected, init);
+    return g_impl.load(std::memory_order_relaxed);
+}
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_problem(const ds4idx_problem *p)
+{
+    if (!p) return DS4IDX_ERR_INVALID_ARG;
+    if (p->B < 1 || p->T < 1 || p->S < 1 || p->H < 1 || p->D < 1) return DS4IDX_ERR_INVALID_ARG;
+    if (p->causal_offset < 0 || p->causal_offset + (int64_t)p->T > (int64_t)p->S)
+        return DS4IDX_ERR_INVALID_ARG;
+    if (p->q_dtype != DS4IDX_F32 && p->q_dtype != DS4IDX_BF16) return DS4IDX_ERR_INVALID_ARG;
+    if (p->k_dtype != DS4IDX_F32 && p->k_dtype != DS4IDX_BF16 && p->k_dtype != DS4IDX_FP8_E4M3)
+        return DS4IDX_ERR_INVALID_ARG;
+    // The grid's x dimension carries B*T rows (top-k) or B*T*key-blocks (scorer).
+    if ((int64_t)p->B * p->T > (int64_t)INT32_MAX) return DS4IDX_ERR_UNSUPPORTED;
+    return DS4IDX_OK;
+}
+
+int check_inputs(const ds4idx_problem *p, const void *Q, const void *K, const float *Ks,
+                 const float *W)
+{
+    if (!Q || !K || !W) return DS4IDX_ERR_INVALID_ARG;
+    if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(W, 4)) return DS4IDX_ERR_INVALID_ARG;
+    if (p->k_dtype == DS4IDX_FP8_E4M3 && (!Ks || !aligned(Ks, 4))) return DS4IDX_ERR_INVALID_ARG;
+    return DS4IDX_OK;
+}
+
+Problem to_internal(const ds4idx_problem *p)
+{
+    return Problem{p->B, p->T, p->S, p->H, p->D, (long long)p->causal_offset, p->q_dtype, p->k_dtype};
+}
+
+bool ref_shape_ok(const ds4idx_problem *p)
+{
+    if ((int64_t)p->H * p->D + p->H > ds4idx::kRefMaxQFloats) return false;
+    const int64_t key_blocks = ((int64_t)p->S + 1023) / 1024;
+    return (int64_t)p->B * p->T * key_blocks <= (int64_t)INT32_MAX;
+}
+
+// Which kernels a call takes: 1 = MFMA, 0 = plain, -1 = none under the forced family.
+int route_score(const ds4idx_problem *p)
+{
+    const Problem q = to_internal(p);
+    const int impl = impl_now();
+    const bool mf = ds4idx::mfma_shape_ok(q);
+    if (impl == DS4IDX_IMPL_OPT) return mf ? 1 : -1;
+    if (impl == DS4IDX_IMPL_AUTO && mf) return 1;
+    return ref_shape_ok(p) ? 0 : -1;
+}
+
+int route_select(const ds4idx_problem *p, int32_t k)
+{
+    const Problem q = to_internal(p);
+    const int impl = impl_now();
+    const bool mf = ds4idx::mfma_shape_ok(q) && k <= ds4idx::kMfmaMaxK;
+    if (impl == DS4IDX_IMPL_OPT) return mf ? 1 : -1;
+    if (impl == DS4IDX_IMPL_AUTO && mf) return 1;
+    return ref_shape_ok(p) ? 0 : -1;
+}
+
+size_t round_up(size_t n, size_t a) { return (n + a - 1) / a * a; }
+
+// Plain select path: materialised scores [B,T,S] fp32.
+size_t ref_select_bytes(const ds4idx_problem *p)
+{
+    return round_up((size_t)p->B * p->T * p->S * sizeof(float), 256);
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? DS4IDX_OK : DS4IDX_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int ds4idx_abi_version(void) { return DS4IDX_ABI_VERSION; }
+
+const char *ds4idx_status_string(int status)
+{
+    switch (status) {
+    case DS4IDX_OK: return "ok";
+    case DS4IDX_ERR_INVALID_ARG: return "invalid argument";
+    case DS4IDX_ERR_UNSUPPORTED: return "unsupported shape or dtype for the selected kernels";
+    case DS4IDX_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case DS4IDX_ERR_HIP: return "HIP launch or runtime error";
+    default: return "unknown status";
+    }
+}
+
+int ds4idx_set_impl(int impl)
+{
+    if (impl != DS4IDX_IMPL_AUTO && impl != DS4IDX_IMPL_REF && impl != DS4IDX_IMPL_OPT) return -1;
+    const int prev = impl_now();
+    g_impl.store(impl, std::memory_order_relaxed);
+    return prev;
+}
+
+int ds4idx_get_impl(void) { return impl_now(); }
+
+size_t ds4idx_workspace_bytes(const ds4idx_problem *p, int32_t k, int32_t op)
+{
+    if (check_problem(p) != DS4IDX_OK) return (size_t)-1;
+    if (op == DS4IDX_OP_SCORE || op == DS4IDX_OP_TOPK) return 0;
+    if (op != DS4IDX_OP_SELECT || k < 1 || k > DS4IDX_MAX_TOPK) return (size_t)-1;
+    const int r = route_select(p, k);
+    if (r == 0) return ref_select_bytes(p);
+    return 0;
+}
+
+int ds4idx_score(const ds4idx_problem *p, const void *Q, const void *K, const float *K_scale,
+                 const float *W, float *scores, void *stream)
+{
+    int st = check_problem(p);
+    if (st != DS4IDX_OK) return st;
+    if ((st = check_inputs(p, Q, K, K_scale, W)) != DS4IDX_OK) return st;
+    if (!scores || !aligned(scores, 4)) return DS4IDX_ERR_INVALID_ARG;
+    const int r = route_score(p);
+    if (r < 0) return DS4IDX_ERR_UNSUPPORTED;
+    const Problem q = to_internal(p);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (r == 1) return launch_status(ds4idx::launch_mfma_score(q, Q, K, K_scale, W, scores, s));
+    return launch_status(ds4idx::launch_score_ref(q, Q, K, K_scale, W, scores, s));
+}
+
+int ds4idx_topk(const ds4idx_problem *p, const float *scores, int32_t k, int32_t *idx, float *vals,
+                void *workspace, size_t ws_bytes, void *stream)
+{
+    (void)workspace;
+    (void)ws_bytes;
+    int st = check_problem(p);
+    if (st != DS4IDX_OK) return st;
+    if (k < 1 || k > DS4IDX_MAX_TOPK) return DS4IDX_ERR_INVALID_ARG;
+    if (!scores || !idx || !aligned(scores, 4) || !aligned(idx, 4) || (vals && !aligned(vals, 4)))
+        return DS4IDX_ERR_INVALID_ARG;
+    const Problem q = to_internal(p);
+    return launch_status(ds4idx::launch_topk_ref(q, scores, k, idx, vals, static_cast<hipStream_t>(stream)));
+}
+
+int ds4idx_select(const ds4idx_problem *p, const void *Q, const void *K, const float *K_scale,
+                  const float *W, int32_t k, int32_t *idx, float *vals, void *workspace,
+                  size_t ws_bytes, void *stream)
+{
+    int st = check_problem(p);
+    if (st != DS4IDX_OK) return st;
+    if ((st = check_inputs(p, Q, K, K_scale, W)) != DS4IDX_OK) return st;
+    if (k < 1 || k > DS4IDX_MAX_TOPK) return DS4IDX_ERR_INVALID_ARG;
+    if (!idx || !aligned(idx, 4) || (vals && !aligned(vals, 4))) return DS4IDX_ERR_INVALID_ARG;
+    const int r = route_select(p, k);
+    if (r < 0) return DS4IDX_ERR_UNSUPPORTED;
+    const size_t need = r == 0 ? ref_select_bytes(p) : 0;
+    if (need > 0 && (!workspace || !aligned(workspace, 256) || ws_bytes < need))
+        return DS4IDX_ERR_WORKSPACE;
+    const Problem q = to_internal(p);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (r == 1) return launch_status(ds4idx::launch_mfma_select(q, Q, K, K_scale, W, k, idx, vals, s));
+    float *sc = static_cast<float *>(workspace);
+    st = launch_status(ds4idx::launch_score_ref(q, Q, K, K_scale, W, sc, s));
+    if (st != DS4IDX_OK) return st;
+    return launch_status(ds4idx::launch_topk_ref(q, sc, k, idx, vals, s));
+}
+
+}  // extern "C"

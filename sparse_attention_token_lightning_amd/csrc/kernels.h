@@ -1,0 +1,34 @@
+// Internal interface between the C-ABI layer (api.cpp) and the HIP kernels.
+// Not installed; the public interface is include/ds4idx.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ds4idx {
+
+enum { F32 = 0, BF16 = 1, FP8 = 2 };
+
+struct Problem {
+    int B, T, S, H, D;
+    long long offset;  // query t sees keys s <= offset + t
+    int q_dtype, k_dtype;
+};
+
+// Plain kernels: any H, D and dtype (the rollback path).
+constexpr int kRefMaxQFloats = 16384;  // H*D + H floats of one query staged in LDS
+hipError_t launch_score_ref(const Problem &p, const void *Q, const void *K, const float *Ks,
+                            const float *W, float *scores, hipStream_t st);
+hipError_t launch_topk_ref(const Problem &p, const float *scores, int k, int *idx, float *vals,
+                           hipStream_t st);
+
+// MFMA kernels: H = 64, D = 128, bf16 queries, bf16 or E4M3 keys.
+constexpr int kMfmaH = 64, kMfmaD = 128, kMfmaMaxK = 512;
+bool mfma_shape_ok(const Problem &p);
+hipError_t launch_mfma_score(const Problem &p, const void *Q, const void *K, const float *Ks,
+                             const float *W, float *scores, hipStream_t st);
+hipError_t launch_mfma_select(const Problem &p, const void *Q, const void *K, const float *Ks,
+                              const float *W, int k, int *idx, float *vals, hipStream_t st);
+
+}  // namespace ds4idx

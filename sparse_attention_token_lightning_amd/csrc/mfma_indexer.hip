@@ -1,0 +1,387 @@
+// Lightning Indexer scorer + streaming top-k on gfx950 matrix cores.
+//
+// The pages' Metal kernels (a threadgroup-tiled scorer, a register-blocked
+// K-resident scorer and a streaming top-512 that replaced a bitonic sort and
+// merge cascade; first page, section details, first and second paragraphs)
+// are prior art for a different GPU. This kernel is laid out for CDNA4:
+//
+//  * Work split. A 256-thread workgroup owns 8 consecutive query tokens of one
+//    batch row; each of its four wavefronts owns two tokens and keeps their
+//    queries (2 tokens x 64 heads x 128 dims, bf16) resident in VGPRs as MFMA
+//    A operands for the whole key loop.
+//  * Keys. Tiles of 64 keys are staged global -> registers -> LDS, double
+//    buffered, once per workgroup. E4M3 codes are widened to bf16 on the way
+//    into LDS (exact: every E4M3 value is a bf16 value); the per-token fp32
+//    scale is kept aside and applied once to the head-reduced score (allowed
+//    since the scale is positive, so it commutes with the ReLU).
+//  * Contraction. Heads sit on the M dimension of v_mfma_f32_32x32x16_bf16:
+//    one token = two 32-row head blocks, 32 keys per block on N, 8 k-steps
+//    over D = 128. fp32 accumulation.
+//  * Epilogue in registers. Each lane holds 16 head rows of one key per
+//    block: ReLU, times w[t,h] (fp32), summed in-lane; the two lane halves
+//    hold disjoint head rows, and one v_permlane32_swap brings token 0's
+//    halves together in lanes 0-31 and token 1's in lanes 32-63. The causal
+//    mask (key <= offset + t) is applied per lane.
+//  * Streaming top-k per token. A candidate buffer of 1024 (score, index)
+//    slots per token lives in LDS. A score enters only if it beats the
+//    token's running threshold (ballot + mbcnt place it in ascending key
+//    order). When the buffer is nearly full, the wavefront finds the k-th
+//    largest key by radix selection over the buffer (four 8-bit digits of an
+//    order-preserving key) and compacts it stably to exactly k entries: those
+//    above the k-th key, plus the lowest-index entries equal to it. The k-th
+//    score becomes the new threshold. A new key, with a higher index than
+//    everything seen, can only enter the top-k by beating that score
+//    strictly, so no candidate is lost and equal scores keep going to the
+//    lower index. At the end the same selection runs once more and the
+//    buffer, already in index order, is the output. No sort anywhere.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace ds4idx {
+namespace {
+
+constexpr int H = kMfmaH;   // indexer heads
+constexpr int D = kMfmaD;   // head dim
+constexpr int NWAVE = 4;    // wavefronts per workgroup
+constexpr int NTOK = 2;     // query tokens per wavefront
+constexpr int TQ = NWAVE * NTOK;
+constexpr int KT = 64;      // keys per LDS tile
+constexpr int KROW = D + 8; // bf16 per LDS key row: 272 B keeps 16-byte reads conflict-free
+constexpr int CAP = 1024;   // candidate slots per token
+constexpr int THREADS = NWAVE * 64;
+
+typedef __attribute__((__vector_size__(8 * sizeof(short)))) short bf16x8;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+
+struct alignas(16) Smem {
+    uint16_t k[2][KT * KROW];
+    float scale[2][KT];
+    float cs[TQ][CAP];
+    int ci[TQ][CAP];
+    uint32_t hist[NWAVE][256];
+};
+
+// Row (head within the 32-row block) that accumulator element i of `lane`
+// holds in the 32x32 MFMA output; the column (key) is lane % 32.
+__device__ __forceinline__ int acc_row(int i, int lane) { return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3); }
+
+// Wavefront-wide: reduce the candidate buffer (cs, ci)[0..n) with n > k to its
+// top-k in place, keeping index order; returns the k-th score (the new
+// admission threshold).
+__device__ float wave_keep_topk(float *cs, int *ci, int n, int k, uint32_t *hist, int lane)
+{
+    uint32_t prefix = 0, pmask = 0, remaining = (uint32_t)k;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+        for (int b = lane; b < 256; b += 64) hist[b] = 0;
+        wave_lds_sync();
+        for (int i = lane; i < n; i += 64) {
+            const uint32_t u = ord_key(cs[i]);
+            if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
+        }
+        wave_lds_sync();
+        uint32_t c[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) c[q] = hist[4 * lane + q];
+        const uint32_t tot = c[0] + c[1] + c[2] + c[3];
+        uint32_t suf = tot;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const uint32_t y = __shfl_down(suf, off);
+            if (lane + off < 64) suf += y;
+        }
+        uint32_t above = suf - tot;
+        int found = -1;
+        uint32_t rem = 0;
+#pragma unroll
+        for (int q = 3; q >= 0; --q) {
+            if (found < 0 && above < remaining && remaining <= above + c[q]) {
+                found = q;
+                rem = remaining - above;
+            }
+            above += c[q];
+        }
+        const int src = __builtin_ctzll(wave_ballot(found >= 0));
+        const uint32_t digit = (uint32_t)(4 * src + wave_readlane(found, src));
+        remaining = (uint32_t)wave_readlane((int)rem, src);
+        prefix |= digit << shift;
+        pmask |= 0xffu << shift;
+        wave_lds_sync();
+    }
+    const uint32_t tau = prefix;
+    uint32_t out = 0, ties = 0;
+    for (int base = 0; base < n; base += 64) {
+        const int i = base + lane;
+        const bool in = i < n;
+        const float sv = in ? cs[i] : 0.0f;
+        const int iv = in ? ci[i] : 0;
+        const uint32_t u = ord_key(sv);
+        const bool eq = in && u == tau;
+        const uint64_t meq = wave_ballot(eq);
+        const bool keep = in && (u > tau || (eq && ties + lanes_below(meq) < remaining));
+        const uint64_t mk = wave_ballot(keep);
+        const uint32_t pos = out + lanes_below(mk);
+        wave_lds_sync();
+        if (keep) {
+            cs[pos] = sv;
+            ci[pos] = iv;
+        }
+        out += (uint32_t)__builtin_popcountll(mk);
+        ties += (uint32_t)__builtin_popcountll(meq);
+    }
+    wave_lds_sync();
+    return key_float(tau);
+}
+
+template <bool KFP8>
+struct TileRegs {
+    uint4 v[KFP8 ? 2 : 4];
+};
+
+// Thread tid stages key (tid / 4) of the tile, bytes quarter (tid % 4) of the row.
+template <bool KFP8>
+__device__ __forceinline__ void load_tile(TileRegs<KFP8> &r, float &sc, const uint8_t *Kb,
+                                          const float *Ksb, int S, int tile, int tid)
+{
+    const int key = tile * KT + (tid >> 2);
+    const int part = tid & 3;
+    constexpr int ROWB = KFP8 ? D : 2 * D;
+    constexpr int NV = KFP8 ? 2 : 4;
+    if (key < S) {
+        const uint4 *src = reinterpret_cast<const uint4 *>(Kb + (size_t)key * ROWB + part * (ROWB / 4));
+#pragma unroll
+        for (int j = 0; j < NV; ++j) r.v[j] = src[j];
+        sc = (KFP8 && part == 0) ? Ksb[key] : 1.0f;
+    } else {
+#pragma unroll
+        for (int j = 0; j < NV; ++j) r.v[j] = make_uint4(0, 0, 0, 0);
+        sc = 1.0f;
+    }
+}
+
+// Two E4M3 codes (the low or high 16 bits of w) -> two bf16 (exact).
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, HI));
+}
+
+template <bool KFP8>
+__device__ __forceinline__ void store_tile(Smem &sm, int buf, const TileRegs<KFP8> &r, float sc, int tid)
+{
+    const int key = tid >> 2, part = tid & 3;
+    uint4 *dst = reinterpret_cast<uint4 *>(&sm.k[buf][key * KROW + part * (D / 4)]);
+    if (KFP8) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const uint4 w = r.v[j];
+            dst[2 * j] = make_uint4(fp8x2_to_bf16x2<false>(w.x), fp8x2_to_bf16x2<true>(w.x),
+                                    fp8x2_to_bf16x2<false>(w.y), fp8x2_to_bf16x2<true>(w.y));
+            dst[2 * j + 1] = make_uint4(fp8x2_to_bf16x2<false>(w.z), fp8x2_to_bf16x2<true>(w.z),
+                                        fp8x2_to_bf16x2<false>(w.w), fp8x2_to_bf16x2<true>(w.w));
+        }
+        if (part == 0) sm.scale[buf][key] = sc;
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dst[j] = r.v[j];
+    }
+}
+
+template <bool KFP8, bool SCORE>
+__global__ __launch_bounds__(THREADS, 1) void mfma_indexer_kernel(
+    const uint16_t *__restrict__ Q, const uint8_t *__restrict__ K, const float *__restrict__ Ks,
+    const float *__restrict__ W, int T, int S, long long offset, int topk, int *__restrict__ idx,
+    float *__restrict__ vals, float *__restrict__ scores)
+{
+    __shared__ Smem sm;
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int nblk = (T + TQ - 1) / TQ;
+    const int t0 = (nblk - 1 - (int)blockIdx.x) * TQ;  // longest rows first
+    const int b = blockIdx.y;
+
+    // This wavefront's two tokens.
+    int tok[NTOK];
+    long long lim[NTOK];
+    long long wave_lim = -1;
+#pragma unroll
+    for (int j = 0; j < NTOK; ++j) {
+        tok[j] = t0 + wid * NTOK + j;
+        lim[j] = tok[j] < T ? offset + tok[j] : -1;
+        wave_lim = lim[j] > wave_lim ? lim[j] : wave_lim;
+    }
+
+    // Queries as MFMA A operands: a[j][hb][ks] = Q[tok j, head hb*32 + lane%32,
+    // dims ks*16 + (lane/32)*8 .. +7]. B operands use the same dim mapping.
+    bf16x8 a[NTOK][2][8];
+    float wv[NTOK][2][16];
+#pragma unroll
+    for (int j = 0; j < NTOK; ++j) {
+        const bool ok = tok[j] < T;
+        const long long qrow = ((long long)b * T + (ok ? tok[j] : 0)) * H;
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+            const bf16x8 *qp = reinterpret_cast<const bf16x8 *>(
+                Q + (qrow + hb * 32 + (lane & 31)) * D + (lane >> 5) * 8);
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) a[j][hb][ks] = ok ? qp[ks * 2] : bf16x8{};
+#pragma unroll
+            for (int i = 0; i < 16; ++i) wv[j][hb][i] = ok ? W[qrow + hb * 32 + acc_row(i, lane)] : 0.0f;
+        }
+    }
+
+    const long long blk_last = offset + (t0 + TQ < T ? t0 + TQ : T) - 1;  // last key any token sees
+    const long long nkeys = SCORE ? (long long)S : blk_last + 1;
+    const int ntiles = (int)((nkeys + KT - 1) / KT);
+    const uint8_t *Kb = K + (size_t)b * S * (KFP8 ? D : 2 * D);
+    const float *Ksb = KFP8 ? Ks + (size_t)b * S : nullptr;
+
+    int cnt[NTOK] = {0, 0};
+    float thr[NTOK] = {-INFINITY, -INFINITY};
+
+    TileRegs<KFP8> tr;
+    float tsc;
+    load_tile<KFP8>(tr, tsc, Kb, Ksb, S, 0, tid);
+    store_tile<KFP8>(sm, 0, tr, tsc, tid);
+    __syncthreads();
+
+    const int jt = lane >> 5;  // token this lane reports after the half swap
+    for (int tile = 0; tile < ntiles; ++tile) {
+        const int cur = tile & 1;
+        if (tile + 1 < ntiles) load_tile<KFP8>(tr, tsc, Kb, Ksb, S, tile + 1, tid);
+        const long long kbase = (long long)tile * KT;
+        if (kbase <= wave_lim) {
+#pragma unroll
+            for (int sb = 0; sb < KT / 32; ++sb) {
+                f32x16 acc[NTOK][2];
+#pragma unroll
+                for (int j = 0; j < NTOK; ++j)
+#pragma unroll
+                    for (int hb = 0; hb < 2; ++hb) acc[j][hb] = f32x16{};
+                const uint16_t *kp = &sm.k[cur][(sb * 32 + (lane & 31)) * KROW + (lane >> 5) * 8];
+#pragma unroll
+                for (int ks = 0; ks < 8; ++ks) {
+                    const bf16x8 bk = *reinterpret_cast<const bf16x8 *>(kp + ks * 16);
+#pragma unroll
+                    for (int j = 0; j < NTOK; ++j)
+#pragma unroll
+                        for (int hb = 0; hb < 2; ++hb)
+                            acc[j][hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j][hb][ks], bk,
+                                                                                 acc[j][hb], 0, 0, 0);
+                }
+                float part[NTOK];
+#pragma unroll
+                for (int j = 0; j < NTOK; ++j) {
+                    float s4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                    for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+                        for (int i = 0; i < 16; ++i)
+                            s4[i & 3] = fmaf(wv[j][hb][i], fmaxf(acc[j][hb][i], 0.0f), s4[i & 3]);
+                    part[j] = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+                }
+                const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0]),
+                                                                 __float_as_uint(part[1]), false, false);
+                float sc = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+                const int kin = sb * 32 + (lane & 31);
+                if (KFP8) sc *= sm.scale[cur][kin];
+                sc = canon(sc);
+                const long long key = kbase + kin;
+                const long long mylim = jt ? lim[1] : lim[0];
+                const bool vis = key <= mylim;
+                if (SCORE) {
+                    const int t = jt ? tok[1] : tok[0];
+                    if (t < T && key < S)
+                        scores[((long long)b * T + t) * S + key] = vis ? sc : -INFINITY;
+                } else {
+                    const float th = jt ? thr[1] : thr[0];
+                    const bool pass = vis && sc > th;
+                    const uint64_t m = wave_ballot(pass);
+                    if (m) {
+                        const uint32_t n0 = (uint32_t)__builtin_popcount((uint32_t)m);
+                        const uint32_t below = lanes_below(m);
+                        const int slot = wid * NTOK + jt;
+                        const int pos = jt ? cnt[1] + (int)(below - n0) : cnt[0] + (int)below;
+                        if (pass) {
+                            sm.cs[slot][pos] = sc;
+                            sm.ci[slot][pos] = (int)key;
+                        }
+                        cnt[0] += (int)n0;
+                        cnt[1] += (int)__builtin_popcount((uint32_t)(m >> 32));
+#pragma unroll
+                        for (int j = 0; j < NTOK; ++j) {
+                            if (cnt[j] > CAP - 32) {
+                                wave_lds_sync();
+                                thr[j] = wave_keep_topk(sm.cs[wid * NTOK + j], sm.ci[wid * NTOK + j],
+                                                        cnt[j], topk, sm.hist[wid], lane);
+                                cnt[j] = topk;
+                            }
+                        }
+                    }
+                }
+            }
+        } else if (SCORE) {
+#pragma unroll
+            for (int j = 0; j < NTOK; ++j) {
+                if (tok[j] >= T) continue;
+                float *orow = scores + ((long long)b * T + tok[j]) * S;
+                for (int i = lane; i < KT; i += 64)
+                    if (kbase + i < S) orow[kbase + i] = -INFINITY;
+            }
+        }
+        if (tile + 1 < ntiles) store_tile<KFP8>(sm, cur ^ 1, tr, tsc, tid);
+        __syncthreads();
+    }
+
+    if (!SCORE) {
+#pragma unroll
+        for (int j = 0; j < NTOK; ++j) {
+            if (tok[j] >= T) continue;
+            float *cs = sm.cs[wid * NTOK + j];
+            int *ci = sm.ci[wid * NTOK + j];
+            wave_lds_sync();
+            if (cnt[j] > topk) {
+                wave_keep_topk(cs, ci, cnt[j], topk, sm.hist[wid], lane);
+                cnt[j] = topk;
+            }
+            const long long orow = ((long long)b * T + tok[j]) * topk;
+            for (int i = lane; i < topk; i += 64) {
+                const bool have = i < cnt[j];
+                idx[orow + i] = have ? ci[i] : -1;
+                if (vals) vals[orow + i] = have ? cs[i] : -INFINITY;
+            }
+        }
+    }
+}
+
+template <bool KFP8, bool SCORE>
+hipError_t launch(const Problem &p, const void *Q, const void *K, const float *Ks, const float *W,
+                  int k, int *idx, float *vals, float *scores, hipStream_t st)
+{
+    const int nblk = (p.T + TQ - 1) / TQ;
+    hipLaunchKernelGGL((mfma_indexer_kernel<KFP8, SCORE>), dim3(nblk, p.B), dim3(THREADS), 0, st,
+                       static_cast<const uint16_t *>(Q), static_cast<const uint8_t *>(K), Ks, W, p.T,
+                       p.S, p.offset, k, idx, vals, scores);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool mfma_shape_ok(const Problem &p)
+{
+    return p.H == H && p.D == D && p.q_dtype == BF16 && (p.k_dtype == BF16 || p.k_dtype == FP8);
+}
+
+hipError_t launch_mfma_score(const Problem &p, const void *Q, const void *K, const float *Ks,
+                             const float *W, float *scores, hipStream_t st)
+{
+    if (p.k_dtype == FP8) return launch<true, true>(p, Q, K, Ks, W, 0, nullptr, nullptr, scores, st);
+    return launch<false, true>(p, Q, K, Ks, W, 0, nullptr, nullptr, scores, st);
+}
+
+hipError_t launch_mfma_select(const Problem &p, const void *Q, const void *K, const float *Ks,
+                              const float *W, int k, int *idx, float *vals, hipStream_t st)
+{
+    if (p.k_dtype == FP8) return launch<true, false>(p, Q, K, Ks, W, k, idx, vals, nullptr, st);
+    return launch<false, false>(p, Q, K, Ks, W, k, idx, vals, nullptr, st);
+}
+
+}  // namespace ds4idx

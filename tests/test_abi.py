@@ -1,0 +1,136 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/ds4idx.h declares, and rejects bad arguments before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_attention_token_lightning_amd as ds
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ds4idx.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ds4idx_[a-z_]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert _declared() == sorted(ds.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = ds.lib()
+    for name in _declared():
+        assert hasattr(L, name), name
+    assert L.ds4idx_abi_version() == ds.ABI_VERSION
+
+
+def test_status_strings():
+    for s in range(5):
+        assert ds.status_string(s)
+    assert ds.status_string(99) == "unknown status"
+
+
+def test_impl_switch():
+    prev = ds.set_impl("ref")
+    try:
+        assert ds.get_impl() == ds.IMPL_REF
+        assert ds.lib().ds4idx_set_impl(7) == -1
+        assert ds.get_impl() == ds.IMPL_REF
+    finally:
+        ds.set_impl(prev)
+
+
+def _prob(**kw):
+    d = dict(B=1, T=16, S=32, H=64, D=128, causal_offset=16, q_dtype=ds.BF16, k_dtype=ds.FP8_E4M3)
+    d.update(kw)
+    return ds.Problem(**d)
+
+
+FAKE = ctypes.c_void_p(0x10000)       # never dereferenced: validation fails first
+FAKE_MIS = ctypes.c_void_p(0x10004)   # 4-byte aligned, not 16
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(T=0), dict(S=0), dict(H=0), dict(D=-1),
+                                dict(causal_offset=-1), dict(causal_offset=17),
+                                dict(q_dtype=2), dict(k_dtype=5), dict(q_dtype=-1)])
+def test_invalid_problem_rejected(kw):
+    L = ds.lib()
+    p = _prob(**kw)
+    args = (ctypes.byref(p), FAKE, FAKE, FAKE, FAKE)
+    assert L.ds4idx_score(*args, FAKE, None) == ds.ERR_INVALID_ARG
+    assert L.ds4idx_select(*args, 512, FAKE, None, None, 0, None) == ds.ERR_INVALID_ARG
+    assert L.ds4idx_topk(ctypes.byref(p), FAKE, 512, FAKE, None, None, 0, None) == ds.ERR_INVALID_ARG
+    assert L.ds4idx_workspace_bytes(ctypes.byref(p), 512, ds.OP_SELECT) == ctypes.c_size_t(-1).value
+
+
+def test_null_problem_rejected():
+    L = ds.lib()
+    assert L.ds4idx_score(None, FAKE, FAKE, FAKE, FAKE, FAKE, None) == ds.ERR_INVALID_ARG
+    assert L.ds4idx_workspace_bytes(None, 512, ds.OP_SELECT) == ctypes.c_size_t(-1).value
+
+
+@pytest.mark.parametrize("which", ["q", "k", "w", "ks", "idx"])
+def test_null_pointers_rejected(which):
+    L = ds.lib()
+    p = _prob()
+    ptr = {n: FAKE for n in ("q", "k", "w", "ks", "idx")}
+    ptr[which] = None
+    st = L.ds4idx_select(ctypes.byref(p), ptr["q"], ptr["k"], ptr["ks"], ptr["w"], 512, ptr["idx"],
+                         None, None, 0, None)
+    assert st == ds.ERR_INVALID_ARG
+
+
+def test_fp8_needs_scale_but_bf16_does_not_validate_it():
+    L = ds.lib()
+    p = _prob()
+    assert L.ds4idx_score(ctypes.byref(p), FAKE, FAKE, None, FAKE, FAKE, None) == ds.ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("which", ["q", "k"])
+def test_misaligned_inputs_rejected(which):
+    L = ds.lib()
+    p = _prob()
+    q = FAKE_MIS if which == "q" else FAKE
+    k = FAKE_MIS if which == "k" else FAKE
+    assert L.ds4idx_select(ctypes.byref(p), q, k, FAKE, FAKE, 512, FAKE, None, None, 0,
+                           None) == ds.ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("k", [0, -1, 2049])
+def test_bad_k_rejected(k):
+    L = ds.lib()
+    p = _prob()
+    assert L.ds4idx_select(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, k, FAKE, None, None, 0,
+                           None) == ds.ERR_INVALID_ARG
+    assert L.ds4idx_topk(ctypes.byref(p), FAKE, k, FAKE, None, None, 0, None) == ds.ERR_INVALID_ARG
+
+
+def test_workspace_sizes_and_checks():
+    L = ds.lib()
+    prev = ds.set_impl("auto")
+    try:
+        p = _prob()
+        assert ds.workspace_bytes(p, 512, ds.OP_SCORE) == 0
+        assert ds.workspace_bytes(p, 512, ds.OP_TOPK) == 0
+        # the MFMA path needs no workspace; the plain path materialises the scores
+        assert ds.workspace_bytes(p, 512) == 0
+        big = ds.workspace_bytes(p, 1024)
+        assert big >= p.B * p.T * p.S * 4 and big % 256 == 0
+        st = L.ds4idx_select(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, 1024, FAKE, None, None, 0, None)
+        assert st == ds.ERR_WORKSPACE
+        st = L.ds4idx_select(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, 1024, FAKE, None,
+                             ctypes.c_void_p(0x10100), big - 1, None)
+        assert st == ds.ERR_WORKSPACE
+        ds.set_impl("ref")
+        assert ds.workspace_bytes(p, 512) >= p.B * p.T * p.S * 4
+        # forcing the MFMA family on a shape it does not cover
+        ds.set_impl("opt")
+        p2 = _prob(H=4, D=64, q_dtype=ds.F32, k_dtype=ds.F32)
+        assert L.ds4idx_score(ctypes.byref(p2), FAKE, FAKE, None, FAKE, FAKE, None) == ds.ERR_UNSUPPORTED
+    finally:
+        ds.set_impl(prev)

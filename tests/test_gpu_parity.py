@@ -1,0 +1,240 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Every test names its workload, seed and shape in its id; inputs are seeded.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_attention_token_lightning_amd as ds
+import workloads as W
+from parity import check_invariants, compare_rows, run_select, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _impl_auto():
+    prev = ds.set_impl("auto")
+    yield
+    ds.set_impl(prev)
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+# ------------------------------------------------------------------ fp8 codec
+
+@pytest.mark.parametrize("impl", ["opt", "ref"])
+def test_e4m3_decode_through_scorer(impl):
+    # K row s holds code s in dim 0; q = +e0 (t=0) or -e0 (t=1) on head 0 only,
+    # w = e_head0, scale 1: score(t, s) = max(0, +-decode(s)). Every OCP code
+    # except the two NaNs is recovered exactly; the FNUZ reading would halve
+    # them.
+    ds.set_impl(impl)
+    S, T, H, D = 256, 2, 64, 128
+    k = np.zeros((1, S, D), np.uint8)
+    k[0, :, 0] = np.arange(256)
+    q = np.zeros((1, T, H, D), np.float32)
+    q[0, 0, 0, 0], q[0, 1, 0, 0] = 1.0, -1.0
+    w = np.zeros((1, T, H), np.float32)
+    w[0, :, 0] = 1.0
+    dev = (torch.from_numpy(q).to(torch.bfloat16).cuda(), torch.from_numpy(k).cuda(),
+           torch.ones((1, S), dtype=torch.float32, device="cuda"), torch.from_numpy(w).cuda())
+    sc = ds.score(*dev, causal_offset=S - T).cpu().numpy()[0]
+    ref = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    for code in range(256):
+        if np.isnan(ref[code]):
+            continue
+        if code <= S - T:  # t = 0 sees s <= 254
+            assert sc[0, code] == max(0.0, ref[code]), (code, sc[0, code], ref[code])
+        assert sc[1, code] == max(0.0, -ref[code]), (code, sc[1, code], ref[code])
+    assert sc[0, 255] == -np.inf
+
+
+# ------------------------------------------------------------------ exact configs
+
+def test_tiny_all_rows_exact():
+    wl = W.tiny()
+    _say("tiny T=S=1024 H=4 D=64 fp32 ints seed=1")
+    gi, gv = run_select(wl, poison=True)
+    check_invariants(wl, gi)
+    compare_rows(wl, np.arange(wl.T), gi, gv, exact=True)
+
+
+@pytest.mark.parametrize("impl", ["auto", "ref"])
+def test_int_prefill_2k_all_rows_exact(impl):
+    ds.set_impl(impl)
+    wl = W.prefill_bf16_int(seed=102, T=2048, S=2048)
+    _say(f"8k-int recipe at T=S=2048 seed=102 impl={impl}")
+    gi, gv = run_select(wl, poison=True)
+    check_invariants(wl, gi)
+    compare_rows(wl, np.arange(wl.T), gi, gv, exact=True)
+
+
+def test_int_prefill_8k_full_size_exact():
+    wl = W.prefill_bf16_int()
+    _say("8k-int T=S=8192 H=64 D=128 seed=102")
+    gi, gv = run_select(wl)
+    check_invariants(wl, gi)
+    rows = W.sample_rows(wl, 96)
+    compare_rows(wl, rows, gi[rows], gv[rows], exact=True)
+
+
+# ------------------------------------------------------------------ float configs
+
+def test_prefill_8k_bf16():
+    wl = W.prefill_bf16()
+    _say("8k T=S=8192 bf16 seed=2")
+    gi, gv = run_select(wl)
+    check_invariants(wl, gi)
+    rows = W.sample_rows(wl, 96)
+    swaps = compare_rows(wl, rows, gi[rows], gv[rows], exact=False)
+    _say("near-tie swaps", swaps)
+
+
+def test_prefill_64k_fp8_chunked():
+    wl = W.prefill_fp8()
+    _say("64k T=S=65536 fp8 K, 16 chunks of 4096, seed=3")
+    gi, gv = run_select(wl)
+    check_invariants(wl, gi)
+    rows = W.sample_rows(wl, 40)
+    swaps = compare_rows(wl, rows, gi[rows], gv[rows], exact=False)
+    _say("near-tie swaps", swaps)
+
+
+def test_decode_256k_fp8():
+    wl = W.decode()
+    _say("decode B=8 T=1 S=262144 fp8 K seed=4")
+    gi, gv = run_select(wl, poison=True)
+    check_invariants(wl, gi)
+    swaps = compare_rows(wl, np.arange(wl.B), gi, gv, exact=False)
+    _say("near-tie swaps", swaps)
+
+
+def test_long_prefill_1m_fp8():
+    wl = W.long_prefill()
+    _say("1m T=2048 S=1048576 offset=1046528 fp8 K seed=5")
+    gi, gv = run_select(wl)
+    check_invariants(wl, gi)
+    rows = np.array([0, 777, 2047])
+    swaps = compare_rows(wl, rows, gi[rows], gv[rows], exact=False)
+    _say("near-tie swaps", swaps)
+
+
+# ------------------------------------------------------------------ edge cases
+
+@pytest.mark.parametrize("T,offset,extra,topk,B", [
+    (13, 0, 0, 512, 1),      # ragged tail, all rows shorter than k
+    (37, 600, 5, 512, 2),    # ragged, offset, keys beyond the horizon, batch 2
+    (9, 100, 0, 1, 1),       # k = 1
+    (21, 3000, 0, 7, 1),     # small k, long rows
+    (64, 511, 0, 512, 1),    # rows of exactly k keys at the first query
+    (8, 4000, 100, 100, 3),  # batch 3
+])
+def test_edge_shapes_fp8(T, offset, extra, topk, B):
+    wl = W.prefill_fp8(seed=31 + T, T=T, S=T + offset + extra, offset=offset, topk=topk, B=B,
+                       chunk=T)
+    wl.chunks = [(0, T, wl.S, offset)]  # the whole cache, including keys past the horizon
+    _say(f"edge fp8 B={B} T={T} offset={offset} extra={extra} k={topk}")
+    gi, gv = run_select(wl, poison=True)
+    check_invariants(wl, gi)
+    compare_rows(wl, np.arange(wl.B * wl.T), gi, gv, exact=False)
+
+
+def test_all_equal_scores_tie_break():
+    # K = 0: every score is exactly 0; the answer is {0..min(k,L)-1}.
+    wl = W.prefill_bf16(seed=5, T=40, S=1200, offset=1160, topk=512)
+    wl.k[:] = 0
+    gi, gv = run_select(wl)
+    for r in range(wl.T):
+        L = wl.offset + r + 1
+        assert list(gi[r, :min(512, L)]) == list(range(min(512, L)))
+        assert np.all(gv[r, :min(512, L)] == 0)
+
+
+@pytest.mark.parametrize("direction", [1, -1])
+def test_monotone_rows_stress_streaming(direction):
+    # Scores strictly monotone in s: rising rows admit every key (the most
+    # buffer refills), falling rows admit almost none after the first k.
+    T, S = 16, 20000
+    off = S - T
+    q = np.zeros((1, T, 64, 128), np.float32)
+    q[..., 0] = 1.0
+    k = np.full((1, S, 128), 0x38, np.uint8)   # E4M3 1.0 in every dim
+    scale = (1.0 + direction * np.arange(S) * 2.0 ** -20).astype(np.float32).reshape(1, S)
+    w = np.full((1, T, 64), 0.5, np.float32)
+    wl = W.Workload("mono", W.to_bf16_bits(q), k, scale, w, 1, T, S, 64, 128, off, 512, W.BF16,
+                    W.FP8, [(0, T, S, off)])
+    gi, gv = run_select(wl)
+    for t in range(T):
+        L = off + t + 1
+        exp = list(range(L - 512, L)) if direction > 0 else list(range(512))
+        assert list(gi[t]) == exp
+
+
+def test_negative_weights_zero_ties():
+    # w < 0 everywhere: every score <= 0, many exactly 0 (some -0.0). Zeros tie.
+    wl = W.prefill_bf16_int(seed=9, T=24, S=3000, offset=2976, topk=512)
+    wl.w[:] = -np.abs(wl.w)
+    gi, gv = run_select(wl)
+    compare_rows(wl, np.arange(wl.T), gi, gv, exact=True)
+
+
+# ------------------------------------------------------------------ consistency
+
+def test_fused_equals_score_then_topk():
+    wl = W.prefill_fp8(seed=12, T=300, S=5000, offset=4700, chunk=300)
+    q, k, ks, w = to_device(wl)
+    idx, vals = ds.select(q, k, ks, w, wl.offset, 512)
+    sc = ds.score(q, k, ks, w, wl.offset)
+    idx2, vals2 = ds.topk(sc, 512, wl.offset)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx2)
+    assert torch.equal(vals, vals2)
+    # the scorer's masked region is -inf, the visible part finite
+    lim = wl.offset + torch.arange(wl.T, device="cuda")
+    cols = torch.arange(wl.S, device="cuda")
+    masked = cols[None, :] > lim[:, None]
+    assert torch.all(torch.isneginf(sc[0][masked]))
+    assert torch.all(torch.isfinite(sc[0][~masked]))
+
+
+def test_scorer_values_against_oracle():
+    wl = W.prefill_fp8(seed=13, T=64, S=3000, offset=2936, chunk=64)
+    sc = ds.score(*to_device(wl), causal_offset=wl.offset).cpu().numpy()[0]
+    g = np.random.Generator(np.random.PCG64(0))
+    rows = g.integers(0, wl.T, 400)
+    keys = np.array([g.integers(0, wl.offset + r + 1) for r in rows])
+    ref = oracle.score_pairs(wl, rows, keys)
+    _, _, _, rms, _ = oracle.select(wl, rows=np.unique(rows))
+    rmsd = dict(zip(np.unique(rows).tolist(), rms))
+    tol = 1e-2 * np.maximum(np.abs(ref), np.array([rmsd[r] for r in rows]))
+    assert np.all(np.abs(sc[rows, keys] - ref) <= tol)
+
+
+def test_rollback_ref_matches_opt_on_integers():
+    wl = W.prefill_bf16_int(seed=41, T=256, S=4096, offset=3840)
+    dev = to_device(wl)
+    ds.set_impl("opt")
+    a, av = run_select(wl, dev=dev)
+    ds.set_impl("ref")
+    b, bv = run_select(wl, dev=dev)
+    assert np.array_equal(a, b) and np.array_equal(av, bv)
+
+
+def test_deterministic_repeat():
+    wl = W.prefill_fp8(seed=14, T=512, S=20000, offset=19488, chunk=512)
+    dev = to_device(wl)
+    a, av = run_select(wl, dev=dev)
+    b, bv = run_select(wl, dev=dev)
+    assert np.array_equal(a, b) and np.array_equal(av.view(np.uint32), bv.view(np.uint32))
+
+
+def test_large_k_routes_to_plain_kernels():
+    wl = W.prefill_fp8(seed=15, T=20, S=3000, offset=2980, topk=1500, chunk=20)
+    gi, gv = run_select(wl)
+    check_invariants(wl, gi)
+    compare_rows(wl, np.arange(wl.T), gi, gv, exact=False)
