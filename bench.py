@@ -1,0 +1,202 @@
+"""Benchmark: Lightning Indexer (score + top-512) on one MI355X.
+
+One step = the 64k cold causal prefill: T = S = 65536 queries in 16 chunks of
+4096 (chunk c: causal offset 4096c against the 4096(c+1) keys cached so far),
+H = 64, D = 128, top-512, bf16 Q, OCP E4M3 K with per-token fp32 scale,
+fp32 head weights, i.e. 16 ds4idx_select calls on one stream. Inputs are
+seeded synthetic data resident in HBM before timing starts.
+
+Printed (one JSON line): query-tok/s of the step, the roofline of the MFMA
+select kernel (algorithmic bf16 flop per launch over its HIP-event-timed
+average duration, against the 2.5 PFLOP/s dense bf16 peak), the 256k decode
+latency (8 streams x 1 query x 262144 keys, rotated over 3 copies of the
+inputs so the 256 MB last-level cache cannot hold them), and the CPU oracle
+timed on a bounded sample of the same prefill rows.
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+METRIC = "indexer query-tok/s at 64k causal prefill (score+top-512); decode µs at 256k"
+BF16_PEAK_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 dense bf16 flop/clk/CU
+HBM_PEAK_GBS = 8000.0
+
+
+def _parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--decode-iters", type=int, default=60)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    return ap.parse_args()
+
+
+def _flops_64k(wl):
+    """Algorithmic work of one step: 2*H*D flop per visible (query, key) pair;
+    chunk c's query j (of T_c) sees offset_c + j + 1 keys."""
+    pairs = sum(tc * oc + tc * (tc + 1) // 2 for (_, tc, _, oc) in wl.chunks)
+    return 2 * wl.H * wl.D * pairs, pairs
+
+
+def main():
+    args = _parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the indexer path here runs on a single MI355X "
+              "(rows shard across GPUs with no exchange; that path is not built). Use --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    import sparse_attention_token_lightning_amd as ds
+    import workloads as W
+
+    ds.lib()  # fail loudly if the HIP library is missing
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    # ---------------------------------------------------------------- 64k prefill
+    wl = W.prefill_fp8()
+    q = torch.from_numpy(wl.q.view(np.int16)).view(torch.bfloat16).to(dev)
+    k = torch.from_numpy(wl.k).to(dev)
+    ks = torch.from_numpy(wl.k_scale).to(dev)
+    w = torch.from_numpy(wl.w).to(dev)
+    idx = torch.empty((1, wl.T, wl.topk), dtype=torch.int32, device=dev)
+    vals = torch.empty((1, wl.T, wl.topk), dtype=torch.float32, device=dev)
+    ws = [ds.new_workspace(ds.make_problem(q[:, t0:t0 + tc], k[:, :sc], oc), wl.topk, dev)
+          for (t0, tc, sc, oc) in wl.chunks]
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        for c, (t0, tc, sc, oc) in enumerate(wl.chunks):
+            if ev is not None:
+                ev[c][0].record(stream)
+            ds.select(q[:, t0:t0 + tc], k[:, :sc], ks[:, :sc], w[:, t0:t0 + tc], oc, wl.topk,
+                      idx=idx[:, t0:t0 + tc], vals=vals[:, t0:t0 + tc], workspace=ws[c],
+                      stream=stream)
+            if ev is not None:
+                ev[c][1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in wl.chunks]
+              for _ in range(args.steps)]
+    t_start = time.perf_counter()
+    for s in range(args.steps):
+        step(events[s])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    launch_ms = [ev[0].elapsed_time(ev[1]) for st in events for ev in st]
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = wl.T * args.steps / elapsed
+
+    flops, pairs = _flops_64k(wl)
+    n_launch = len(wl.chunks)
+    avg_launch_s = (sum(launch_ms) / len(launch_ms)) * 1e-3
+    achieved_tflops = flops / n_launch / avg_launch_s / 1e12
+    roofline = {"bound": "mfma", "achieved": round(achieved_tflops, 1), "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved_tflops / BF16_PEAK_TFLOPS, 4),
+                "traffic": None,
+                "kernel": "mfma_indexer_kernel<fp8 keys, select>",
+                "avg_launch_us": round(avg_launch_s * 1e6, 2),
+                "flop_per_launch": flops // n_launch}
+
+    extra = {"kernel_ms_per_step": round(sum(launch_ms) / args.steps, 3),
+             "bf16_tflops_step_wall": round(flops / (ms_per_step * 1e-3) / 1e12, 1)}
+
+    # ---------------------------------------------------------------- 256k decode
+    if not args.no_decode:
+        dl = W.decode()
+        sets = []
+        qd = torch.from_numpy(dl.q.view(np.int16)).view(torch.bfloat16).to(dev)
+        kd = torch.from_numpy(dl.k).to(dev)
+        ksd = torch.from_numpy(dl.k_scale).to(dev)
+        wd = torch.from_numpy(dl.w).to(dev)
+        for r in range(3):
+            sets.append((qd.clone(), kd.clone(), ksd.clone(), wd.clone()))
+        del qd, kd, ksd, wd
+        pd = ds.make_problem(sets[0][0], sets[0][1], dl.offset)
+        wsd = ds.new_workspace(pd, dl.topk, dev)
+        idd = torch.empty((dl.B, 1, dl.topk), dtype=torch.int32, device=dev)
+        vd = torch.empty((dl.B, 1, dl.topk), dtype=torch.float32, device=dev)
+
+        def dstep(i):
+            a = sets[i % 3]
+            ds.select(*a, dl.offset, dl.topk, idx=idd, vals=vd, workspace=wsd, stream=stream)
+
+        for i in range(6):
+            dstep(i)
+        torch.cuda.synchronize()
+        dev_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
+                  for _ in range(args.decode_iters)]
+        for i in range(args.decode_iters):
+            dev_ev[i][0].record(stream)
+            dstep(i)
+            dev_ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        dus = sorted(e[0].elapsed_time(e[1]) * 1e3 for e in dev_ev)
+        dbytes = dl.k.nbytes + dl.k_scale.nbytes + dl.q.nbytes + dl.w.nbytes + dl.B * dl.topk * 8
+        med = dus[len(dus) // 2]
+        extra["decode_256k"] = {"us_median": round(med, 2), "us_min": round(dus[0], 2),
+                                "alg_bytes": int(dbytes),
+                                "GB_s": round(dbytes / (med * 1e-6) / 1e9, 1),
+                                "hbm_frac": round(dbytes / (med * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        del sets
+
+    # ---------------------------------------------------------------- CPU oracle
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        oracle.build(force=False)
+        rng = np.random.Generator(np.random.PCG64(17))
+        probe = np.sort(rng.choice(wl.T, 8, replace=False)).astype(np.int64)
+        t0 = time.perf_counter()
+        _, _, _, _, used = oracle.select(wl, rows=probe)
+        t_probe = time.perf_counter() - t0
+        keys_probe = int(sum(wl.offset + r + 1 for r in probe))
+        rate = keys_probe / max(t_probe, 1e-6)                       # keys scored per second
+        n = int(min(wl.T, max(8, args.cpu_seconds * rate / (pairs / wl.T))))
+        rows = np.sort(rng.choice(wl.T, n, replace=False)).astype(np.int64)
+        t0 = time.perf_counter()
+        _, _, _, _, used = oracle.select(wl, rows=rows)
+        t_cpu = time.perf_counter() - t0
+        keys = int(sum(wl.offset + r + 1 for r in rows))
+        full_s = t_cpu * pairs / keys
+        cpu = {"value": round(wl.T / full_s, 2), "unit": "query-tok/s", "cores": int(used),
+               "kind": "oracle",
+               "sample": f"{n} uniformly drawn query rows of the 64k prefill ({keys} visible keys, "
+                         f"{t_cpu:.1f} s measured), extrapolated by visible-key count to all "
+                         f"{wl.T} rows ({pairs} keys)"}
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "query-tok/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "64k cold causal prefill: T=S=65536 in 16 chunks of 4096 queries, "
+                               "H=64, D=128, top-512, bf16 Q, OCP E4M3 K + per-token fp32 scale, "
+                               "fp32 head weights",
+                   "global_batch": 1, "seq_len": wl.T, "topk": wl.topk, "heads": wl.H,
+                   "head_dim": wl.D},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
