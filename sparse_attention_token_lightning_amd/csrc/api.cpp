@@ -77,14 +77,26 @@ int route_score(const ds4idx_problem *p)
     return ref_shape_ok(p) ? 0 : -1;
 }
 
+enum Route { R_NONE = -1, R_REF = 0, R_PREFILL = 1, R_SPLIT = 2 };
+
+// Fused select: the MFMA prefill kernel (8 query tokens per workgroup, whole
+// rows) when there are enough rows to fill the GPU; the split-key kernel when
+// there are too few rows (decode); the plain kernels otherwise.
 int route_select(const ds4idx_problem *p, int32_t k)
 {
     const Problem q = to_internal(p);
     const int impl = impl_now();
-    const bool mf = ds4idx::mfma_shape_ok(q) && k <= ds4idx::kMfmaMaxK;
-    if (impl == DS4IDX_IMPL_OPT) return mf ? 1 : -1;
-    if (impl == DS4IDX_IMPL_AUTO && mf) return 1;
-    return ref_shape_ok(p) ? 0 : -1;
+    const bool shape = ds4idx::mfma_shape_ok(q);
+    const int64_t rows = (int64_t)p->B * p->T;
+    const bool prefill_ok = shape && k <= ds4idx::kMfmaMaxK && p->B <= 65535;
+    const bool split_ok = shape && rows <= 65535 && ds4idx::split_parts(q) <= ds4idx::kSplitMaxParts;
+    const int64_t prefill_blocks = (int64_t)p->B * ((p->T + 7) / 8);
+    int mf = R_NONE;
+    if (split_ok && (prefill_blocks < 128 || !prefill_ok)) mf = R_SPLIT;
+    else if (prefill_ok) mf = R_PREFILL;
+    if (impl == DS4IDX_IMPL_OPT) return mf;
+    if (impl == DS4IDX_IMPL_AUTO && mf != R_NONE) return mf;
+    return ref_shape_ok(p) ? R_REF : R_NONE;
 }
 
 size_t round_up(size_t n, size_t a) { return (n + a - 1) / a * a; }
@@ -131,7 +143,8 @@ size_t ds4idx_workspace_bytes(const ds4idx_problem *p, int32_t k, int32_t op)
     if (op == DS4IDX_OP_SCORE || op == DS4IDX_OP_TOPK) return 0;
     if (op != DS4IDX_OP_SELECT || k < 1 || k > DS4IDX_MAX_TOPK) return (size_t)-1;
     const int r = route_select(p, k);
-    if (r == 0) return ref_select_bytes(p);
+    if (r == R_REF) return ref_select_bytes(p);
+    if (r == R_SPLIT) return ds4idx::split_workspace_bytes(to_internal(p), k);
     return 0;
 }
 
@@ -174,13 +187,17 @@ int ds4idx_select(const ds4idx_problem *p, const void *Q, const void *K, const f
     if (k < 1 || k > DS4IDX_MAX_TOPK) return DS4IDX_ERR_INVALID_ARG;
     if (!idx || !aligned(idx, 4) || (vals && !aligned(vals, 4))) return DS4IDX_ERR_INVALID_ARG;
     const int r = route_select(p, k);
-    if (r < 0) return DS4IDX_ERR_UNSUPPORTED;
-    const size_t need = r == 0 ? ref_select_bytes(p) : 0;
+    if (r == R_NONE) return DS4IDX_ERR_UNSUPPORTED;
+    const Problem q = to_internal(p);
+    const size_t need = r == R_REF ? ref_select_bytes(p)
+                        : r == R_SPLIT ? ds4idx::split_workspace_bytes(q, k) : 0;
     if (need > 0 && (!workspace || !aligned(workspace, 256) || ws_bytes < need))
         return DS4IDX_ERR_WORKSPACE;
-    const Problem q = to_internal(p);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (r == 1) return launch_status(ds4idx::launch_mfma_select(q, Q, K, K_scale, W, k, idx, vals, s));
+    if (r == R_PREFILL)
+        return launch_status(ds4idx::launch_mfma_select(q, Q, K, K_scale, W, k, idx, vals, s));
+    if (r == R_SPLIT)
+        return launch_status(ds4idx::launch_split_select(q, Q, K, K_scale, W, k, idx, vals, workspace, s));
     float *sc = static_cast<float *>(workspace);
     st = launch_status(ds4idx::launch_score_ref(q, Q, K, K_scale, W, sc, s));
     if (st != DS4IDX_OK) return st;

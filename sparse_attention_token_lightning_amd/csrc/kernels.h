@@ -31,4 +31,19 @@ hipError_t launch_mfma_score(const Problem &p, const void *Q, const void *K, con
 hipError_t launch_mfma_select(const Problem &p, const void *Q, const void *K, const float *Ks,
                               const float *W, int k, int *idx, float *vals, hipStream_t st);
 
+// Split-key kernel for few rows over long caches (decode): partitions of 8192
+// keys, per-partition exact top-k, last-arriving workgroup merges each row.
+constexpr int kSplitMaxParts = 256;
+struct SplitWorkspace {
+    uint32_t *ctr;     // [rows] arrival counters, zero between calls
+    uint32_t *cand_n;  // [rows, P] candidates per partition
+    float *cand_s;     // [rows, P, k]
+    int *cand_i;       // [rows, P, k]
+};
+int split_parts(const Problem &p);
+size_t split_workspace_bytes(const Problem &p, int k);
+SplitWorkspace split_workspace(void *ws, const Problem &p, int k);
+hipError_t launch_split_select(const Problem &p, const void *Q, const void *K, const float *Ks,
+                               const float *W, int k, int *idx, float *vals, void *ws, hipStream_t st);
+
 }  // namespace ds4idx

@@ -1,0 +1,452 @@
+// Lightning Indexer for few query rows over long key caches (decode, a few
+// streams each attending to a 256k-token cache): split the keys, stream them
+// from HBM once, merge per row. The pages report that single-stream decode
+// stayed a wall for their Metal kernels (first page, section details, second
+// paragraph) and give no decode design; this one is built for HBM streaming.
+//
+//  * Grid = (P partitions of 8192 keys) x (rows). Eight wavefronts per
+//    workgroup, each scoring 1024 keys in rounds of 64 (two 32-key MFMA
+//    blocks whose partial head sums pair up in one v_permlane32_swap).
+//  * Keys go HBM -> VGPRs directly as MFMA B operands: the contraction index
+//    d is assigned so that lane half h of k-step ks covers dims
+//    h*64 + ks*8 .. +7, which makes every lane read 64 contiguous bytes of its
+//    key (four 16-byte loads; the two halves of a wave cover each 128-byte fp8
+//    row). Queries use the same assignment. E4M3 widens to bf16 in registers.
+//    The next round's keys are in flight while the current one is scored.
+//  * Scores stay in registers (16 per lane). The partition's exact top-k is
+//    found by block-wide radix selection over an order-preserving 32-bit key
+//    (per-wavefront LDS histograms, four 8-bit digits) and written, in index
+//    order, to the workspace.
+//  * The last workgroup of a row to finish (device-scope arrival counter)
+//    merges the row's P candidate lists with the same exact selection and
+//    writes the final indices in ascending order, then resets the counter.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace ds4idx {
+namespace {
+
+constexpr int H = kMfmaH;
+constexpr int D = kMfmaD;
+constexpr int NW = 8;
+constexpr int THREADS = NW * 64;
+constexpr int ROUNDS = 16;
+constexpr int WAVE_KEYS = ROUNDS * 64;
+constexpr int PART = NW * WAVE_KEYS;  // 8192
+
+typedef __attribute__((__vector_size__(8 * sizeof(short)))) short bf16x8;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+
+struct SplitSmem {
+    uint32_t sc[NW][WAVE_KEYS];  // order-preserving score keys, 0 = no key
+    uint32_t hist[NW][256];
+    uint32_t tot[256];
+    uint32_t wsum[NW];
+    uint32_t pick[2];
+    uint32_t pn[kSplitMaxParts];
+    int last;
+};
+
+__device__ __forceinline__ int acc_row(int i, int lane) { return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3); }
+
+template <bool HI>
+__device__ __forceinline__ uint32_t cvt2(uint32_t w)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, HI));
+}
+
+// Block-wide exclusive prefix sum of v; `total` receives the block sum.
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, SplitSmem &sm, uint32_t &total)
+{
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    uint32_t x = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = __shfl_up(x, off);
+        if (lane >= off) x += y;
+    }
+    if (lane == 63) sm.wsum[wid] = x;
+    __syncthreads();
+    uint32_t before = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        const uint32_t c = sm.wsum[w];
+        before += (w < wid) ? c : 0u;
+        tot += c;
+    }
+    __syncthreads();
+    total = tot;
+    return before + x - v;
+}
+
+// One radix digit step shared by both selections: after every thread has
+// added its keys to its wavefront's histogram, find the digit of the k-th
+// largest key and how many keys of that digit are still wanted.
+__device__ __forceinline__ void pick_digit(SplitSmem &sm, uint32_t remaining)
+{
+    const int tid = threadIdx.x, lane = tid & 63;
+    __syncthreads();
+    if (tid < 256) {
+        uint32_t s = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) s += sm.hist[w][tid];
+        sm.tot[tid] = s;
+    }
+    __syncthreads();
+    if (tid < 64) {
+        uint32_t c[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) c[q] = sm.tot[4 * lane + q];
+        const uint32_t tot = c[0] + c[1] + c[2] + c[3];
+        uint32_t suf = tot;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const uint32_t y = __shfl_down(suf, off);
+            if (lane + off < 64) suf += y;
+        }
+        uint32_t above = suf - tot;
+        int found = -1;
+        uint32_t rem = 0;
+#pragma unroll
+        for (int q = 3; q >= 0; --q) {
+            if (found < 0 && above < remaining && remaining <= above + c[q]) {
+                found = q;
+                rem = remaining - above;
+            }
+            above += c[q];
+        }
+        const int src = __builtin_ctzll(wave_ballot(found >= 0));
+        if (lane == src) {
+            sm.pick[0] = (uint32_t)(4 * lane + found);
+            sm.pick[1] = rem;
+        }
+    }
+    __syncthreads();
+}
+
+__device__ __forceinline__ void clear_hist(SplitSmem &sm)
+{
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    for (int b = lane; b < 256; b += 64) sm.hist[wid][b] = 0;
+    wave_lds_sync();
+}
+
+// This lane's half of one key row of a 32-key sub-block (key = base + lane%32,
+// dims half*64 .. +63): 64 bytes of E4M3 codes or 128 bytes of bf16.
+template <bool KFP8>
+struct Raw {
+    uint4 v[KFP8 ? 4 : 8];
+};
+
+template <bool KFP8>
+__device__ __forceinline__ void load_sub(Raw<KFP8> &r, const uint8_t *Kr, long long kbase,
+                                         long long L, int lane)
+{
+    constexpr int NV = KFP8 ? 4 : 8;
+    constexpr int ROWB = KFP8 ? D : 2 * D;
+    const long long key = kbase + (lane & 31);
+    if (key < L) {
+        const uint4 *src = reinterpret_cast<const uint4 *>(Kr + key * ROWB + (lane >> 5) * (ROWB / 2));
+#pragma unroll
+        for (int j = 0; j < NV; ++j) r.v[j] = src[j];
+    } else {
+#pragma unroll
+        for (int j = 0; j < NV; ++j) r.v[j] = make_uint4(0, 0, 0, 0);
+    }
+}
+
+// B operand of k-step ks: dims half*64 + ks*8 .. +7 of the lane's half row.
+template <bool KFP8>
+__device__ __forceinline__ bf16x8 b_operand(const Raw<KFP8> &r, int ks)
+{
+    if (KFP8) {
+        const uint4 &w = r.v[ks >> 1];
+        const uint32_t lo = (ks & 1) ? w.z : w.x;
+        const uint32_t hi = (ks & 1) ? w.w : w.y;
+        const uint4 o = make_uint4(cvt2<false>(lo), cvt2<true>(lo), cvt2<false>(hi), cvt2<true>(hi));
+        return __builtin_bit_cast(bf16x8, o);
+    } else {
+        return __builtin_bit_cast(bf16x8, r.v[ks]);
+    }
+}
+
+// Partial (this lane's 16 head rows of each head block) score of one sub-block.
+template <bool KFP8>
+__device__ __forceinline__ float score_sub(const Raw<KFP8> &r, const bf16x8 (&a)[2][8],
+                                           const float (&wv)[2][16])
+{
+    f32x16 acc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+        const bf16x8 bk = b_operand<KFP8>(r, ks);
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb)
+            acc[hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[hb][ks], bk, acc[hb], 0, 0, 0);
+    }
+    float s4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s4[i & 3] = fmaf(wv[hb][i], fmaxf(acc[hb][i], 0.0f), s4[i & 3]);
+    return (s4[0] + s4[1]) + (s4[2] + s4[3]);
+}
+
+template <bool KFP8>
+__global__ __launch_bounds__(THREADS, 1) void split_indexer_kernel(
+    const uint16_t *__restrict__ Q, const uint8_t *__restrict__ K, const float *__restrict__ Ks,
+    const float *__restrict__ W, int T, int S, long long offset, int topk, int P,
+    uint32_t *__restrict__ ctr, uint32_t *__restrict__ cand_n, float *__restrict__ cand_s,
+    int *__restrict__ cand_i, int *__restrict__ idx, float *__restrict__ vals)
+{
+    __shared__ SplitSmem sm;
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int p = blockIdx.x;
+    const long long r = blockIdx.y;  // b * T + t
+    const int b = (int)(r / T), t = (int)(r % T);
+    const long long L = offset + t + 1;
+    const long long pbase = (long long)p * PART;
+    const long long nvalid = L - pbase < 0 ? 0 : (L - pbase > PART ? PART : L - pbase);
+
+    const long long wbase = pbase + (long long)wid * WAVE_KEYS;
+    const long long wkeys = L - wbase < 0 ? 0 : (L - wbase > WAVE_KEYS ? WAVE_KEYS : L - wbase);
+    if (wkeys > 0) {
+        bf16x8 a[2][8];
+        float wv[2][16];
+        const int half = lane >> 5;
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+            const bf16x8 *qp = reinterpret_cast<const bf16x8 *>(
+                Q + ((r * H + hb * 32 + (lane & 31)) * D + half * 64));
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) a[hb][ks] = qp[ks];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) wv[hb][i] = W[r * H + hb * 32 + acc_row(i, lane)];
+        }
+        const uint8_t *Kr = K + (size_t)b * S * (KFP8 ? D : 2 * D);
+        const float *Ksr = KFP8 ? Ks + (size_t)b * S : nullptr;
+        // Sub-blocks of 32 keys; pairs (2j, 2j+1) share one half swap. A ring
+        // of NBUF raw sub-blocks keeps NBUF-1 loads in flight.
+        constexpr int NBUF = KFP8 ? 4 : 2;
+        const int nsub = (int)((wkeys + 63) / 64) * 2;
+        Raw<KFP8> buf[NBUF];
+#pragma unroll
+        for (int i = 0; i < NBUF - 1; ++i)
+            if (i < nsub) load_sub<KFP8>(buf[i], Kr, wbase + 32 * i, L, lane);
+        float prev = 0.0f;
+        for (int sb0 = 0; sb0 < nsub; sb0 += NBUF) {
+#pragma unroll
+            for (int i = 0; i < NBUF; ++i) {
+                const int sb = sb0 + i;
+                if (sb < nsub) {
+                    if (sb + NBUF - 1 < nsub)
+                        load_sub<KFP8>(buf[(i + NBUF - 1) % NBUF], Kr, wbase + 32 * (sb + NBUF - 1), L, lane);
+                    const float part = score_sub<KFP8>(buf[i], a, wv);
+                    if (i & 1) {
+                        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(prev),
+                                                                         __float_as_uint(part), false, false);
+                        float sc = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+                        const long long key = wbase + 32 * (sb - 1) + lane;
+                        if (KFP8) sc *= key < L ? Ksr[key] : 1.0f;
+                        sm.sc[wid][32 * (sb - 1) + lane] = key < L ? ord_key(canon(sc)) : 0u;
+                    } else {
+                        prev = part;
+                    }
+                }
+            }
+        }
+    }
+    for (int i = (int)(wkeys < 0 ? 0 : ((wkeys + 63) / 64) * 64) + lane; i < WAVE_KEYS; i += 64)
+        sm.sc[wid][i] = 0u;
+    wave_lds_sync();
+    uint32_t u[ROUNDS];
+#pragma unroll
+    for (int j = 0; j < ROUNDS; ++j) u[j] = sm.sc[wid][j * 64 + lane];
+
+    // ---- exact top-k of this partition, in index order -> workspace
+    const uint32_t want = (uint32_t)(nvalid < topk ? nvalid : topk);
+    uint32_t tau = 0, ties = 0;
+    const bool select_all = nvalid <= topk;
+    if (!select_all) {
+        uint32_t prefix = 0, pmask = 0, remaining = (uint32_t)topk;
+        for (int shift = 24; shift >= 0; shift -= 8) {
+            clear_hist(sm);
+#pragma unroll
+            for (int j = 0; j < ROUNDS; ++j)
+                if (u[j] != 0u && (u[j] & pmask) == prefix) atomicAdd(&sm.hist[wid][(u[j] >> shift) & 255u], 1u);
+            pick_digit(sm, remaining);
+            prefix |= sm.pick[0] << shift;
+            pmask |= 0xffu << shift;
+            remaining = sm.pick[1];
+        }
+        tau = prefix;
+        ties = remaining;
+    }
+    // Element order is (wave, round, lane) = ascending key.
+    uint32_t neq = 0;
+#pragma unroll
+    for (int j = 0; j < ROUNDS; ++j)
+        neq += (uint32_t)__builtin_popcountll(wave_ballot(!select_all && u[j] != 0u && u[j] == tau));
+    uint32_t total;
+    uint32_t eq_before = block_excl_scan(lane == 0 ? neq : 0u, sm, total);
+    eq_before = (uint32_t)__shfl(eq_before, 0);
+    uint32_t keepbits = 0, nkeep = 0;
+#pragma unroll
+    for (int j = 0; j < ROUNDS; ++j) {
+        const bool valid = u[j] != 0u;
+        const bool eq = !select_all && valid && u[j] == tau;
+        const uint64_t meq = wave_ballot(eq);
+        const bool keep = valid && (select_all || u[j] > tau || (eq && eq_before + lanes_below(meq) < ties));
+        eq_before += (uint32_t)__builtin_popcountll(meq);
+        const uint64_t mk = wave_ballot(keep);
+        keepbits |= keep ? (1u << j) : 0u;
+        nkeep += (uint32_t)__builtin_popcountll(mk);
+    }
+    uint32_t out = block_excl_scan(lane == 0 ? nkeep : 0u, sm, total);
+    out = (uint32_t)__shfl(out, 0);
+    const long long cbase = (r * P + p) * (long long)topk;
+#pragma unroll
+    for (int j = 0; j < ROUNDS; ++j) {
+        const bool keep = (keepbits >> j) & 1u;
+        const uint64_t mk = wave_ballot(keep);
+        const uint32_t pos = out + lanes_below(mk);
+        if (keep && pos < want) {
+            cand_s[cbase + pos] = key_float(u[j]);
+            cand_i[cbase + pos] = (int)(pbase + (long long)wid * WAVE_KEYS + j * 64 + lane);
+        }
+        out += (uint32_t)__builtin_popcountll(mk);
+    }
+    if (tid == 0) cand_n[r * P + p] = want;
+
+    // ---- arrival: the last workgroup of the row merges
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) sm.last = atomicAdd(&ctr[r], 1u) == (uint32_t)(P - 1);
+    __syncthreads();
+    if (!sm.last) return;
+    __threadfence();
+
+    for (int q = tid; q < P; q += THREADS) sm.pn[q] = __atomic_load_n(&cand_n[r * P + q], __ATOMIC_RELAXED);
+    __syncthreads();
+    uint32_t N = 0;
+    for (int q = 0; q < P; ++q) N += sm.pn[q];
+    const int E = P * topk;  // <= kSplitMaxParts * DS4IDX_MAX_TOPK
+    const float *rs = cand_s + r * E;
+    const int *ri = cand_i + r * E;
+    const bool all = N <= (uint32_t)topk;
+    uint32_t mtau = 0, mties = 0;
+    if (!all) {
+        uint32_t prefix = 0, pmask = 0, remaining = (uint32_t)topk;
+        for (int shift = 24; shift >= 0; shift -= 8) {
+            clear_hist(sm);
+            for (int e = tid; e < E; e += THREADS) {
+                const int q = e / topk;
+                if ((uint32_t)(e - q * topk) >= sm.pn[q]) continue;
+                const uint32_t uu = ord_key(rs[e]);
+                if ((uu & pmask) == prefix) atomicAdd(&sm.hist[wid][(uu >> shift) & 255u], 1u);
+            }
+            pick_digit(sm, remaining);
+            prefix |= sm.pick[0] << shift;
+            pmask |= 0xffu << shift;
+            remaining = sm.pick[1];
+        }
+        mtau = prefix;
+        mties = remaining;
+    }
+    // Ordered output: thread-contiguous chunks of the (partition, position) space.
+    const int chunk = (E + THREADS - 1) / THREADS;
+    const int e0 = tid * chunk;
+    const int e1 = e0 + chunk < E ? e0 + chunk : E;
+    uint32_t my_eq = 0;
+    for (int e = e0; e < e1; ++e) {
+        const int q = e / topk;
+        if ((uint32_t)(e - q * topk) >= sm.pn[q]) continue;
+        my_eq += (!all && ord_key(rs[e]) == mtau) ? 1u : 0u;
+    }
+    uint32_t eq_base = block_excl_scan(my_eq, sm, total);
+    uint32_t my_keep = 0, run = eq_base;
+    for (int e = e0; e < e1; ++e) {
+        const int q = e / topk;
+        if ((uint32_t)(e - q * topk) >= sm.pn[q]) continue;
+        const uint32_t uu = ord_key(rs[e]);
+        const bool eq = !all && uu == mtau;
+        my_keep += (all || uu > mtau || (eq && run < mties)) ? 1u : 0u;
+        run += eq ? 1u : 0u;
+    }
+    uint32_t pos = block_excl_scan(my_keep, sm, total);
+    const uint32_t m = N < (uint32_t)topk ? N : (uint32_t)topk;
+    int *io = idx + r * topk;
+    float *vo = vals ? vals + r * topk : nullptr;
+    run = eq_base;
+    for (int e = e0; e < e1; ++e) {
+        const int q = e / topk;
+        if ((uint32_t)(e - q * topk) >= sm.pn[q]) continue;
+        const float sv = rs[e];
+        const uint32_t uu = ord_key(sv);
+        const bool eq = !all && uu == mtau;
+        const bool keep = all || uu > mtau || (eq && run < mties);
+        run += eq ? 1u : 0u;
+        if (keep && pos < m) {
+            io[pos] = ri[e];
+            if (vo) vo[pos] = sv;
+        }
+        pos += keep ? 1u : 0u;
+    }
+    for (int j = (int)m + tid; j < topk; j += THREADS) {
+        io[j] = -1;
+        if (vo) vo[j] = -INFINITY;
+    }
+    if (tid == 0) ctr[r] = 0u;
+}
+
+template <bool KFP8>
+hipError_t launch_t(const Problem &p, const void *Q, const void *K, const float *Ks, const float *W,
+                    int k, int *idx, float *vals, void *ws, hipStream_t st)
+{
+    const int rows = p.B * p.T;
+    const int P = split_parts(p);
+    SplitWorkspace w = split_workspace(ws, p, k);
+    hipLaunchKernelGGL((split_indexer_kernel<KFP8>), dim3(P, rows), dim3(THREADS), 0, st,
+                       static_cast<const uint16_t *>(Q), static_cast<const uint8_t *>(K), Ks, W,
+                       p.T, p.S, p.offset, k, P, w.ctr, w.cand_n, w.cand_s, w.cand_i, idx, vals);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+int split_parts(const Problem &p)
+{
+    const long long maxL = p.offset + p.T;
+    return (int)((maxL + PART - 1) / PART);
+}
+
+static size_t align256(size_t n) { return (n + 255) / 256 * 256; }
+
+size_t split_workspace_bytes(const Problem &p, int k)
+{
+    const size_t rows = (size_t)p.B * p.T, P = (size_t)split_parts(p);
+    return align256(rows * 4) + align256(rows * P * 4) + 2 * align256(rows * P * (size_t)k * 4);
+}
+
+SplitWorkspace split_workspace(void *ws, const Problem &p, int k)
+{
+    const size_t rows = (size_t)p.B * p.T, P = (size_t)split_parts(p);
+    char *c = static_cast<char *>(ws);
+    SplitWorkspace w;
+    w.ctr = reinterpret_cast<uint32_t *>(c);
+    c += align256(rows * 4);
+    w.cand_n = reinterpret_cast<uint32_t *>(c);
+    c += align256(rows * P * 4);
+    w.cand_s = reinterpret_cast<float *>(c);
+    c += align256(rows * P * (size_t)k * 4);
+    w.cand_i = reinterpret_cast<int *>(c);
+    return w;
+}
+
+hipError_t launch_split_select(const Problem &p, const void *Q, const void *K, const float *Ks,
+                               const float *W, int k, int *idx, float *vals, void *ws, hipStream_t st)
+{
+    if (p.k_dtype == FP8) return launch_t<true>(p, Q, K, Ks, W, k, idx, vals, ws, st);
+    return launch_t<false>(p, Q, K, Ks, W, k, idx, vals, ws, st);
+}
+
+}  // namespace ds4idx

@@ -114,23 +114,32 @@ def test_workspace_sizes_and_checks():
     L = ds.lib()
     prev = ds.set_impl("auto")
     try:
-        p = _prob()
-        assert ds.workspace_bytes(p, 512, ds.OP_SCORE) == 0
-        assert ds.workspace_bytes(p, 512, ds.OP_TOPK) == 0
-        # the MFMA path needs no workspace; the plain path materialises the scores
-        assert ds.workspace_bytes(p, 512) == 0
-        big = ds.workspace_bytes(p, 1024)
-        assert big >= p.B * p.T * p.S * 4 and big % 256 == 0
-        st = L.ds4idx_select(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, 1024, FAKE, None, None, 0, None)
+        # Enough rows to fill the GPU: the MFMA prefill kernel, no workspace.
+        p_pre = _prob(T=2048, S=4096, causal_offset=2048)
+        assert ds.workspace_bytes(p_pre, 512, ds.OP_SCORE) == 0
+        assert ds.workspace_bytes(p_pre, 512, ds.OP_TOPK) == 0
+        assert ds.workspace_bytes(p_pre, 512) == 0
+        # Few rows (decode-like): the split-key kernel; counters + candidates.
+        p_dec = _prob(B=8, T=1, S=262144, causal_offset=262143)
+        need = ds.workspace_bytes(p_dec, 512)
+        parts = 262144 // 8192
+        assert need >= 8 * 4 + 8 * parts * 4 + 2 * 8 * parts * 512 * 4 and need % 256 == 0
+        st = L.ds4idx_select(ctypes.byref(p_dec), FAKE, FAKE, FAKE, FAKE, 512, FAKE, None, None, 0, None)
         assert st == ds.ERR_WORKSPACE
-        st = L.ds4idx_select(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, 1024, FAKE, None,
-                             ctypes.c_void_p(0x10100), big - 1, None)
+        st = L.ds4idx_select(ctypes.byref(p_dec), FAKE, FAKE, FAKE, FAKE, 512, FAKE, None,
+                             ctypes.c_void_p(0x10100), need - 1, None)
         assert st == ds.ERR_WORKSPACE
+        st = L.ds4idx_select(ctypes.byref(p_dec), FAKE, FAKE, FAKE, FAKE, 512, FAKE, None,
+                             ctypes.c_void_p(0x10080), need, None)  # not 256-byte aligned
+        assert st == ds.ERR_WORKSPACE
+        # The plain kernels materialise the scores.
         ds.set_impl("ref")
-        assert ds.workspace_bytes(p, 512) >= p.B * p.T * p.S * 4
-        # forcing the MFMA family on a shape it does not cover
+        assert ds.workspace_bytes(p_pre, 512) >= p_pre.B * p_pre.T * p_pre.S * 4
+        # Forcing the MFMA family on a shape it does not cover.
         ds.set_impl("opt")
         p2 = _prob(H=4, D=64, q_dtype=ds.F32, k_dtype=ds.F32)
         assert L.ds4idx_score(ctypes.byref(p2), FAKE, FAKE, None, FAKE, FAKE, None) == ds.ERR_UNSUPPORTED
+        assert L.ds4idx_select(ctypes.byref(p2), FAKE, FAKE, None, FAKE, 8, FAKE, None, None, 0,
+                               None) == ds.ERR_UNSUPPORTED
     finally:
         ds.set_impl(prev)

@@ -185,15 +185,25 @@ def test_negative_weights_zero_ties():
 
 # ------------------------------------------------------------------ consistency
 
-def test_fused_equals_score_then_topk():
-    wl = W.prefill_fp8(seed=12, T=300, S=5000, offset=4700, chunk=300)
+@pytest.mark.parametrize("T", [1024, 300])
+def test_fused_equals_score_then_topk(T):
+    # T=1024 runs the prefill kernel, whose scorer arithmetic is that of
+    # ds4idx_score: bit-identical. T=300 runs the split-key kernel, which sums
+    # the same products in another order: equal up to fp32 rounding.
+    wl = W.prefill_fp8(seed=12, T=T, S=5000, offset=5000 - T, chunk=T)
     q, k, ks, w = to_device(wl)
     idx, vals = ds.select(q, k, ks, w, wl.offset, 512)
     sc = ds.score(q, k, ks, w, wl.offset)
     idx2, vals2 = ds.topk(sc, 512, wl.offset)
     torch.cuda.synchronize()
-    assert torch.equal(idx, idx2)
-    assert torch.equal(vals, vals2)
+    if T == 1024:
+        assert torch.equal(idx, idx2)
+        assert torch.equal(vals, vals2)
+    else:
+        same = (idx == idx2).all(dim=-1)
+        assert same.float().mean() > 0.9
+        ok = idx >= 0
+        assert torch.allclose(vals[same][ok[same]], vals2[same][ok[same]], rtol=1e-5, atol=1e-5)
     # the scorer's masked region is -inf, the visible part finite
     lim = wl.offset + torch.arange(wl.T, device="cuda")
     cols = torch.arange(wl.S, device="cuda")
@@ -233,8 +243,43 @@ def test_deterministic_repeat():
     assert np.array_equal(a, b) and np.array_equal(av.view(np.uint32), bv.view(np.uint32))
 
 
-def test_large_k_routes_to_plain_kernels():
-    wl = W.prefill_fp8(seed=15, T=20, S=3000, offset=2980, topk=1500, chunk=20)
-    gi, gv = run_select(wl)
+@pytest.mark.parametrize("impl", ["auto", "ref"])
+def test_large_k(impl):
+    # k = 1500 > 512: the split-key kernel (few rows) or the plain kernels.
+    ds.set_impl(impl)
+    wl = W.prefill_fp8(seed=15, T=20, S=30000, offset=29980, topk=1500, chunk=20)
+    gi, gv = run_select(wl, poison=True)
     check_invariants(wl, gi)
     compare_rows(wl, np.arange(wl.T), gi, gv, exact=False)
+
+
+@pytest.mark.parametrize("B,T,S,offset,topk,kdt", [
+    (3, 1, 20000, 19999, 512, "fp8"),     # partial last partition
+    (2, 5, 8192 * 3, 8192 * 3 - 5, 512, "fp8"),  # several queries per stream, exact partitions
+    (1, 2, 700, 698, 512, "fp8"),         # rows shorter than k
+    (2, 3, 40000, 39997, 64, "bf16"),     # bf16 keys
+    (4, 1, 9000, 8999, 1, "fp8"),         # k = 1
+])
+def test_split_kernel_shapes(B, T, S, offset, topk, kdt):
+    if kdt == "fp8":
+        wl = W.prefill_fp8(seed=60 + T, T=T, S=S, offset=offset, topk=topk, B=B, chunk=T)
+    else:
+        wl = W.prefill_bf16(seed=60 + T, T=T, S=S, offset=offset, topk=topk, B=B)
+    wl.chunks = [(0, T, S, offset)]
+    _say(f"split B={B} T={T} S={S} offset={offset} k={topk} {kdt}")
+    gi, gv = run_select(wl, poison=True)
+    check_invariants(wl, gi)
+    compare_rows(wl, np.arange(B * T), gi, gv, exact=False)
+    # three calls on one workspace: the arrival counters must return to zero
+    q, k, ks, w = to_device(wl)
+    ws = ds.new_workspace(ds.make_problem(q, k, offset), topk)
+    for _ in range(3):
+        idx, _v = ds.select(q, k, ks, w, offset, topk, workspace=ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(idx.reshape(B * T, topk).cpu().numpy(), gi)
+
+
+def test_split_int_exact():
+    wl = W.prefill_bf16_int(seed=77, T=2, S=50000, offset=49998, topk=512, B=3)
+    gi, gv = run_select(wl, poison=True)
+    compare_rows(wl, np.arange(6), gi, gv, exact=True)
