@@ -1,7 +1,7 @@
 // C-ABI entry points of libds4idx (declared in include/ds4idx.h): argument
 // validation (always before any HIP call), workspace sizing, and dispatch to
 // the MFMA kernels or the plain kernels.
-#include "../../include/ds4idx.h"
+#include "ds4idx.h"
 
 #include <atomic>
 #include <cstdlib>

@@ -5,23 +5,25 @@
 // merge cascade; first page, section details, first and second paragraphs)
 // are prior art for a different GPU. This kernel is laid out for CDNA4:
 //
-//  * Work split. A 256-thread workgroup owns 8 consecutive query tokens of one
-//    batch row; each of its four wavefronts owns two tokens and keeps their
-//    queries (2 tokens x 64 heads x 128 dims, bf16) resident in VGPRs as MFMA
-//    A operands for the whole key loop.
-//  * Keys. Tiles of 64 keys are staged global -> registers -> LDS, double
+//  * Work split. A 512-thread workgroup owns 8 consecutive query tokens of one
+//    batch row; each of its eight wavefronts owns one token and keeps its
+//    query (64 heads x 128 dims, bf16) resident in VGPRs as MFMA A operands
+//    for the whole key loop. Two wavefronts share each SIMD, so one's LDS
+//    waits and epilogue overlap the other's matrix work.
+//  * Keys. Tiles of 128 keys are staged global -> registers -> LDS, double
 //    buffered, once per workgroup. E4M3 codes are widened to bf16 on the way
 //    into LDS (exact: every E4M3 value is a bf16 value); the per-token fp32
 //    scale is kept aside and applied once to the head-reduced score (allowed
 //    since the scale is positive, so it commutes with the ReLU).
 //  * Contraction. Heads sit on the M dimension of v_mfma_f32_32x32x16_bf16:
-//    one token = two 32-row head blocks, 32 keys per block on N, 8 k-steps
-//    over D = 128. fp32 accumulation.
-//  * Epilogue in registers. Each lane holds 16 head rows of one key per
-//    block: ReLU, times w[t,h] (fp32), summed in-lane; the two lane halves
-//    hold disjoint head rows, and one v_permlane32_swap brings token 0's
-//    halves together in lanes 0-31 and token 1's in lanes 32-63. The causal
-//    mask (key <= offset + t) is applied per lane.
+//    two 32-row head blocks, 32 keys per block on N, 8 k-steps over D = 128,
+//    fp32 accumulation. Two 32-key sub-blocks are scored together: four
+//    independent accumulator chains per k-step.
+//  * Epilogue in registers. Each lane holds 16 head rows of one key per head
+//    block: ReLU (one v_med3), times w[t,h] (fp32), summed in-lane. The two
+//    lane halves hold disjoint head rows; one v_permlane32_swap completes
+//    sub-block A's keys in lanes 0-31 and sub-block B's in lanes 32-63. The
+//    causal mask (key <= offset + t) is applied per lane.
 //  * Streaming top-k per token. A candidate buffer of 1024 (score, index)
 //    slots per token lives in LDS. A score enters only if it beats the
 //    token's running threshold (ballot + mbcnt place it in ascending key
@@ -42,10 +44,9 @@ namespace {
 
 constexpr int H = kMfmaH;   // indexer heads
 constexpr int D = kMfmaD;   // head dim
-constexpr int NWAVE = 4;    // wavefronts per workgroup
-constexpr int NTOK = 2;     // query tokens per wavefront
-constexpr int TQ = NWAVE * NTOK;
-constexpr int KT = 64;      // keys per LDS tile
+constexpr int NWAVE = 8;    // wavefronts per workgroup, one query token each
+constexpr int TQ = NWAVE;
+constexpr int KT = 128;     // keys per LDS tile
 constexpr int KROW = D + 8; // bf16 per LDS key row: 272 B keeps 16-byte reads conflict-free
 constexpr int CAP = 1024;   // candidate slots per token
 constexpr int THREADS = NWAVE * 64;
@@ -64,6 +65,9 @@ struct alignas(16) Smem {
 // Row (head within the 32-row block) that accumulator element i of `lane`
 // holds in the 32x32 MFMA output; the column (key) is lane % 32.
 __device__ __forceinline__ int acc_row(int i, int lane) { return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3); }
+
+// max(x, 0) in one instruction (scores stay far below the upper clamp).
+__device__ __forceinline__ float relu(float x) { return __builtin_amdgcn_fmed3f(x, 0.0f, 3.0e38f); }
 
 // Wavefront-wide: reduce the candidate buffer (cs, ci)[0..n) with n > k to its
 // top-k in place, keeping index order; returns the k-th score (the new
@@ -197,34 +201,24 @@ __global__ __launch_bounds__(THREADS, 1) void mfma_indexer_kernel(
     const int nblk = (T + TQ - 1) / TQ;
     const int t0 = (nblk - 1 - (int)blockIdx.x) * TQ;  // longest rows first
     const int b = blockIdx.y;
+    const int tok = t0 + wid;
+    const bool tok_ok = tok < T;
+    const long long lim = tok_ok ? offset + tok : -1;  // last key this token sees
 
-    // This wavefront's two tokens.
-    int tok[NTOK];
-    long long lim[NTOK];
-    long long wave_lim = -1;
-#pragma unroll
-    for (int j = 0; j < NTOK; ++j) {
-        tok[j] = t0 + wid * NTOK + j;
-        lim[j] = tok[j] < T ? offset + tok[j] : -1;
-        wave_lim = lim[j] > wave_lim ? lim[j] : wave_lim;
-    }
-
-    // Queries as MFMA A operands: a[j][hb][ks] = Q[tok j, head hb*32 + lane%32,
+    // Query as MFMA A operands: a[hb][ks] = Q[tok, head hb*32 + lane%32,
     // dims ks*16 + (lane/32)*8 .. +7]. B operands use the same dim mapping.
-    bf16x8 a[NTOK][2][8];
-    float wv[NTOK][2][16];
-#pragma unroll
-    for (int j = 0; j < NTOK; ++j) {
-        const bool ok = tok[j] < T;
-        const long long qrow = ((long long)b * T + (ok ? tok[j] : 0)) * H;
+    bf16x8 a[2][8];
+    float wv[2][16];
+    {
+        const long long qrow = ((long long)b * T + (tok_ok ? tok : 0)) * H;
 #pragma unroll
         for (int hb = 0; hb < 2; ++hb) {
             const bf16x8 *qp = reinterpret_cast<const bf16x8 *>(
                 Q + (qrow + hb * 32 + (lane & 31)) * D + (lane >> 5) * 8);
 #pragma unroll
-            for (int ks = 0; ks < 8; ++ks) a[j][hb][ks] = ok ? qp[ks * 2] : bf16x8{};
+            for (int ks = 0; ks < 8; ++ks) a[hb][ks] = tok_ok ? qp[ks * 2] : bf16x8{};
 #pragma unroll
-            for (int i = 0; i < 16; ++i) wv[j][hb][i] = ok ? W[qrow + hb * 32 + acc_row(i, lane)] : 0.0f;
+            for (int i = 0; i < 16; ++i) wv[hb][i] = tok_ok ? W[qrow + hb * 32 + acc_row(i, lane)] : 0.0f;
         }
     }
 
@@ -233,9 +227,10 @@ __global__ __launch_bounds__(THREADS, 1) void mfma_indexer_kernel(
     const int ntiles = (int)((nkeys + KT - 1) / KT);
     const uint8_t *Kb = K + (size_t)b * S * (KFP8 ? D : 2 * D);
     const float *Ksb = KFP8 ? Ks + (size_t)b * S : nullptr;
-
-    int cnt[NTOK] = {0, 0};
-    float thr[NTOK] = {-INFINITY, -INFINITY};
+    float *cs = sm.cs[wid];
+    int *ci = sm.ci[wid];
+    int cnt = 0;
+    float thr = -INFINITY;
 
     TileRegs<KFP8> tr;
     float tsc;
@@ -243,111 +238,89 @@ __global__ __launch_bounds__(THREADS, 1) void mfma_indexer_kernel(
     store_tile<KFP8>(sm, 0, tr, tsc, tid);
     __syncthreads();
 
-    const int jt = lane >> 5;  // token this lane reports after the half swap
     for (int tile = 0; tile < ntiles; ++tile) {
         const int cur = tile & 1;
         if (tile + 1 < ntiles) load_tile<KFP8>(tr, tsc, Kb, Ksb, S, tile + 1, tid);
         const long long kbase = (long long)tile * KT;
-        if (kbase <= wave_lim) {
 #pragma unroll
-            for (int sb = 0; sb < KT / 32; ++sb) {
-                f32x16 acc[NTOK][2];
+        for (int pp = 0; pp < KT / 64; ++pp) {
+            const long long pbase = kbase + pp * 64;  // sub-blocks A = pbase.., B = pbase+32..
+            if (pbase <= lim) {
+                f32x16 acc[2][2];
 #pragma unroll
-                for (int j = 0; j < NTOK; ++j)
+                for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-                    for (int hb = 0; hb < 2; ++hb) acc[j][hb] = f32x16{};
-                const uint16_t *kp = &sm.k[cur][(sb * 32 + (lane & 31)) * KROW + (lane >> 5) * 8];
+                    for (int hb = 0; hb < 2; ++hb) acc[s2][hb] = f32x16{};
+                const uint16_t *kp = &sm.k[cur][(pp * 64 + (lane & 31)) * KROW + (lane >> 5) * 8];
 #pragma unroll
                 for (int ks = 0; ks < 8; ++ks) {
-                    const bf16x8 bk = *reinterpret_cast<const bf16x8 *>(kp + ks * 16);
+                    const bf16x8 bA = *reinterpret_cast<const bf16x8 *>(kp + ks * 16);
+                    const bf16x8 bB = *reinterpret_cast<const bf16x8 *>(kp + 32 * KROW + ks * 16);
 #pragma unroll
-                    for (int j = 0; j < NTOK; ++j)
-#pragma unroll
-                        for (int hb = 0; hb < 2; ++hb)
-                            acc[j][hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j][hb][ks], bk,
-                                                                                 acc[j][hb], 0, 0, 0);
+                    for (int hb = 0; hb < 2; ++hb) {
+                        acc[0][hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[hb][ks], bA, acc[0][hb], 0, 0, 0);
+                        acc[1][hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[hb][ks], bB, acc[1][hb], 0, 0, 0);
+                    }
                 }
-                float part[NTOK];
+                float part[2];
 #pragma unroll
-                for (int j = 0; j < NTOK; ++j) {
+                for (int s2 = 0; s2 < 2; ++s2) {
                     float s4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                     for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
                         for (int i = 0; i < 16; ++i)
-                            s4[i & 3] = fmaf(wv[j][hb][i], fmaxf(acc[j][hb][i], 0.0f), s4[i & 3]);
-                    part[j] = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+                            s4[i & 3] = fmaf(wv[hb][i], relu(acc[s2][hb][i]), s4[i & 3]);
+                    part[s2] = (s4[0] + s4[1]) + (s4[2] + s4[3]);
                 }
                 const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0]),
                                                                  __float_as_uint(part[1]), false, false);
                 float sc = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-                const int kin = sb * 32 + (lane & 31);
+                const int kin = pp * 64 + lane;
                 if (KFP8) sc *= sm.scale[cur][kin];
                 sc = canon(sc);
                 const long long key = kbase + kin;
-                const long long mylim = jt ? lim[1] : lim[0];
-                const bool vis = key <= mylim;
+                const bool vis = key <= lim;
                 if (SCORE) {
-                    const int t = jt ? tok[1] : tok[0];
-                    if (t < T && key < S)
-                        scores[((long long)b * T + t) * S + key] = vis ? sc : -INFINITY;
+                    if (tok_ok && key < S) scores[((long long)b * T + tok) * S + key] = vis ? sc : -INFINITY;
                 } else {
-                    const float th = jt ? thr[1] : thr[0];
-                    const bool pass = vis && sc > th;
+                    const bool pass = vis && sc > thr;
                     const uint64_t m = wave_ballot(pass);
                     if (m) {
-                        const uint32_t n0 = (uint32_t)__builtin_popcount((uint32_t)m);
-                        const uint32_t below = lanes_below(m);
-                        const int slot = wid * NTOK + jt;
-                        const int pos = jt ? cnt[1] + (int)(below - n0) : cnt[0] + (int)below;
+                        const int pos = cnt + (int)lanes_below(m);
                         if (pass) {
-                            sm.cs[slot][pos] = sc;
-                            sm.ci[slot][pos] = (int)key;
+                            cs[pos] = sc;
+                            ci[pos] = (int)key;
                         }
-                        cnt[0] += (int)n0;
-                        cnt[1] += (int)__builtin_popcount((uint32_t)(m >> 32));
-#pragma unroll
-                        for (int j = 0; j < NTOK; ++j) {
-                            if (cnt[j] > CAP - 32) {
-                                wave_lds_sync();
-                                thr[j] = wave_keep_topk(sm.cs[wid * NTOK + j], sm.ci[wid * NTOK + j],
-                                                        cnt[j], topk, sm.hist[wid], lane);
-                                cnt[j] = topk;
-                            }
+                        cnt += __builtin_popcountll(m);
+                        if (cnt > CAP - 64) {
+                            wave_lds_sync();
+                            thr = wave_keep_topk(cs, ci, cnt, topk, sm.hist[wid], lane);
+                            cnt = topk;
                         }
                     }
                 }
-            }
-        } else if (SCORE) {
-#pragma unroll
-            for (int j = 0; j < NTOK; ++j) {
-                if (tok[j] >= T) continue;
-                float *orow = scores + ((long long)b * T + tok[j]) * S;
-                for (int i = lane; i < KT; i += 64)
-                    if (kbase + i < S) orow[kbase + i] = -INFINITY;
+            } else if (SCORE && tok_ok) {
+                float *orow = scores + ((long long)b * T + tok) * S;
+                const long long key = pbase + lane;
+                if (key < S) orow[key] = -INFINITY;
             }
         }
         if (tile + 1 < ntiles) store_tile<KFP8>(sm, cur ^ 1, tr, tsc, tid);
         __syncthreads();
     }
 
-    if (!SCORE) {
-#pragma unroll
-        for (int j = 0; j < NTOK; ++j) {
-            if (tok[j] >= T) continue;
-            float *cs = sm.cs[wid * NTOK + j];
-            int *ci = sm.ci[wid * NTOK + j];
-            wave_lds_sync();
-            if (cnt[j] > topk) {
-                wave_keep_topk(cs, ci, cnt[j], topk, sm.hist[wid], lane);
-                cnt[j] = topk;
-            }
-            const long long orow = ((long long)b * T + tok[j]) * topk;
-            for (int i = lane; i < topk; i += 64) {
-                const bool have = i < cnt[j];
-                idx[orow + i] = have ? ci[i] : -1;
-                if (vals) vals[orow + i] = have ? cs[i] : -INFINITY;
-            }
+    if (!SCORE && tok_ok) {
+        wave_lds_sync();
+        if (cnt > topk) {
+            wave_keep_topk(cs, ci, cnt, topk, sm.hist[wid], lane);
+            cnt = topk;
+        }
+        const long long orow = ((long long)b * T + tok) * topk;
+        for (int i = lane; i < topk; i += 64) {
+            const bool have = i < cnt;
+            idx[orow + i] = have ? ci[i] : -1;
+            if (vals) vals[orow + i] = have ? cs[i] : -INFINITY;
         }
     }
 }

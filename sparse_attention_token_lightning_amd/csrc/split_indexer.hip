@@ -13,13 +13,19 @@
 //    key (four 16-byte loads; the two halves of a wave cover each 128-byte fp8
 //    row). Queries use the same assignment. E4M3 widens to bf16 in registers.
 //    The next round's keys are in flight while the current one is scored.
-//  * Scores stay in registers (16 per lane). The partition's exact top-k is
-//    found by block-wide radix selection over an order-preserving 32-bit key
-//    (per-wavefront LDS histograms, four 8-bit digits) and written, in index
+//  * The partition's exact top-k is found by block-wide radix selection over
+//    an order-preserving 32-bit key held in registers (16 per lane). Each
+//    digit pass first reduces the AND and OR of the keys still in play and
+//    starts its 8-bit window at their highest differing bit, so bits that
+//    every live key shares cost nothing and the histogram spreads over
+//    bins instead of piling onto one (the candidates of a row are all top
+//    scores and share their high bits). The selected keys go, in index
 //    order, to the workspace.
 //  * The last workgroup of a row to finish (device-scope arrival counter)
-//    merges the row's P candidate lists with the same exact selection and
-//    writes the final indices in ascending order, then resets the counter.
+//    merges the row's P candidate lists: they are staged through LDS with
+//    coalesced loads, each thread keeps a contiguous run in registers, the
+//    same selection runs, and one block-wide scan orders the output. The
+//    counter is reset for the next call.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -33,12 +39,18 @@ constexpr int THREADS = NW * 64;
 constexpr int ROUNDS = 16;
 constexpr int WAVE_KEYS = ROUNDS * 64;
 constexpr int PART = NW * WAVE_KEYS;  // 8192
+constexpr int MREG = 32;              // merge keys held per thread
+constexpr int MSTAGE = THREADS * MREG;  // candidates the merge stages in LDS
 
 typedef __attribute__((__vector_size__(8 * sizeof(short)))) short bf16x8;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 
 struct SplitSmem {
-    uint32_t sc[NW][WAVE_KEYS];  // order-preserving score keys, 0 = no key
+    union {
+        uint32_t sc[NW][WAVE_KEYS];            // partition score keys, 0 = no key
+        uint32_t stage[MSTAGE + MSTAGE / 32];  // merge staging, one pad word per 32
+    };
+    uint32_t red[3][NW];
     uint32_t hist[NW][256];
     uint32_t tot[256];
     uint32_t wsum[NW];
@@ -46,6 +58,18 @@ struct SplitSmem {
     uint32_t pn[kSplitMaxParts];
     int last;
 };
+
+template <class V>
+__device__ __forceinline__ void store_agent(V *p, V v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <class V>
+__device__ __forceinline__ V load_agent(const V *p)
+{
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 __device__ __forceinline__ int acc_row(int i, int lane) { return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3); }
 
@@ -79,9 +103,37 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, SplitSmem &sm, u
     return before + x - v;
 }
 
-// One radix digit step shared by both selections: after every thread has
-// added its keys to its wavefront's histogram, find the digit of the k-th
-// largest key and how many keys of that digit are still wanted.
+// Block-wide sum, AND and OR.
+__device__ __forceinline__ void block_reduce3(uint32_t &s, uint32_t &a, uint32_t &o, SplitSmem &sm)
+{
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        s += __shfl_xor(s, off);
+        a &= __shfl_xor(a, off);
+        o |= __shfl_xor(o, off);
+    }
+    if (lane == 0) {
+        sm.red[0][wid] = s;
+        sm.red[1][wid] = a;
+        sm.red[2][wid] = o;
+    }
+    __syncthreads();
+    s = 0u;
+    a = ~0u;
+    o = 0u;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        s += sm.red[0][w];
+        a &= sm.red[1][w];
+        o |= sm.red[2][w];
+    }
+    __syncthreads();
+}
+
+// After every thread has added its keys to its wavefront's histogram, find
+// the digit of the k-th largest key and how many keys of that digit are
+// still wanted (sm.pick).
 __device__ __forceinline__ void pick_digit(SplitSmem &sm, uint32_t remaining)
 {
     const int tid = threadIdx.x, lane = tid & 63;
@@ -124,23 +176,68 @@ __device__ __forceinline__ void pick_digit(SplitSmem &sm, uint32_t remaining)
     __syncthreads();
 }
 
-__device__ __forceinline__ void clear_hist(SplitSmem &sm)
+// Exact k-th largest key among the keys this block holds (0 = no key; more
+// than k keys present). each(f) calls f(key) for every key of the calling
+// thread. Returns tau, the k-th largest key, and ties, how many keys equal
+// to tau belong to the top k (the lowest-index ones).
+template <class Each>
+__device__ void block_select(Each each, uint32_t k, SplitSmem &sm, uint32_t &tau, uint32_t &ties)
 {
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-    for (int b = lane; b < 256; b += 64) sm.hist[wid][b] = 0;
-    wave_lds_sync();
+    uint32_t prefix = 0, pmask = 0, remaining = k;
+    {
+        // When at least k scores are >= +0, the k-th largest is too.
+        uint32_t nn = 0, a = 0, o = 0;
+        each([&](uint32_t u) { nn += u >= 0x80000000u ? 1u : 0u; });
+        block_reduce3(nn, a, o, sm);
+        if (nn >= k) prefix = pmask = 0x80000000u;
+    }
+    while (pmask != ~0u) {
+        uint32_t n = 0, a = ~0u, o = 0u;
+        each([&](uint32_t u) {
+            if ((u & pmask) == prefix) {
+                a &= u;
+                o |= u;
+            }
+        });
+        block_reduce3(n, a, o, sm);
+        const uint32_t diff = (a ^ o) & ~pmask;
+        if (diff == 0u) {  // every key still in play is equal: that is tau
+            prefix = a;
+            break;
+        }
+        const int hb = 31 - __builtin_clz(diff);
+        const uint32_t above = hb == 31 ? 0u : (~0u << (hb + 1));
+        prefix = (prefix & pmask) | (a & above & ~pmask);
+        pmask |= above;
+        const int lo = hb >= 7 ? hb - 7 : 0;
+        const uint32_t dmask = (2u << (hb - lo)) - 1u;
+        for (int b = lane; b < 256; b += 64) sm.hist[wid][b] = 0;
+        wave_lds_sync();
+        each([&](uint32_t u) {
+            if ((u & pmask) == prefix) atomicAdd(&sm.hist[wid][(u >> lo) & dmask], 1u);
+        });
+        pick_digit(sm, remaining);
+        prefix |= sm.pick[0] << lo;
+        pmask |= dmask << lo;
+        remaining = sm.pick[1];
+    }
+    tau = prefix;
+    ties = remaining;
 }
 
 // This lane's half of one key row of a 32-key sub-block (key = base + lane%32,
-// dims half*64 .. +63): 64 bytes of E4M3 codes or 128 bytes of bf16.
+// dims half*64 .. +63): 64 bytes of E4M3 codes or 128 bytes of bf16; for the
+// first sub-block of a pair also the scale of key base + lane.
 template <bool KFP8>
 struct Raw {
     uint4 v[KFP8 ? 4 : 8];
+    float scale;
 };
 
-template <bool KFP8>
-__device__ __forceinline__ void load_sub(Raw<KFP8> &r, const uint8_t *Kr, long long kbase,
-                                         long long L, int lane)
+template <bool KFP8, bool SCALE>
+__device__ __forceinline__ void load_sub(Raw<KFP8> &r, const uint8_t *Kr, const float *Ksr,
+                                         long long kbase, long long L, int lane)
 {
     constexpr int NV = KFP8 ? 4 : 8;
     constexpr int ROWB = KFP8 ? D : 2 * D;
@@ -152,6 +249,10 @@ __device__ __forceinline__ void load_sub(Raw<KFP8> &r, const uint8_t *Kr, long l
     } else {
 #pragma unroll
         for (int j = 0; j < NV; ++j) r.v[j] = make_uint4(0, 0, 0, 0);
+    }
+    if (KFP8 && SCALE) {
+        const long long sk = kbase + lane;
+        r.scale = sk < L ? Ksr[sk] : 1.0f;
     }
 }
 
@@ -170,7 +271,7 @@ __device__ __forceinline__ bf16x8 b_operand(const Raw<KFP8> &r, int ks)
     }
 }
 
-// Partial (this lane's 16 head rows of each head block) score of one sub-block.
+// Partial score of one sub-block: this lane's 16 head rows of each head block.
 template <bool KFP8>
 __device__ __forceinline__ float score_sub(const Raw<KFP8> &r, const bf16x8 (&a)[2][8],
                                            const float (&wv)[2][16])
@@ -187,7 +288,8 @@ __device__ __forceinline__ float score_sub(const Raw<KFP8> &r, const bf16x8 (&a)
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) s4[i & 3] = fmaf(wv[hb][i], fmaxf(acc[hb][i], 0.0f), s4[i & 3]);
+        for (int i = 0; i < 16; ++i)
+            s4[i & 3] = fmaf(wv[hb][i], __builtin_amdgcn_fmed3f(acc[hb][i], 0.0f, 3.0e38f), s4[i & 3]);
     return (s4[0] + s4[1]) + (s4[2] + s4[3]);
 }
 
@@ -207,6 +309,7 @@ __global__ __launch_bounds__(THREADS, 1) void split_indexer_kernel(
     const long long pbase = (long long)p * PART;
     const long long nvalid = L - pbase < 0 ? 0 : (L - pbase > PART ? PART : L - pbase);
 
+    // ---- score this wavefront's 1024 keys into sm.sc
     const long long wbase = pbase + (long long)wid * WAVE_KEYS;
     const long long wkeys = L - wbase < 0 ? 0 : (L - wbase > WAVE_KEYS ? WAVE_KEYS : L - wbase);
     if (wkeys > 0) {
@@ -230,23 +333,33 @@ __global__ __launch_bounds__(THREADS, 1) void split_indexer_kernel(
         const int nsub = (int)((wkeys + 63) / 64) * 2;
         Raw<KFP8> buf[NBUF];
 #pragma unroll
-        for (int i = 0; i < NBUF - 1; ++i)
-            if (i < nsub) load_sub<KFP8>(buf[i], Kr, wbase + 32 * i, L, lane);
-        float prev = 0.0f;
+        for (int i = 0; i < NBUF - 1; ++i) {
+            if (i < nsub) {
+                if (i & 1) load_sub<KFP8, false>(buf[i], Kr, Ksr, wbase + 32 * i, L, lane);
+                else load_sub<KFP8, true>(buf[i], Kr, Ksr, wbase + 32 * i, L, lane);
+            }
+        }
+        float prev = 0.0f, pscale = 1.0f;
         for (int sb0 = 0; sb0 < nsub; sb0 += NBUF) {
 #pragma unroll
             for (int i = 0; i < NBUF; ++i) {
                 const int sb = sb0 + i;
                 if (sb < nsub) {
-                    if (sb + NBUF - 1 < nsub)
-                        load_sub<KFP8>(buf[(i + NBUF - 1) % NBUF], Kr, wbase + 32 * (sb + NBUF - 1), L, lane);
+                    if (!(i & 1)) pscale = buf[i].scale;
+                    const int nx = sb + NBUF - 1;
+                    if (nx < nsub) {
+                        if ((i + NBUF - 1) & 1)
+                            load_sub<KFP8, false>(buf[(i + NBUF - 1) % NBUF], Kr, Ksr, wbase + 32 * nx, L, lane);
+                        else
+                            load_sub<KFP8, true>(buf[(i + NBUF - 1) % NBUF], Kr, Ksr, wbase + 32 * nx, L, lane);
+                    }
                     const float part = score_sub<KFP8>(buf[i], a, wv);
                     if (i & 1) {
                         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(prev),
                                                                          __float_as_uint(part), false, false);
                         float sc = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+                        if (KFP8) sc *= pscale;
                         const long long key = wbase + 32 * (sb - 1) + lane;
-                        if (KFP8) sc *= key < L ? Ksr[key] : 1.0f;
                         sm.sc[wid][32 * (sb - 1) + lane] = key < L ? ord_key(canon(sc)) : 0u;
                     } else {
                         prev = part;
@@ -255,33 +368,25 @@ __global__ __launch_bounds__(THREADS, 1) void split_indexer_kernel(
             }
         }
     }
-    for (int i = (int)(wkeys < 0 ? 0 : ((wkeys + 63) / 64) * 64) + lane; i < WAVE_KEYS; i += 64)
-        sm.sc[wid][i] = 0u;
+    for (int i = (int)(((wkeys + 63) / 64) * 64) + lane; i < WAVE_KEYS; i += 64) sm.sc[wid][i] = 0u;
     wave_lds_sync();
     uint32_t u[ROUNDS];
 #pragma unroll
     for (int j = 0; j < ROUNDS; ++j) u[j] = sm.sc[wid][j * 64 + lane];
 
-    // ---- exact top-k of this partition, in index order -> workspace
+    // ---- exact top-k of this partition, in index order (wave, round, lane)
     const uint32_t want = (uint32_t)(nvalid < topk ? nvalid : topk);
-    uint32_t tau = 0, ties = 0;
     const bool select_all = nvalid <= topk;
+    uint32_t tau = 0, ties = 0;
     if (!select_all) {
-        uint32_t prefix = 0, pmask = 0, remaining = (uint32_t)topk;
-        for (int shift = 24; shift >= 0; shift -= 8) {
-            clear_hist(sm);
+        block_select(
+            [&](auto f) {
 #pragma unroll
-            for (int j = 0; j < ROUNDS; ++j)
-                if (u[j] != 0u && (u[j] & pmask) == prefix) atomicAdd(&sm.hist[wid][(u[j] >> shift) & 255u], 1u);
-            pick_digit(sm, remaining);
-            prefix |= sm.pick[0] << shift;
-            pmask |= 0xffu << shift;
-            remaining = sm.pick[1];
-        }
-        tau = prefix;
-        ties = remaining;
+                for (int j = 0; j < ROUNDS; ++j)
+                    if (u[j] != 0u) f(u[j]);
+            },
+            (uint32_t)topk, sm, tau, ties);
     }
-    // Element order is (wave, round, lane) = ascending key.
     uint32_t neq = 0;
 #pragma unroll
     for (int j = 0; j < ROUNDS; ++j)
@@ -310,86 +415,133 @@ __global__ __launch_bounds__(THREADS, 1) void split_indexer_kernel(
         const uint64_t mk = wave_ballot(keep);
         const uint32_t pos = out + lanes_below(mk);
         if (keep && pos < want) {
-            cand_s[cbase + pos] = key_float(u[j]);
-            cand_i[cbase + pos] = (int)(pbase + (long long)wid * WAVE_KEYS + j * 64 + lane);
+            store_agent(&cand_s[cbase + pos], key_float(u[j]));
+            store_agent(&cand_i[cbase + pos], (int)(pbase + (long long)wid * WAVE_KEYS + j * 64 + lane));
         }
         out += (uint32_t)__builtin_popcountll(mk);
     }
-    if (tid == 0) cand_n[r * P + p] = want;
+    if (tid == 0) store_agent(&cand_n[r * P + p], want);
 
-    // ---- arrival: the last workgroup of the row merges
-    __threadfence();
+    // ---- arrival: the last workgroup of the row merges. The candidate lists
+    // travel through device-coherent (agent-scope) stores and loads, which
+    // bypass the per-XCD L2's non-coherent lines; waiting for every store to
+    // complete before the counter increment orders them, with no cache-wide
+    // writeback or invalidate.
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (tid == 0) sm.last = atomicAdd(&ctr[r], 1u) == (uint32_t)(P - 1);
+    if (tid == 0)
+        sm.last = __hip_atomic_fetch_add(&ctr[r], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                  (uint32_t)(P - 1);
     __syncthreads();
     if (!sm.last) return;
-    __threadfence();
 
-    for (int q = tid; q < P; q += THREADS) sm.pn[q] = __atomic_load_n(&cand_n[r * P + q], __ATOMIC_RELAXED);
+    for (int q = tid; q < P; q += THREADS) sm.pn[q] = load_agent(&cand_n[r * P + q]);
     __syncthreads();
     uint32_t N = 0;
     for (int q = 0; q < P; ++q) N += sm.pn[q];
     const int E = P * topk;  // <= kSplitMaxParts * DS4IDX_MAX_TOPK
     const float *rs = cand_s + r * E;
     const int *ri = cand_i + r * E;
-    const bool all = N <= (uint32_t)topk;
-    uint32_t mtau = 0, mties = 0;
-    if (!all) {
-        uint32_t prefix = 0, pmask = 0, remaining = (uint32_t)topk;
-        for (int shift = 24; shift >= 0; shift -= 8) {
-            clear_hist(sm);
-            for (int e = tid; e < E; e += THREADS) {
-                const int q = e / topk;
-                if ((uint32_t)(e - q * topk) >= sm.pn[q]) continue;
-                const uint32_t uu = ord_key(rs[e]);
-                if ((uu & pmask) == prefix) atomicAdd(&sm.hist[wid][(uu >> shift) & 255u], 1u);
-            }
-            pick_digit(sm, remaining);
-            prefix |= sm.pick[0] << shift;
-            pmask |= 0xffu << shift;
-            remaining = sm.pick[1];
-        }
-        mtau = prefix;
-        mties = remaining;
-    }
-    // Ordered output: thread-contiguous chunks of the (partition, position) space.
-    const int chunk = (E + THREADS - 1) / THREADS;
-    const int e0 = tid * chunk;
-    const int e1 = e0 + chunk < E ? e0 + chunk : E;
-    uint32_t my_eq = 0;
-    for (int e = e0; e < e1; ++e) {
-        const int q = e / topk;
-        if ((uint32_t)(e - q * topk) >= sm.pn[q]) continue;
-        my_eq += (!all && ord_key(rs[e]) == mtau) ? 1u : 0u;
-    }
-    uint32_t eq_base = block_excl_scan(my_eq, sm, total);
-    uint32_t my_keep = 0, run = eq_base;
-    for (int e = e0; e < e1; ++e) {
-        const int q = e / topk;
-        if ((uint32_t)(e - q * topk) >= sm.pn[q]) continue;
-        const uint32_t uu = ord_key(rs[e]);
-        const bool eq = !all && uu == mtau;
-        my_keep += (all || uu > mtau || (eq && run < mties)) ? 1u : 0u;
-        run += eq ? 1u : 0u;
-    }
-    uint32_t pos = block_excl_scan(my_keep, sm, total);
     const uint32_t m = N < (uint32_t)topk ? N : (uint32_t)topk;
+    const bool all = N <= (uint32_t)topk;
     int *io = idx + r * topk;
     float *vo = vals ? vals + r * topk : nullptr;
-    run = eq_base;
-    for (int e = e0; e < e1; ++e) {
-        const int q = e / topk;
-        if ((uint32_t)(e - q * topk) >= sm.pn[q]) continue;
-        const float sv = rs[e];
-        const uint32_t uu = ord_key(sv);
-        const bool eq = !all && uu == mtau;
-        const bool keep = all || uu > mtau || (eq && run < mties);
-        run += eq ? 1u : 0u;
-        if (keep && pos < m) {
-            io[pos] = ri[e];
-            if (vo) vo[pos] = sv;
+    // Element e = (partition, position) in index order; thread t owns the
+    // contiguous run [t*chunk, (t+1)*chunk), which keeps the output order.
+    const int chunk = (E + THREADS - 1) / THREADS;
+    const int e0 = tid * chunk;
+    if (chunk <= MREG) {
+        for (int q = 0; q < P; ++q)
+            for (int pos = tid; pos < topk; pos += THREADS) {
+                const int e = q * topk + pos;
+                sm.stage[e + (e >> 5)] = (uint32_t)pos < sm.pn[q] ? ord_key(load_agent(&rs[e])) : 0u;
+            }
+        __syncthreads();
+        uint32_t mu[MREG];
+#pragma unroll
+        for (int i = 0; i < MREG; ++i) {
+            const int e = e0 + i;
+            mu[i] = (i < chunk && e < E) ? sm.stage[e + (e >> 5)] : 0u;
         }
-        pos += keep ? 1u : 0u;
+        uint32_t mtau = 0, mties = 0;
+        if (!all) {
+            block_select(
+                [&](auto f) {
+#pragma unroll
+                    for (int i = 0; i < MREG; ++i)
+                        if (mu[i] != 0u) f(mu[i]);
+                },
+                (uint32_t)topk, sm, mtau, mties);
+        }
+        uint32_t my_eq = 0;
+#pragma unroll
+        for (int i = 0; i < MREG; ++i) my_eq += (!all && mu[i] != 0u && mu[i] == mtau) ? 1u : 0u;
+        uint32_t run = block_excl_scan(my_eq, sm, total);
+        uint64_t keepmask = 0;
+        uint32_t my_keep = 0;
+#pragma unroll
+        for (int i = 0; i < MREG; ++i) {
+            const bool valid = mu[i] != 0u;
+            const bool eq = !all && valid && mu[i] == mtau;
+            const bool keep = valid && (all || mu[i] > mtau || (eq && run < mties));
+            run += eq ? 1u : 0u;
+            keepmask |= keep ? (1ull << i) : 0ull;
+            my_keep += keep ? 1u : 0u;
+        }
+        uint32_t pos = block_excl_scan(my_keep, sm, total);
+#pragma unroll
+        for (int i = 0; i < MREG; ++i) {
+            if ((keepmask >> i) & 1ull) {
+                if (pos < m) {
+                    io[pos] = load_agent(&ri[e0 + i]);
+                    if (vo) vo[pos] = key_float(mu[i]);
+                }
+                ++pos;
+            }
+        }
+    } else {
+        // Long candidate lists: the same selection, reading the workspace.
+        auto valid_at = [&](int e) {
+            const int q = e / topk;
+            return (uint32_t)(e - q * topk) < sm.pn[q];
+        };
+        uint32_t mtau = 0, mties = 0;
+        if (!all) {
+            block_select(
+                [&](auto f) {
+                    for (int e = tid; e < E; e += THREADS)
+                        if (valid_at(e)) f(ord_key(load_agent(&rs[e])));
+                },
+                (uint32_t)topk, sm, mtau, mties);
+        }
+        const int e1 = e0 + chunk < E ? e0 + chunk : E;
+        uint32_t my_eq = 0;
+        for (int e = e0; e < e1; ++e)
+            if (valid_at(e)) my_eq += (!all && ord_key(load_agent(&rs[e])) == mtau) ? 1u : 0u;
+        const uint32_t eq_base = block_excl_scan(my_eq, sm, total);
+        uint32_t my_keep = 0, run = eq_base;
+        for (int e = e0; e < e1; ++e) {
+            if (!valid_at(e)) continue;
+            const uint32_t uu = ord_key(load_agent(&rs[e]));
+            const bool eq = !all && uu == mtau;
+            my_keep += (all || uu > mtau || (eq && run < mties)) ? 1u : 0u;
+            run += eq ? 1u : 0u;
+        }
+        uint32_t pos = block_excl_scan(my_keep, sm, total);
+        run = eq_base;
+        for (int e = e0; e < e1; ++e) {
+            if (!valid_at(e)) continue;
+            const float sv = load_agent(&rs[e]);
+            const uint32_t uu = ord_key(sv);
+            const bool eq = !all && uu == mtau;
+            const bool keep = all || uu > mtau || (eq && run < mties);
+            run += eq ? 1u : 0u;
+            if (keep && pos < m) {
+                io[pos] = load_agent(&ri[e]);
+                if (vo) vo[pos] = sv;
+            }
+            pos += keep ? 1u : 0u;
+        }
     }
     for (int j = (int)m + tid; j < topk; j += THREADS) {
         io[j] = -1;
