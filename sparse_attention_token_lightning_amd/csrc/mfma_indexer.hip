@@ -48,7 +48,7 @@ constexpr int NWAVE = 8;    // wavefronts per workgroup, one query token each
 constexpr int TQ = NWAVE;
 constexpr int KT = 128;     // keys per LDS tile
 constexpr int KROW = D + 8; // bf16 per LDS key row: 272 B keeps 16-byte reads conflict-free
-constexpr int CAP = 1024;   // candidate slots per token
+constexpr int CAP = 1280;   // candidate slots per token
 constexpr int THREADS = NWAVE * 64;
 
 typedef __attribute__((__vector_size__(8 * sizeof(short)))) short bf16x8;
@@ -69,71 +69,183 @@ __device__ __forceinline__ int acc_row(int i, int lane) { return 8 * (i >> 2) + 
 // max(x, 0) in one instruction (scores stay far below the upper clamp).
 __device__ __forceinline__ float relu(float x) { return __builtin_amdgcn_fmed3f(x, 0.0f, 3.0e38f); }
 
-// Wavefront-wide: reduce the candidate buffer (cs, ci)[0..n) with n > k to its
-// top-k in place, keeping index order; returns the k-th score (the new
-// admission threshold).
-__device__ float wave_keep_topk(float *cs, int *ci, int n, int k, uint32_t *hist, int lane)
+constexpr int CREG = CAP / 64;  // buffer entries per lane when held in registers
+
+__device__ __forceinline__ uint32_t wave_and(uint32_t v)
 {
-    uint32_t prefix = 0, pmask = 0, remaining = (uint32_t)k;
-    for (int shift = 24; shift >= 0; shift -= 8) {
-        for (int b = lane; b < 256; b += 64) hist[b] = 0;
-        wave_lds_sync();
-        for (int i = lane; i < n; i += 64) {
-            const uint32_t u = ord_key(cs[i]);
-            if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
-        }
-        wave_lds_sync();
-        uint32_t c[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) c[q] = hist[4 * lane + q];
-        const uint32_t tot = c[0] + c[1] + c[2] + c[3];
-        uint32_t suf = tot;
+    for (int off = 32; off >= 1; off >>= 1) v &= __shfl_xor(v, off);
+    return v;
+}
+
+__device__ __forceinline__ uint32_t wave_or(uint32_t v)
+{
 #pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const uint32_t y = __shfl_down(suf, off);
-            if (lane + off < 64) suf += y;
-        }
-        uint32_t above = suf - tot;
-        int found = -1;
-        uint32_t rem = 0;
+    for (int off = 32; off >= 1; off >>= 1) v |= __shfl_xor(v, off);
+    return v;
+}
+
+// Lane `lane` holds buffer entries i = j*64 + lane (j < CREG) in registers;
+// entries past n read as key 0 (no key: below every finite score's key).
+__device__ __forceinline__ void load_buffer(const float *cs, const int *ci, int n, int lane,
+                                            uint32_t (&u)[CREG], int (&iv)[CREG])
+{
 #pragma unroll
-        for (int q = 3; q >= 0; --q) {
-            if (found < 0 && above < remaining && remaining <= above + c[q]) {
-                found = q;
-                rem = remaining - above;
-            }
-            above += c[q];
-        }
-        const int src = __builtin_ctzll(wave_ballot(found >= 0));
-        const uint32_t digit = (uint32_t)(4 * src + wave_readlane(found, src));
-        remaining = (uint32_t)wave_readlane((int)rem, src);
-        prefix |= digit << shift;
-        pmask |= 0xffu << shift;
-        wave_lds_sync();
+    for (int j = 0; j < CREG; ++j) {
+        const int i = j * 64 + lane;
+        u[j] = i < n ? ord_key(cs[i]) : 0u;
+        iv[j] = i < n ? ci[i] : 0;
     }
-    const uint32_t tau = prefix;
+}
+
+// Histogram of the digit (u >> lo) & dmask over keys matching (prefix, pmask),
+// then the bin holding the `want`-th largest key; returns the bin and sets
+// `above_cnt` to the number of matching keys in higher bins.
+__device__ __forceinline__ uint32_t wave_digit(const uint32_t (&u)[CREG], uint32_t prefix,
+                                               uint32_t pmask, int lo, uint32_t dmask,
+                                               uint32_t want, uint32_t *hist, int lane,
+                                               uint32_t &above_cnt)
+{
+    for (int b = lane; b < 256; b += 64) hist[b] = 0;
+    wave_lds_sync();
+#pragma unroll
+    for (int j = 0; j < CREG; ++j)
+        if (u[j] != 0u && (u[j] & pmask) == prefix) atomicAdd(&hist[(u[j] >> lo) & dmask], 1u);
+    wave_lds_sync();
+    uint32_t c[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) c[q] = hist[4 * lane + q];
+    const uint32_t tot = c[0] + c[1] + c[2] + c[3];
+    uint32_t suf = tot;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = __shfl_down(suf, off);
+        if (lane + off < 64) suf += y;
+    }
+    uint32_t abv = suf - tot, mine = 0;
+    int found = -1;
+#pragma unroll
+    for (int q = 3; q >= 0; --q) {
+        if (found < 0 && abv < want && want <= abv + c[q]) {
+            found = q;
+            mine = abv;
+        }
+        abv += c[q];
+    }
+    const int src = __builtin_ctzll(wave_ballot(found >= 0));
+    above_cnt = (uint32_t)wave_readlane((int)mine, src);
+    const uint32_t bin = (uint32_t)(4 * src + wave_readlane(found, src));
+    wave_lds_sync();
+    return bin;
+}
+
+// Stable in-place compaction of the register-held buffer: keep(key, rank
+// among equal-to-tie keys) decides; returns the new count.
+template <class Keep>
+__device__ __forceinline__ int wave_compact(float *cs, int *ci, const uint32_t (&u)[CREG],
+                                            const int (&iv)[CREG], uint32_t tie, int lane, Keep keep)
+{
     uint32_t out = 0, ties = 0;
-    for (int base = 0; base < n; base += 64) {
-        const int i = base + lane;
-        const bool in = i < n;
-        const float sv = in ? cs[i] : 0.0f;
-        const int iv = in ? ci[i] : 0;
-        const uint32_t u = ord_key(sv);
-        const bool eq = in && u == tau;
+    wave_lds_sync();
+#pragma unroll
+    for (int j = 0; j < CREG; ++j) {
+        const bool valid = u[j] != 0u;
+        const bool eq = valid && u[j] == tie;
         const uint64_t meq = wave_ballot(eq);
-        const bool keep = in && (u > tau || (eq && ties + lanes_below(meq) < remaining));
-        const uint64_t mk = wave_ballot(keep);
-        const uint32_t pos = out + lanes_below(mk);
-        wave_lds_sync();
-        if (keep) {
-            cs[pos] = sv;
-            ci[pos] = iv;
+        const bool k = valid && keep(u[j], eq, ties + lanes_below(meq));
+        const uint64_t mk = wave_ballot(k);
+        if (k) {
+            const uint32_t pos = out + lanes_below(mk);
+            cs[pos] = key_float(u[j]);
+            ci[pos] = iv[j];
         }
         out += (uint32_t)__builtin_popcountll(mk);
         ties += (uint32_t)__builtin_popcountll(meq);
     }
     wave_lds_sync();
+    return (int)out;
+}
+
+// Wavefront-wide: reduce the candidate buffer (cs, ci)[0..n) with n > k to
+// exactly its top-k, keeping index order; returns the k-th score. The k-th
+// largest order key is found digit by digit: each pass takes the AND and OR
+// of the keys still in play and starts its 8-bit window at their highest
+// differing bit, so shared high bits cost no pass.
+__device__ float wave_keep_topk(float *cs, int *ci, int n, int k, uint32_t *hist, int lane)
+{
+    uint32_t u[CREG];
+    int iv[CREG];
+    load_buffer(cs, ci, n, lane, u, iv);
+    uint32_t prefix = 0, pmask = 0, remaining = (uint32_t)k;
+    while (pmask != ~0u) {
+        uint32_t a = ~0u, o = 0u;
+#pragma unroll
+        for (int j = 0; j < CREG; ++j)
+            if (u[j] != 0u && (u[j] & pmask) == prefix) {
+                a &= u[j];
+                o |= u[j];
+            }
+        a = wave_and(a);
+        o = wave_or(o);
+        const uint32_t diff = (a ^ o) & ~pmask;
+        if (diff == 0u) {  // every key still in play is equal: that is the k-th
+            prefix = a;
+            break;
+        }
+        const int hb = 31 - __builtin_clz(diff);
+        const uint32_t above = hb == 31 ? 0u : (~0u << (hb + 1));
+        prefix = (prefix & pmask) | (a & above & ~pmask);
+        pmask |= above;
+        const int lo = hb >= 7 ? hb - 7 : 0;
+        const uint32_t dmask = (2u << (hb - lo)) - 1u;
+        uint32_t higher;
+        const uint32_t bin = wave_digit(u, prefix, pmask, lo, dmask, remaining, hist, lane, higher);
+        remaining -= higher;
+        prefix |= bin << lo;
+        pmask |= dmask << lo;
+    }
+    const uint32_t tau = prefix, ties = remaining;
+    wave_compact(cs, ci, u, iv, tau, lane,
+                 [&](uint32_t key, bool eq, uint32_t rank) { return key > tau || (eq && rank < ties); });
     return key_float(tau);
+}
+
+// Wavefront-wide, cheap: raise the admission threshold without finding the
+// exact k-th key. The AND/OR of all entries gives the bits they share; one
+// 8-bit histogram over the window just below them finds the highest bin edge
+// with at least k entries at or above it; a stable pass keeps exactly those.
+// Nothing that can still reach the top k is dropped (k entries already sit at
+// or above the edge). Returns the new count (n when no edge frees space);
+// `edge` receives the order key from which later scores are admitted.
+__device__ int wave_raise_threshold(float *cs, int *ci, int n, int k, uint32_t *hist, int lane,
+                                    uint32_t &edge)
+{
+    uint32_t u[CREG];
+    int iv[CREG];
+    load_buffer(cs, ci, n, lane, u, iv);
+    uint32_t a = ~0u, o = 0u;
+#pragma unroll
+    for (int j = 0; j < CREG; ++j)
+        if (u[j] != 0u) {
+            a &= u[j];
+            o |= u[j];
+        }
+    a = wave_and(a);
+    o = wave_or(o);
+    const uint32_t diff = a ^ o;
+    if (diff == 0u) return n;
+    const int hb = 31 - __builtin_clz(diff);
+    const uint32_t above = hb == 31 ? 0u : (~0u << (hb + 1));
+    const int lo = hb >= 7 ? hb - 7 : 0;
+    const uint32_t dmask = (2u << (hb - lo)) - 1u;
+    uint32_t higher;
+    const uint32_t bin = wave_digit(u, a & above, above, lo, dmask, (uint32_t)k, hist, lane, higher);
+    uint32_t e = (a & above) | (bin << lo);
+    if (e < 0x00800000u) e = 0x00800000u;  // never below -FLT_MAX: a NaN threshold admits nothing
+    const int kept = wave_compact(cs, ci, u, iv, 0xffffffffu, lane,
+                                  [&](uint32_t key, bool, uint32_t) { return key >= e; });
+    edge = e;
+    return kept;
 }
 
 template <bool KFP8>
@@ -230,7 +342,7 @@ __global__ __launch_bounds__(THREADS, 1) void mfma_indexer_kernel(
     float *cs = sm.cs[wid];
     int *ci = sm.ci[wid];
     int cnt = 0;
-    float thr = -INFINITY;
+    float thr = -INFINITY;  // a score enters the buffer iff score >= thr
 
     TileRegs<KFP8> tr;
     float tsc;
@@ -284,7 +396,7 @@ __global__ __launch_bounds__(THREADS, 1) void mfma_indexer_kernel(
                 if (SCORE) {
                     if (tok_ok && key < S) scores[((long long)b * T + tok) * S + key] = vis ? sc : -INFINITY;
                 } else {
-                    const bool pass = vis && sc > thr;
+                    const bool pass = vis && sc >= thr;
                     const uint64_t m = wave_ballot(pass);
                     if (m) {
                         const int pos = cnt + (int)lanes_below(m);
@@ -295,8 +407,16 @@ __global__ __launch_bounds__(THREADS, 1) void mfma_indexer_kernel(
                         cnt += __builtin_popcountll(m);
                         if (cnt > CAP - 64) {
                             wave_lds_sync();
-                            thr = wave_keep_topk(cs, ci, cnt, topk, sm.hist[wid], lane);
-                            cnt = topk;
+                            uint32_t edge = 0;
+                            const int kept = wave_raise_threshold(cs, ci, cnt, topk, sm.hist[wid], lane, edge);
+                            if (kept <= CAP - 256) {
+                                cnt = kept;
+                                thr = key_float(edge);
+                            } else {  // too little freed: exact k-th, admit strictly above it
+                                const float kth = wave_keep_topk(cs, ci, kept, topk, sm.hist[wid], lane);
+                                cnt = topk;
+                                thr = key_float(ord_key(kth) + 1u);
+                            }
                         }
                     }
                 }

@@ -50,6 +50,7 @@ struct SplitSmem {
         uint32_t sc[NW][WAVE_KEYS];            // partition score keys, 0 = no key
         uint32_t stage[MSTAGE + MSTAGE / 32];  // merge staging, one pad word per 32
     };
+    int stage_i[MSTAGE + MSTAGE / 32];        // merge staging: key indices
     uint32_t red[3][NW];
     uint32_t hist[NW][256];
     uint32_t tot[256];
@@ -63,12 +64,6 @@ template <class V>
 __device__ __forceinline__ void store_agent(V *p, V v)
 {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-template <class V>
-__device__ __forceinline__ V load_agent(const V *p)
-{
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __device__ __forceinline__ int acc_row(int i, int lane) { return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3); }
@@ -434,8 +429,11 @@ __global__ __launch_bounds__(THREADS, 1) void split_indexer_kernel(
                   (uint32_t)(P - 1);
     __syncthreads();
     if (!sm.last) return;
+    // Every other workgroup's candidate stores completed before its counter
+    // increment; drop this XCD's stale L2 lines (no writeback) and read.
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 
-    for (int q = tid; q < P; q += THREADS) sm.pn[q] = load_agent(&cand_n[r * P + q]);
+    for (int q = tid; q < P; q += THREADS) sm.pn[q] = cand_n[r * P + q];
     __syncthreads();
     uint32_t N = 0;
     for (int q = 0; q < P; ++q) N += sm.pn[q];
@@ -451,11 +449,25 @@ __global__ __launch_bounds__(THREADS, 1) void split_indexer_kernel(
     const int chunk = (E + THREADS - 1) / THREADS;
     const int e0 = tid * chunk;
     if (chunk <= MREG) {
-        for (int q = 0; q < P; ++q)
-            for (int pos = tid; pos < topk; pos += THREADS) {
-                const int e = q * topk + pos;
-                sm.stage[e + (e >> 5)] = (uint32_t)pos < sm.pn[q] ? ord_key(load_agent(&rs[e])) : 0u;
+        // Coalesced staging, all loads in flight before any is used.
+        float vs[MREG];
+        int vi[MREG];
+#pragma unroll
+        for (int j = 0; j < MREG; ++j) {
+            const int e = tid + THREADS * j;
+            vs[j] = e < E ? rs[e] : 0.0f;
+            vi[j] = e < E ? ri[e] : 0;
+        }
+#pragma unroll
+        for (int j = 0; j < MREG; ++j) {
+            const int e = tid + THREADS * j;
+            if (e < E) {
+                const int q = e / topk;
+                const bool ok = (uint32_t)(e - q * topk) < sm.pn[q];
+                sm.stage[e + (e >> 5)] = ok ? ord_key(vs[j]) : 0u;
+                sm.stage_i[e + (e >> 5)] = vi[j];
             }
+        }
         __syncthreads();
         uint32_t mu[MREG];
 #pragma unroll
@@ -493,7 +505,7 @@ __global__ __launch_bounds__(THREADS, 1) void split_indexer_kernel(
         for (int i = 0; i < MREG; ++i) {
             if ((keepmask >> i) & 1ull) {
                 if (pos < m) {
-                    io[pos] = load_agent(&ri[e0 + i]);
+                    io[pos] = sm.stage_i[(e0 + i) + ((e0 + i) >> 5)];
                     if (vo) vo[pos] = key_float(mu[i]);
                 }
                 ++pos;
@@ -510,19 +522,19 @@ __global__ __launch_bounds__(THREADS, 1) void split_indexer_kernel(
             block_select(
                 [&](auto f) {
                     for (int e = tid; e < E; e += THREADS)
-                        if (valid_at(e)) f(ord_key(load_agent(&rs[e])));
+                        if (valid_at(e)) f(ord_key(rs[e]));
                 },
                 (uint32_t)topk, sm, mtau, mties);
         }
         const int e1 = e0 + chunk < E ? e0 + chunk : E;
         uint32_t my_eq = 0;
         for (int e = e0; e < e1; ++e)
-            if (valid_at(e)) my_eq += (!all && ord_key(load_agent(&rs[e])) == mtau) ? 1u : 0u;
+            if (valid_at(e)) my_eq += (!all && ord_key(rs[e]) == mtau) ? 1u : 0u;
         const uint32_t eq_base = block_excl_scan(my_eq, sm, total);
         uint32_t my_keep = 0, run = eq_base;
         for (int e = e0; e < e1; ++e) {
             if (!valid_at(e)) continue;
-            const uint32_t uu = ord_key(load_agent(&rs[e]));
+            const uint32_t uu = ord_key(rs[e]);
             const bool eq = !all && uu == mtau;
             my_keep += (all || uu > mtau || (eq && run < mties)) ? 1u : 0u;
             run += eq ? 1u : 0u;
@@ -531,13 +543,13 @@ __global__ __launch_bounds__(THREADS, 1) void split_indexer_kernel(
         run = eq_base;
         for (int e = e0; e < e1; ++e) {
             if (!valid_at(e)) continue;
-            const float sv = load_agent(&rs[e]);
+            const float sv = rs[e];
             const uint32_t uu = ord_key(sv);
             const bool eq = !all && uu == mtau;
             const bool keep = all || uu > mtau || (eq && run < mties);
             run += eq ? 1u : 0u;
             if (keep && pos < m) {
-                io[pos] = load_agent(&ri[e]);
+                io[pos] = ri[e];
                 if (vo) vo[pos] = sv;
             }
             pos += keep ? 1u : 0u;
