@@ -38,7 +38,40 @@ def _parse():
                     help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the timed steps, copy 256 MiB once (the reference kernel that "
+                         "scales the FETCH_SIZE / WRITE_SIZE counters to bytes)")
     return ap.parse_args()
+
+
+PROFILES = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles")
+KERNEL_SRC = os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                          "sparse_attention_token_lightning_amd", "csrc", "mfma_indexer.hip")
+
+
+def kernel_digest() -> str:
+    import hashlib
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per select launch from the committed counter summary, or None
+    when the kernel source changed since the counters were taken."""
+    path = os.path.join(PROFILES, "mfma_select_64k_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256_16") != kernel_digest():
+        return None
+    try:
+        return int(float(kv["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
 
 
 def _flops_64k(wl):
@@ -109,10 +142,18 @@ def main():
     achieved_tflops = flops / n_launch / avg_launch_s / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved_tflops, 1), "peak": BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved_tflops / BF16_PEAK_TFLOPS, 4),
-                "traffic": None,
+                "traffic": measured_traffic(),
                 "kernel": "mfma_indexer_kernel<fp8 keys, select>",
                 "avg_launch_us": round(avg_launch_s * 1e6, 2),
                 "flop_per_launch": flops // n_launch}
+
+    if args.copy_calibration:
+        src = torch.ones(256 << 18, dtype=torch.float32, device=dev)  # 256 MiB
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     extra = {"kernel_ms_per_step": round(sum(launch_ms) / args.steps, 3),
              "bf16_tflops_step_wall": round(flops / (ms_per_step * 1e-3) / 1e12, 1)}
