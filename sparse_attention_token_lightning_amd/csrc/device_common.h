@@ -35,6 +35,35 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t m)
 
 __device__ __forceinline__ int wave_readlane(int v, int lane) { return __builtin_amdgcn_readlane(v, lane); }
 
+// Inclusive scan across the 64 lanes with DPP moves (row shifts by 1, 2, 4, 8
+// within each 16-lane row, then row broadcasts of lanes 15 and 31): a few
+// VALU operations instead of a chain of LDS-crossbar permutes. `id` is the
+// identity of `op`; lane 63 ends with the reduction of the whole wavefront.
+template <class Op>
+__device__ __forceinline__ uint32_t wave_scan_incl(uint32_t v, uint32_t id, Op op)
+{
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)v, 0x111, 0xf, 0xf, false));
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)v, 0x112, 0xf, 0xf, false));
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)v, 0x114, 0xf, 0xf, false));
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)v, 0x118, 0xf, 0xf, false));
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)v, 0x142, 0xa, 0xf, false));
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)v, 0x143, 0xc, 0xf, false));
+    return v;
+}
+
+struct OpAdd { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a + b; } };
+struct OpAnd { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a & b; } };
+struct OpOr { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a | b; } };
+struct OpMin { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a < b ? a : b; } };
+struct OpMax { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a > b ? a : b; } };
+
+__device__ __forceinline__ uint32_t wave_total(uint32_t incl) { return (uint32_t)__builtin_amdgcn_readlane((int)incl, 63); }
+__device__ __forceinline__ uint32_t wave_sum(uint32_t v) { return wave_total(wave_scan_incl(v, 0u, OpAdd{})); }
+__device__ __forceinline__ uint32_t wave_and(uint32_t v) { return wave_total(wave_scan_incl(v, ~0u, OpAnd{})); }
+__device__ __forceinline__ uint32_t wave_or(uint32_t v) { return wave_total(wave_scan_incl(v, 0u, OpOr{})); }
+__device__ __forceinline__ uint32_t wave_min(uint32_t v) { return wave_total(wave_scan_incl(v, ~0u, OpMin{})); }
+__device__ __forceinline__ uint32_t wave_max(uint32_t v) { return wave_total(wave_scan_incl(v, 0u, OpMax{})); }
+
 // Orders this wavefront's LDS accesses before and after the call.
 __device__ __forceinline__ void wave_lds_sync()
 {

@@ -37,6 +37,7 @@ constexpr int kSplitMaxParts = 256;
 struct SplitWorkspace {
     uint32_t *ctr;     // [rows] arrival counters, zero between calls
     uint32_t *cand_n;  // [rows, P] candidates per partition
+    uint32_t *cand_t;  // [rows, P] partition's m-th largest order key (0: none), m = ceil(k/P)
     float *cand_s;     // [rows, P, k]
     int *cand_i;       // [rows, P, k]
 };

@@ -38,6 +38,7 @@
 //    buffer, already in index order, is the output. No sort anywhere.
 #include "device_common.h"
 #include "kernels.h"
+#include "wave_select.h"
 
 namespace ds4idx {
 namespace {
@@ -71,20 +72,6 @@ __device__ __forceinline__ float relu(float x) { return __builtin_amdgcn_fmed3f(
 
 constexpr int CREG = CAP / 64;  // buffer entries per lane when held in registers
 
-__device__ __forceinline__ uint32_t wave_and(uint32_t v)
-{
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v &= __shfl_xor(v, off);
-    return v;
-}
-
-__device__ __forceinline__ uint32_t wave_or(uint32_t v)
-{
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v |= __shfl_xor(v, off);
-    return v;
-}
-
 // Lane `lane` holds buffer entries i = j*64 + lane (j < CREG) in registers;
 // entries past n read as key 0 (no key: below every finite score's key).
 __device__ __forceinline__ void load_buffer(const float *cs, const int *ci, int n, int lane,
@@ -96,47 +83,6 @@ __device__ __forceinline__ void load_buffer(const float *cs, const int *ci, int 
         u[j] = i < n ? ord_key(cs[i]) : 0u;
         iv[j] = i < n ? ci[i] : 0;
     }
-}
-
-// Histogram of the digit (u >> lo) & dmask over keys matching (prefix, pmask),
-// then the bin holding the `want`-th largest key; returns the bin and sets
-// `above_cnt` to the number of matching keys in higher bins.
-__device__ __forceinline__ uint32_t wave_digit(const uint32_t (&u)[CREG], uint32_t prefix,
-                                               uint32_t pmask, int lo, uint32_t dmask,
-                                               uint32_t want, uint32_t *hist, int lane,
-                                               uint32_t &above_cnt)
-{
-    for (int b = lane; b < 256; b += 64) hist[b] = 0;
-    wave_lds_sync();
-#pragma unroll
-    for (int j = 0; j < CREG; ++j)
-        if (u[j] != 0u && (u[j] & pmask) == prefix) atomicAdd(&hist[(u[j] >> lo) & dmask], 1u);
-    wave_lds_sync();
-    uint32_t c[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) c[q] = hist[4 * lane + q];
-    const uint32_t tot = c[0] + c[1] + c[2] + c[3];
-    uint32_t suf = tot;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t y = __shfl_down(suf, off);
-        if (lane + off < 64) suf += y;
-    }
-    uint32_t abv = suf - tot, mine = 0;
-    int found = -1;
-#pragma unroll
-    for (int q = 3; q >= 0; --q) {
-        if (found < 0 && abv < want && want <= abv + c[q]) {
-            found = q;
-            mine = abv;
-        }
-        abv += c[q];
-    }
-    const int src = __builtin_ctzll(wave_ballot(found >= 0));
-    above_cnt = (uint32_t)wave_readlane((int)mine, src);
-    const uint32_t bin = (uint32_t)(4 * src + wave_readlane(found, src));
-    wave_lds_sync();
-    return bin;
 }
 
 // Stable in-place compaction of the register-held buffer: keep(key, rank
@@ -176,35 +122,8 @@ __device__ float wave_keep_topk(float *cs, int *ci, int n, int k, uint32_t *hist
     uint32_t u[CREG];
     int iv[CREG];
     load_buffer(cs, ci, n, lane, u, iv);
-    uint32_t prefix = 0, pmask = 0, remaining = (uint32_t)k;
-    while (pmask != ~0u) {
-        uint32_t a = ~0u, o = 0u;
-#pragma unroll
-        for (int j = 0; j < CREG; ++j)
-            if (u[j] != 0u && (u[j] & pmask) == prefix) {
-                a &= u[j];
-                o |= u[j];
-            }
-        a = wave_and(a);
-        o = wave_or(o);
-        const uint32_t diff = (a ^ o) & ~pmask;
-        if (diff == 0u) {  // every key still in play is equal: that is the k-th
-            prefix = a;
-            break;
-        }
-        const int hb = 31 - __builtin_clz(diff);
-        const uint32_t above = hb == 31 ? 0u : (~0u << (hb + 1));
-        prefix = (prefix & pmask) | (a & above & ~pmask);
-        pmask |= above;
-        const int lo = hb >= 7 ? hb - 7 : 0;
-        const uint32_t dmask = (2u << (hb - lo)) - 1u;
-        uint32_t higher;
-        const uint32_t bin = wave_digit(u, prefix, pmask, lo, dmask, remaining, hist, lane, higher);
-        remaining -= higher;
-        prefix |= bin << lo;
-        pmask |= dmask << lo;
-    }
-    const uint32_t tau = prefix, ties = remaining;
+    uint32_t ties;
+    const uint32_t tau = wave_kth_key<CREG>(u, (uint32_t)k, hist, lane, ties);
     wave_compact(cs, ci, u, iv, tau, lane,
                  [&](uint32_t key, bool eq, uint32_t rank) { return key > tau || (eq && rank < ties); });
     return key_float(tau);
@@ -239,7 +158,7 @@ __device__ int wave_raise_threshold(float *cs, int *ci, int n, int k, uint32_t *
     const int lo = hb >= 7 ? hb - 7 : 0;
     const uint32_t dmask = (2u << (hb - lo)) - 1u;
     uint32_t higher;
-    const uint32_t bin = wave_digit(u, a & above, above, lo, dmask, (uint32_t)k, hist, lane, higher);
+    const uint32_t bin = wave_digit<CREG>(u, a & above, above, lo, dmask, (uint32_t)k, hist, lane, higher);
     uint32_t e = (a & above) | (bin << lo);
     if (e < 0x00800000u) e = 0x00800000u;  // never below -FLT_MAX: a NaN threshold admits nothing
     const int kept = wave_compact(cs, ci, u, iv, 0xffffffffu, lane,

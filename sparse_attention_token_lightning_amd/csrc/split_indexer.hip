@@ -28,6 +28,7 @@
 //    counter is reset for the next call.
 #include "device_common.h"
 #include "kernels.h"
+#include "wave_select.h"
 
 namespace ds4idx {
 namespace {
@@ -41,6 +42,8 @@ constexpr int WAVE_KEYS = ROUNDS * 64;
 constexpr int PART = NW * WAVE_KEYS;  // 8192
 constexpr int MREG = 32;              // merge keys held per thread
 constexpr int MSTAGE = THREADS * MREG;  // candidates the merge stages in LDS
+constexpr int MEXT = 32;              // largest per-partition order statistic kept for the row bound
+constexpr int MSURV = 2048;           // survivors of the bound that one wavefront selects from
 
 typedef __attribute__((__vector_size__(8 * sizeof(short)))) short bf16x8;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
@@ -48,9 +51,13 @@ typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 struct SplitSmem {
     union {
         uint32_t sc[NW][WAVE_KEYS];            // partition score keys, 0 = no key
+        uint32_t fin[NW][MEXT];                // per-wavefront top-m keys (after sc is read)
         uint32_t stage[MSTAGE + MSTAGE / 32];  // merge staging, one pad word per 32
     };
     int stage_i[MSTAGE + MSTAGE / 32];        // merge staging: key indices
+    uint32_t fs[MSURV];                       // merge survivors: keys
+    int fe[MSURV];                            // merge survivors: key indices
+    uint32_t pt[kSplitMaxParts];              // partitions' m-th largest keys
     uint32_t red[3][NW];
     uint32_t hist[NW][256];
     uint32_t tot[256];
@@ -66,6 +73,12 @@ __device__ __forceinline__ void store_agent(V *p, V v)
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+template <class V>
+__device__ __forceinline__ V load_agent(const V *p)
+{
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __device__ __forceinline__ int acc_row(int i, int lane) { return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3); }
 
 template <bool HI>
@@ -78,12 +91,7 @@ __device__ __forceinline__ uint32_t cvt2(uint32_t w)
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, SplitSmem &sm, uint32_t &total)
 {
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-    uint32_t x = v;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t y = __shfl_up(x, off);
-        if (lane >= off) x += y;
-    }
+    const uint32_t x = wave_scan_incl(v, 0u, OpAdd{});
     if (lane == 63) sm.wsum[wid] = x;
     __syncthreads();
     uint32_t before = 0, tot = 0;
@@ -102,12 +110,9 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, SplitSmem &sm, u
 __device__ __forceinline__ void block_reduce3(uint32_t &s, uint32_t &a, uint32_t &o, SplitSmem &sm)
 {
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        s += __shfl_xor(s, off);
-        a &= __shfl_xor(a, off);
-        o |= __shfl_xor(o, off);
-    }
+    s = wave_sum(s);
+    a = wave_and(a);
+    o = wave_or(o);
     if (lane == 0) {
         sm.red[0][wid] = s;
         sm.red[1][wid] = a;
@@ -145,13 +150,8 @@ __device__ __forceinline__ void pick_digit(SplitSmem &sm, uint32_t remaining)
 #pragma unroll
         for (int q = 0; q < 4; ++q) c[q] = sm.tot[4 * lane + q];
         const uint32_t tot = c[0] + c[1] + c[2] + c[3];
-        uint32_t suf = tot;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const uint32_t y = __shfl_down(suf, off);
-            if (lane + off < 64) suf += y;
-        }
-        uint32_t above = suf - tot;
+        const uint32_t incl = wave_scan_incl(tot, 0u, OpAdd{});
+        uint32_t above = wave_total(incl) - incl;
         int found = -1;
         uint32_t rem = 0;
 #pragma unroll
@@ -292,8 +292,9 @@ template <bool KFP8>
 __global__ __launch_bounds__(THREADS, 1) void split_indexer_kernel(
     const uint16_t *__restrict__ Q, const uint8_t *__restrict__ K, const float *__restrict__ Ks,
     const float *__restrict__ W, int T, int S, long long offset, int topk, int P,
-    uint32_t *__restrict__ ctr, uint32_t *__restrict__ cand_n, float *__restrict__ cand_s,
-    int *__restrict__ cand_i, int *__restrict__ idx, float *__restrict__ vals)
+    uint32_t *__restrict__ ctr, uint32_t *__restrict__ cand_n, uint32_t *__restrict__ cand_t,
+    float *__restrict__ cand_s, int *__restrict__ cand_i, int *__restrict__ idx,
+    float *__restrict__ vals)
 {
     __shared__ SplitSmem sm;
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -388,7 +389,7 @@ __global__ __launch_bounds__(THREADS, 1) void split_indexer_kernel(
         neq += (uint32_t)__builtin_popcountll(wave_ballot(!select_all && u[j] != 0u && u[j] == tau));
     uint32_t total;
     uint32_t eq_before = block_excl_scan(lane == 0 ? neq : 0u, sm, total);
-    eq_before = (uint32_t)__shfl(eq_before, 0);
+    eq_before = (uint32_t)__builtin_amdgcn_readlane((int)eq_before, 0);
     uint32_t keepbits = 0, nkeep = 0;
 #pragma unroll
     for (int j = 0; j < ROUNDS; ++j) {
@@ -402,7 +403,7 @@ __global__ __launch_bounds__(THREADS, 1) void split_indexer_kernel(
         nkeep += (uint32_t)__builtin_popcountll(mk);
     }
     uint32_t out = block_excl_scan(lane == 0 ? nkeep : 0u, sm, total);
-    out = (uint32_t)__shfl(out, 0);
+    out = (uint32_t)__builtin_amdgcn_readlane((int)out, 0);
     const long long cbase = (r * P + p) * (long long)topk;
 #pragma unroll
     for (int j = 0; j < ROUNDS; ++j) {
@@ -416,6 +417,33 @@ __global__ __launch_bounds__(THREADS, 1) void split_indexer_kernel(
         out += (uint32_t)__builtin_popcountll(mk);
     }
     if (tid == 0) store_agent(&cand_n[r * P + p], want);
+    // Unused slots hold the key-0 pattern (all bits set), which reads as "no key".
+    for (int i = (int)want + tid; i < topk; i += THREADS) store_agent(&cand_s[cbase + i], __uint_as_float(~0u));
+
+    // ---- this partition's m-th largest key, m = ceil(k / P). With every
+    // partition holding m keys at or above its own m-th, the row holds at
+    // least P*m >= k keys at or above the smallest of them: a lower bound on
+    // the row's k-th key that lets the merge skip most candidates.
+    const int mth = (topk + P - 1) / P;
+    if (mth <= MEXT) {
+        uint32_t top[MEXT];
+        wave_mth_key<ROUNDS>(u, mth, lane, top);  // this wavefront's m largest keys
+        if (lane == 0)
+            for (int i = 0; i < mth; ++i) sm.fin[wid][i] = top[i];
+        __syncthreads();
+        if (wid == 0) {
+            uint32_t fu[(NW * MEXT) / 64];
+#pragma unroll
+            for (int j = 0; j < (NW * MEXT) / 64; ++j) {
+                const int i = j * 64 + lane;
+                fu[j] = (i % MEXT) < mth ? sm.fin[i / MEXT][i % MEXT] : 0u;
+            }
+            const uint32_t tp = wave_mth_key<(NW * MEXT) / 64>(fu, mth, lane, nullptr);
+            if (lane == 0) store_agent(&cand_t[r * P + p], tp);  // 0: fewer than m keys, no bound
+        }
+    } else if (tid == 0) {
+        store_agent(&cand_t[r * P + p], 0u);
+    }
 
     // ---- arrival: the last workgroup of the row merges. The candidate lists
     // travel through device-coherent (agent-scope) stores and loads, which
@@ -429,90 +457,159 @@ __global__ __launch_bounds__(THREADS, 1) void split_indexer_kernel(
                   (uint32_t)(P - 1);
     __syncthreads();
     if (!sm.last) return;
-    // Every other workgroup's candidate stores completed before its counter
-    // increment; drop this XCD's stale L2 lines (no writeback) and read.
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 
-    for (int q = tid; q < P; q += THREADS) sm.pn[q] = cand_n[r * P + q];
-    __syncthreads();
-    uint32_t N = 0;
-    for (int q = 0; q < P; ++q) N += sm.pn[q];
     const int E = P * topk;  // <= kSplitMaxParts * DS4IDX_MAX_TOPK
     const float *rs = cand_s + r * E;
     const int *ri = cand_i + r * E;
-    const uint32_t m = N < (uint32_t)topk ? N : (uint32_t)topk;
-    const bool all = N <= (uint32_t)topk;
     int *io = idx + r * topk;
     float *vo = vals ? vals + r * topk : nullptr;
     // Element e = (partition, position) in index order; thread t owns the
     // contiguous run [t*chunk, (t+1)*chunk), which keeps the output order.
     const int chunk = (E + THREADS - 1) / THREADS;
     const int e0 = tid * chunk;
+    uint32_t m_out = 0;  // selected count (the rest of the row is padding)
     if (chunk <= MREG) {
-        // Coalesced staging, all loads in flight before any is used.
+        // One batch of device-coherent loads, all in flight before any is used:
+        // every other workgroup's stores completed before its counter increment.
+        // Unused slots carry the no-key pattern, so no per-partition counts.
         float vs[MREG];
         int vi[MREG];
 #pragma unroll
         for (int j = 0; j < MREG; ++j) {
             const int e = tid + THREADS * j;
-            vs[j] = e < E ? rs[e] : 0.0f;
-            vi[j] = e < E ? ri[e] : 0;
+            vs[j] = e < E ? load_agent(&rs[e]) : __uint_as_float(~0u);
+            vi[j] = e < E ? load_agent(&ri[e]) : 0;
         }
+        const uint32_t ptv = tid < P ? load_agent(&cand_t[r * P + tid]) : ~0u;
+        const uint32_t wb = wave_min(ptv);
+        if (lane == 0) sm.red[0][wid] = wb;
 #pragma unroll
         for (int j = 0; j < MREG; ++j) {
             const int e = tid + THREADS * j;
             if (e < E) {
-                const int q = e / topk;
-                const bool ok = (uint32_t)(e - q * topk) < sm.pn[q];
-                sm.stage[e + (e >> 5)] = ok ? ord_key(vs[j]) : 0u;
+                sm.stage[e + (e >> 5)] = ord_key(vs[j]);
                 sm.stage_i[e + (e >> 5)] = vi[j];
             }
         }
         __syncthreads();
+        uint32_t bound = ~0u;  // keys below it cannot be among the row's top k (0: no bound)
+#pragma unroll
+        for (int w = 0; w < NW; ++w) bound = sm.red[0][w] < bound ? sm.red[0][w] : bound;
         uint32_t mu[MREG];
 #pragma unroll
         for (int i = 0; i < MREG; ++i) {
             const int e = e0 + i;
             mu[i] = (i < chunk && e < E) ? sm.stage[e + (e >> 5)] : 0u;
         }
-        uint32_t mtau = 0, mties = 0;
-        if (!all) {
-            block_select(
-                [&](auto f) {
+        // Survivors of the bound, kept in (partition, position) = index order.
+        uint32_t nsurv = 0;
 #pragma unroll
-                    for (int i = 0; i < MREG; ++i)
-                        if (mu[i] != 0u) f(mu[i]);
-                },
-                (uint32_t)topk, sm, mtau, mties);
-        }
-        uint32_t my_eq = 0;
+        for (int i = 0; i < MREG; ++i) nsurv += (mu[i] != 0u && mu[i] >= bound) ? 1u : 0u;
+        uint32_t F;
+        const uint32_t sbase = block_excl_scan(nsurv, sm, F);
+        // With a bound, F >= k whenever the row has k keys; without one, F = all keys.
+        const uint32_t m = F < (uint32_t)topk ? F : (uint32_t)topk;
+        const bool all = F <= (uint32_t)topk;
+        m_out = m;
+        if (F <= (uint32_t)topk) {
+            // Everything that survives is selected (F = min(N, k) here).
+            uint32_t pos = sbase;
 #pragma unroll
-        for (int i = 0; i < MREG; ++i) my_eq += (!all && mu[i] != 0u && mu[i] == mtau) ? 1u : 0u;
-        uint32_t run = block_excl_scan(my_eq, sm, total);
-        uint64_t keepmask = 0;
-        uint32_t my_keep = 0;
-#pragma unroll
-        for (int i = 0; i < MREG; ++i) {
-            const bool valid = mu[i] != 0u;
-            const bool eq = !all && valid && mu[i] == mtau;
-            const bool keep = valid && (all || mu[i] > mtau || (eq && run < mties));
-            run += eq ? 1u : 0u;
-            keepmask |= keep ? (1ull << i) : 0ull;
-            my_keep += keep ? 1u : 0u;
-        }
-        uint32_t pos = block_excl_scan(my_keep, sm, total);
-#pragma unroll
-        for (int i = 0; i < MREG; ++i) {
-            if ((keepmask >> i) & 1ull) {
-                if (pos < m) {
-                    io[pos] = sm.stage_i[(e0 + i) + ((e0 + i) >> 5)];
-                    if (vo) vo[pos] = key_float(mu[i]);
+            for (int i = 0; i < MREG; ++i) {
+                if (mu[i] != 0u && mu[i] >= bound) {
+                    if (pos < m) {
+                        io[pos] = sm.stage_i[(e0 + i) + ((e0 + i) >> 5)];
+                        if (vo) vo[pos] = key_float(mu[i]);
+                    }
+                    ++pos;
                 }
-                ++pos;
+            }
+        } else if (F <= (uint32_t)MSURV) {
+            uint32_t pos = sbase;
+#pragma unroll
+            for (int i = 0; i < MREG; ++i) {
+                if (mu[i] != 0u && mu[i] >= bound) {
+                    sm.fs[pos] = mu[i];
+                    sm.fe[pos] = sm.stage_i[(e0 + i) + ((e0 + i) >> 5)];
+                    ++pos;
+                }
+            }
+            __syncthreads();
+            if (wid == 0) {  // one wavefront, no block barriers: exact top-k of the survivors
+                uint32_t fu[MSURV / 64];
+#pragma unroll
+                for (int j = 0; j < MSURV / 64; ++j) {
+                    const int i = j * 64 + lane;
+                    fu[j] = i < (int)F ? sm.fs[i] : 0u;
+                }
+                uint32_t ties;
+                const uint32_t tau = wave_kth_key<MSURV / 64>(fu, (uint32_t)topk, sm.hist[0], lane, ties);
+                uint32_t out = 0, tr = 0;
+#pragma unroll
+                for (int j = 0; j < MSURV / 64; ++j) {
+                    const int i = j * 64 + lane;
+                    const bool eq = fu[j] != 0u && fu[j] == tau;
+                    const uint64_t meq = wave_ballot(eq);
+                    const bool keep = fu[j] != 0u && (fu[j] > tau || (eq && tr + lanes_below(meq) < ties));
+                    const uint64_t mk = wave_ballot(keep);
+                    const uint32_t o = out + lanes_below(mk);
+                    if (keep && o < m) {
+                        io[o] = sm.fe[i];
+                        if (vo) vo[o] = key_float(fu[j]);
+                    }
+                    out += (uint32_t)__builtin_popcountll(mk);
+                    tr += (uint32_t)__builtin_popcountll(meq);
+                }
+            }
+        } else {
+            // Too many survivors (adversarial rows): block-wide selection of all.
+            uint32_t mtau = 0, mties = 0;
+            if (!all) {
+                block_select(
+                    [&](auto f) {
+#pragma unroll
+                        for (int i = 0; i < MREG; ++i)
+                            if (mu[i] != 0u) f(mu[i]);
+                    },
+                    (uint32_t)topk, sm, mtau, mties);
+            }
+            uint32_t my_eq = 0;
+#pragma unroll
+            for (int i = 0; i < MREG; ++i) my_eq += (!all && mu[i] != 0u && mu[i] == mtau) ? 1u : 0u;
+            uint32_t run = block_excl_scan(my_eq, sm, total);
+            uint64_t keepmask = 0;
+            uint32_t my_keep = 0;
+#pragma unroll
+            for (int i = 0; i < MREG; ++i) {
+                const bool valid = mu[i] != 0u;
+                const bool eq = !all && valid && mu[i] == mtau;
+                const bool keep = valid && (all || mu[i] > mtau || (eq && run < mties));
+                run += eq ? 1u : 0u;
+                keepmask |= keep ? (1ull << i) : 0ull;
+                my_keep += keep ? 1u : 0u;
+            }
+            uint32_t pos = block_excl_scan(my_keep, sm, total);
+#pragma unroll
+            for (int i = 0; i < MREG; ++i) {
+                if ((keepmask >> i) & 1ull) {
+                    if (pos < m) {
+                        io[pos] = sm.stage_i[(e0 + i) + ((e0 + i) >> 5)];
+                        if (vo) vo[pos] = key_float(mu[i]);
+                    }
+                    ++pos;
+                }
             }
         }
     } else {
         // Long candidate lists: the same selection, reading the workspace.
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // drop stale L2 lines, then plain loads
+        for (int q = tid; q < P; q += THREADS) sm.pn[q] = cand_n[r * P + q];
+        __syncthreads();
+        uint32_t N = 0;
+        for (int q = 0; q < P; ++q) N += sm.pn[q];
+        const uint32_t m = N < (uint32_t)topk ? N : (uint32_t)topk;
+        const bool all = N <= (uint32_t)topk;
+        m_out = m;
         auto valid_at = [&](int e) {
             const int q = e / topk;
             return (uint32_t)(e - q * topk) < sm.pn[q];
@@ -555,7 +652,7 @@ __global__ __launch_bounds__(THREADS, 1) void split_indexer_kernel(
             pos += keep ? 1u : 0u;
         }
     }
-    for (int j = (int)m + tid; j < topk; j += THREADS) {
+    for (int j = (int)m_out + tid; j < topk; j += THREADS) {
         io[j] = -1;
         if (vo) vo[j] = -INFINITY;
     }
@@ -571,7 +668,7 @@ hipError_t launch_t(const Problem &p, const void *Q, const void *K, const float 
     SplitWorkspace w = split_workspace(ws, p, k);
     hipLaunchKernelGGL((split_indexer_kernel<KFP8>), dim3(P, rows), dim3(THREADS), 0, st,
                        static_cast<const uint16_t *>(Q), static_cast<const uint8_t *>(K), Ks, W,
-                       p.T, p.S, p.offset, k, P, w.ctr, w.cand_n, w.cand_s, w.cand_i, idx, vals);
+                       p.T, p.S, p.offset, k, P, w.ctr, w.cand_n, w.cand_t, w.cand_s, w.cand_i, idx, vals);
     return hipGetLastError();
 }
 
@@ -588,7 +685,7 @@ static size_t align256(size_t n) { return (n + 255) / 256 * 256; }
 size_t split_workspace_bytes(const Problem &p, int k)
 {
     const size_t rows = (size_t)p.B * p.T, P = (size_t)split_parts(p);
-    return align256(rows * 4) + align256(rows * P * 4) + 2 * align256(rows * P * (size_t)k * 4);
+    return align256(rows * 4) + 2 * align256(rows * P * 4) + 2 * align256(rows * P * (size_t)k * 4);
 }
 
 SplitWorkspace split_workspace(void *ws, const Problem &p, int k)
@@ -599,6 +696,8 @@ SplitWorkspace split_workspace(void *ws, const Problem &p, int k)
     w.ctr = reinterpret_cast<uint32_t *>(c);
     c += align256(rows * 4);
     w.cand_n = reinterpret_cast<uint32_t *>(c);
+    c += align256(rows * P * 4);
+    w.cand_t = reinterpret_cast<uint32_t *>(c);
     c += align256(rows * P * 4);
     w.cand_s = reinterpret_cast<float *>(c);
     c += align256(rows * P * (size_t)k * 4);
