@@ -32,15 +32,17 @@ hipError_t launch_mfma_select(const Problem &p, const void *Q, const void *K, co
                               const float *W, int k, int *idx, float *vals, hipStream_t st);
 
 // Split-key kernel for few rows over long caches (decode): partitions of 8192
-// keys, per-partition exact top-k, last-arriving workgroup merges each row.
+// keys, each emitting a superset of its top k plus its m-th largest key; the
+// last-arriving workgroup of a row merges.
 constexpr int kSplitMaxParts = 256;
 struct SplitWorkspace {
-    uint32_t *ctr;     // [rows] arrival counters, zero between calls
-    uint32_t *cand_n;  // [rows, P] candidates per partition
-    uint32_t *cand_t;  // [rows, P] partition's m-th largest order key (0: none), m = ceil(k/P)
-    float *cand_s;     // [rows, P, k]
-    int *cand_i;       // [rows, P, k]
+    uint32_t *ctr;         // [rows] arrival counters, zero between calls
+    uint64_t *meta;        // [rows, P, 2] short-list edge << 32 | m-th largest key (~0: none); largest key
+    uint64_t *full_list;   // [rows, P, slots] (index << 32 | order key), key 0 = empty slot
+    uint64_t *short_list;  // [rows, P, short slots], same format
 };
+int split_slots(int k);
+int split_short_slots(const Problem &p, int k);
 int split_parts(const Problem &p);
 size_t split_workspace_bytes(const Problem &p, int k);
 SplitWorkspace split_workspace(void *ws, const Problem &p, int k);

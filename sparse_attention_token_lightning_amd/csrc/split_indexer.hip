@@ -13,22 +13,25 @@
 //    key (four 16-byte loads; the two halves of a wave cover each 128-byte fp8
 //    row). Queries use the same assignment. E4M3 widens to bf16 in registers.
 //    The next round's keys are in flight while the current one is scored.
-//  * The partition's exact top-k is found by block-wide radix selection over
-//    an order-preserving 32-bit key held in registers (16 per lane). Each
-//    digit pass first reduces the AND and OR of the keys still in play and
-//    starts its 8-bit window at their highest differing bit, so bits that
-//    every live key shares cost nothing and the histogram spreads over
-//    bins instead of piling onto one (the candidates of a row are all top
-//    scores and share their high bits). The selected keys go, in index
-//    order, to the workspace.
+//  * While the keys stream, every score's order key adds one count to a
+//    4096-bin LDS histogram of its top 12 bits (sign, exponent, 3 mantissa
+//    bits: eight bins per octave). These adds hide under the HBM wait. One
+//    block scan of the histogram then gives the bin of the partition's k-th
+//    largest key and of its m-th largest (m = ceil(k / full partitions)).
+//  * The partition emits, in index order, every key at or above the lower
+//    edge of the k-th key's bin: a superset of its top k, usually ~15% more,
+//    with no exact selection. The m-th key is refined exactly from the few
+//    keys of its bin. Every partition that holds m keys publishes that key;
+//    the smallest of them is a lower bound on the row's k-th key, because
+//    the full partitions alone hold at least k keys at or above it.
 //  * The last workgroup of a row to finish (device-scope arrival counter)
-//    merges the row's P candidate lists: they are staged through LDS with
-//    coalesced loads, each thread keeps a contiguous run in registers, the
-//    same selection runs, and one block-wide scan orders the output. The
-//    counter is reset for the next call.
+//    loads every candidate slot of the row in one batch, keeps those at or
+//    above the bound (index order preserved by a block scan over 64-slot
+//    groups) and selects the exact top k among them with block-wide radix
+//    passes over 12-bit digits whose window starts at the highest bit in
+//    which the live keys differ. The output is one ordered compaction.
 #include "device_common.h"
 #include "kernels.h"
-#include "wave_select.h"
 
 namespace ds4idx {
 namespace {
@@ -39,31 +42,37 @@ constexpr int NW = 8;
 constexpr int THREADS = NW * 64;
 constexpr int ROUNDS = 16;
 constexpr int WAVE_KEYS = ROUNDS * 64;
-constexpr int PART = NW * WAVE_KEYS;  // 8192
-constexpr int MREG = 32;              // merge keys held per thread
-constexpr int MSTAGE = THREADS * MREG;  // candidates the merge stages in LDS
-constexpr int MEXT = 32;              // largest per-partition order statistic kept for the row bound
-constexpr int MSURV = 2048;           // survivors of the bound that one wavefront selects from
+constexpr int PART = NW * WAVE_KEYS;     // 8192
+constexpr int HBITS = 12;                // histogram digit width
+constexpr int HBINS = 1 << HBITS;        // 4096 = 8 bins per thread
+constexpr int HSHIFT = 32 - HBITS;       // partition histogram: top 12 key bits
+constexpr int NLIST = 64;                // keys of one bin that a single wavefront ranks
+constexpr int MSURV = 8192;              // merge survivors held in LDS
+constexpr int MREG = MSURV / THREADS;    // survivors per thread
+constexpr int GB = 16;                   // 64-slot groups per wavefront per merge batch
+static_assert(HBINS == 8 * THREADS, "each thread owns eight histogram bins");
 
 typedef __attribute__((__vector_size__(8 * sizeof(short)))) short bf16x8;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 
 struct SplitSmem {
     union {
-        uint32_t sc[NW][WAVE_KEYS];            // partition score keys, 0 = no key
-        uint32_t fin[NW][MEXT];                // per-wavefront top-m keys (after sc is read)
-        uint32_t stage[MSTAGE + MSTAGE / 32];  // merge staging, one pad word per 32
+        uint32_t sc[NW][WAVE_KEYS];  // partition score keys, 0 = no key
+        struct {
+            uint32_t key[MSURV];     // merge survivors, index order
+            int idx[MSURV];
+        } sv;
     };
-    int stage_i[MSTAGE + MSTAGE / 32];        // merge staging: key indices
-    uint32_t fs[MSURV];                       // merge survivors: keys
-    int fe[MSURV];                            // merge survivors: key indices
-    uint32_t pt[kSplitMaxParts];              // partitions' m-th largest keys
-    uint32_t red[3][NW];
-    uint32_t hist[NW][256];
-    uint32_t tot[256];
+    uint32_t hist[HBINS];
+    uint32_t lk[NLIST];              // keys of one bin, for exact ranking
+    uint32_t gcnt[NW * GB];          // merge: survivors per 64-slot group
+    uint32_t goff[NW * GB];          // merge: output offset per group
+    uint32_t wcnt[2][NW];
     uint32_t wsum[NW];
-    uint32_t pick[2];
-    uint32_t pn[kSplitMaxParts];
+    uint32_t wmax[NW];
+    uint32_t red[2][NW];
+    uint32_t pick[12];
+    uint32_t nl;
     int last;
 };
 
@@ -79,6 +88,12 @@ __device__ __forceinline__ V load_agent(const V *p)
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// A candidate slot: order key in the low word (0 = empty), key index in the high word.
+__device__ __forceinline__ uint64_t slot(uint32_t key, long long index)
+{
+    return ((uint64_t)(uint32_t)index << 32) | key;
+}
+
 __device__ __forceinline__ int acc_row(int i, int lane) { return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3); }
 
 template <bool HI>
@@ -87,7 +102,8 @@ __device__ __forceinline__ uint32_t cvt2(uint32_t w)
     return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, HI));
 }
 
-// Block-wide exclusive prefix sum of v; `total` receives the block sum.
+// Block-wide exclusive prefix sum of v; `total` receives the block sum. One
+// barrier: sm.wsum must not be written again before the next barrier.
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, SplitSmem &sm, uint32_t &total)
 {
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
@@ -101,124 +117,187 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, SplitSmem &sm, u
         before += (w < wid) ? c : 0u;
         tot += c;
     }
-    __syncthreads();
     total = tot;
     return before + x - v;
 }
 
-// Block-wide sum, AND and OR.
-__device__ __forceinline__ void block_reduce3(uint32_t &s, uint32_t &a, uint32_t &o, SplitSmem &sm)
+// Block-wide AND and OR. One barrier.
+__device__ __forceinline__ void block_and_or(uint32_t &a, uint32_t &o, SplitSmem &sm)
 {
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-    s = wave_sum(s);
     a = wave_and(a);
     o = wave_or(o);
     if (lane == 0) {
-        sm.red[0][wid] = s;
-        sm.red[1][wid] = a;
-        sm.red[2][wid] = o;
+        sm.red[0][wid] = a;
+        sm.red[1][wid] = o;
     }
     __syncthreads();
-    s = 0u;
     a = ~0u;
     o = 0u;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
-        s += sm.red[0][w];
-        a &= sm.red[1][w];
-        o |= sm.red[2][w];
+        a &= sm.red[0][w];
+        o |= sm.red[1][w];
     }
-    __syncthreads();
 }
 
-// After every thread has added its keys to its wavefront's histogram, find
-// the digit of the k-th largest key and how many keys of that digit are
-// still wanted (sm.pick).
-__device__ __forceinline__ void pick_digit(SplitSmem &sm, uint32_t remaining)
+struct Found {
+    uint32_t bin;    // bin holding the target key
+    uint32_t above;  // keys in higher bins
+    uint32_t cnt;    // keys in the bin
+};
+
+// With sm.hist complete (a barrier passed): for each of up to three target
+// ranks (1-based from the largest key; 0, or more than the keys counted, =
+// no target) the bin holding that key. Thread t owns bins 4095 - 8t - j,
+// j = 0..7, so one scan in thread order runs from the top. Returns the
+// number of keys counted; with MAX, `bmax` receives the block maximum of
+// `mx`. Two barriers.
+template <int NT, bool MAX = false>
+__device__ __forceinline__ uint32_t hist_find(SplitSmem &sm, const uint32_t (&tgt)[NT], Found (&f)[NT],
+                                              uint32_t mx = 0u, uint32_t *bmax = nullptr)
 {
-    const int tid = threadIdx.x, lane = tid & 63;
-    __syncthreads();
-    if (tid < 256) {
-        uint32_t s = 0;
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int top = HBINS - 1 - 8 * tid;
+    const uint4 h = *reinterpret_cast<const uint4 *>(&sm.hist[top - 3]);
+    const uint4 l = *reinterpret_cast<const uint4 *>(&sm.hist[top - 7]);
+    const uint32_t c[8] = {h.w, h.z, h.y, h.x, l.w, l.z, l.y, l.x};
+    uint32_t s = 0;
 #pragma unroll
-        for (int w = 0; w < NW; ++w) s += sm.hist[w][tid];
-        sm.tot[tid] = s;
+    for (int j = 0; j < 8; ++j) s += c[j];
+    const uint32_t x = wave_scan_incl(s, 0u, OpAdd{});
+    if (MAX) mx = wave_max(mx);
+    if (lane == 63) {
+        sm.wsum[wid] = x;
+        if (MAX) sm.wmax[wid] = mx;
     }
     __syncthreads();
-    if (tid < 64) {
-        uint32_t c[4];
+    uint32_t run = x - s, total = 0;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) c[q] = sm.tot[4 * lane + q];
-        const uint32_t tot = c[0] + c[1] + c[2] + c[3];
-        const uint32_t incl = wave_scan_incl(tot, 0u, OpAdd{});
-        uint32_t above = wave_total(incl) - incl;
-        int found = -1;
-        uint32_t rem = 0;
+    for (int w = 0; w < NW; ++w) {
+        run += (w < wid) ? sm.wsum[w] : 0u;
+        total += sm.wsum[w];
+        if (MAX) mx = sm.wmax[w] > mx ? sm.wmax[w] : mx;
+    }
+    if (MAX) *bmax = mx;
 #pragma unroll
-        for (int q = 3; q >= 0; --q) {
-            if (found < 0 && above < remaining && remaining <= above + c[q]) {
-                found = q;
-                rem = remaining - above;
+    for (int j = 0; j < 8; ++j) {
+#pragma unroll
+        for (int q = 0; q < NT; ++q) {
+            if (tgt[q] <= total && run < tgt[q] && tgt[q] <= run + c[j]) {
+                sm.pick[3 * q] = (uint32_t)(top - j);
+                sm.pick[3 * q + 1] = run;
+                sm.pick[3 * q + 2] = c[j];
             }
-            above += c[q];
         }
-        const int src = __builtin_ctzll(wave_ballot(found >= 0));
-        if (lane == src) {
-            sm.pick[0] = (uint32_t)(4 * lane + found);
-            sm.pick[1] = rem;
-        }
+        run += c[j];
     }
     __syncthreads();
+#pragma unroll
+    for (int q = 0; q < NT; ++q) f[q] = Found{sm.pick[3 * q], sm.pick[3 * q + 1], sm.pick[3 * q + 2]};
+    return total;
+}
+
+// One wavefront: the r-th largest (1-based, r <= n) of the n <= 64 keys in
+// sm.lk, and how many of them are strictly larger. Wave-uniform results.
+__device__ __forceinline__ void list_rank(const SplitSmem &sm, uint32_t n, uint32_t r, uint32_t &kth,
+                                          uint32_t &gt_out)
+{
+    const int lane = threadIdx.x & 63;
+    const uint32_t mine = lane < (int)n ? sm.lk[lane] : 0u;
+    uint32_t gt = 0, ge = 0;
+    for (uint32_t j = 0; j < n; ++j) {
+        const uint32_t v = (uint32_t)__builtin_amdgcn_readlane((int)mine, (int)j);
+        gt += v > mine ? 1u : 0u;
+        ge += v >= mine ? 1u : 0u;
+    }
+    const int src = __builtin_ctzll(wave_ballot(lane < (int)n && gt < r && r <= ge));
+    kth = (uint32_t)__builtin_amdgcn_readlane((int)mine, src);
+    gt_out = (uint32_t)__builtin_amdgcn_readlane((int)gt, src);
+}
+
+// Appends the calling wavefront's keys that satisfy `in` to sm.lk (order
+// irrelevant; the caller knows there are at most NLIST of them).
+__device__ __forceinline__ void list_append(SplitSmem &sm, bool in, uint32_t key)
+{
+    const int lane = threadIdx.x & 63;
+    const uint64_t m = wave_ballot(in);
+    if (m == 0) return;
+    const int src = __builtin_ctzll(m);
+    uint32_t base = 0;
+    if (lane == src) base = atomicAdd(&sm.nl, (uint32_t)__builtin_popcountll(m));
+    base = (uint32_t)__builtin_amdgcn_readlane((int)base, src);
+    const uint32_t pos = base + lanes_below(m);
+    if (in && pos < (uint32_t)NLIST) sm.lk[pos] = key;
 }
 
 // Exact k-th largest key among the keys this block holds (0 = no key; more
-// than k keys present). each(f) calls f(key) for every key of the calling
-// thread. Returns tau, the k-th largest key, and ties, how many keys equal
-// to tau belong to the top k (the lowest-index ones).
+// than k keys present). each(f) calls f(key) for every nonzero key of the
+// calling thread. Returns tau, the k-th largest key, and ties, how many keys
+// equal to tau belong to the top k (the lowest-index ones). Each pass takes
+// the AND and OR of the keys still in play and histograms the 12 bits below
+// their highest differing bit; a bin of at most 64 keys is ranked exactly by
+// one wavefront.
 template <class Each>
-__device__ void block_select(Each each, uint32_t k, SplitSmem &sm, uint32_t &tau, uint32_t &ties)
+__device__ __forceinline__ void block_kth(Each each, uint32_t k, SplitSmem &sm, uint32_t &tau, uint32_t &ties)
 {
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int tid = threadIdx.x, wid = tid >> 6;
     uint32_t prefix = 0, pmask = 0, remaining = k;
-    {
-        // When at least k scores are >= +0, the k-th largest is too.
-        uint32_t nn = 0, a = 0, o = 0;
-        each([&](uint32_t u) { nn += u >= 0x80000000u ? 1u : 0u; });
-        block_reduce3(nn, a, o, sm);
-        if (nn >= k) prefix = pmask = 0x80000000u;
-    }
-    while (pmask != ~0u) {
-        uint32_t n = 0, a = ~0u, o = 0u;
+    for (;;) {
+        for (int b = tid; b < HBINS; b += THREADS) sm.hist[b] = 0;
+        if (tid == 0) sm.nl = 0;
+        uint32_t a = ~0u, o = 0u;
         each([&](uint32_t u) {
             if ((u & pmask) == prefix) {
                 a &= u;
                 o |= u;
             }
         });
-        block_reduce3(n, a, o, sm);
+        block_and_or(a, o, sm);
         const uint32_t diff = (a ^ o) & ~pmask;
         if (diff == 0u) {  // every key still in play is equal: that is tau
-            prefix = a;
-            break;
+            tau = a;
+            ties = remaining;
+            return;
         }
         const int hb = 31 - __builtin_clz(diff);
         const uint32_t above = hb == 31 ? 0u : (~0u << (hb + 1));
         prefix = (prefix & pmask) | (a & above & ~pmask);
         pmask |= above;
-        const int lo = hb >= 7 ? hb - 7 : 0;
+        const int lo = hb >= HBITS - 1 ? hb - (HBITS - 1) : 0;
         const uint32_t dmask = (2u << (hb - lo)) - 1u;
-        for (int b = lane; b < 256; b += 64) sm.hist[wid][b] = 0;
-        wave_lds_sync();
         each([&](uint32_t u) {
-            if ((u & pmask) == prefix) atomicAdd(&sm.hist[wid][(u >> lo) & dmask], 1u);
+            if ((u & pmask) == prefix) atomicAdd(&sm.hist[(u >> lo) & dmask], 1u);
         });
-        pick_digit(sm, remaining);
-        prefix |= sm.pick[0] << lo;
+        __syncthreads();
+        Found fd[1];
+        hist_find<1>(sm, {remaining}, fd);
+        const Found f = fd[0];
+        remaining -= f.above;
+        prefix |= f.bin << lo;
         pmask |= dmask << lo;
-        remaining = sm.pick[1];
+        if (pmask == ~0u) {
+            tau = prefix;
+            ties = remaining;
+            return;
+        }
+        if (f.cnt <= (uint32_t)NLIST) {
+            each([&](uint32_t u) { list_append(sm, (u & pmask) == prefix, u); });
+            __syncthreads();
+            if (wid == 0) {
+                uint32_t kth, gt;
+                list_rank(sm, f.cnt, remaining, kth, gt);
+                if ((threadIdx.x & 63) == 0) {
+                    sm.pick[9] = kth;
+                    sm.pick[10] = remaining - gt;
+                }
+            }
+            __syncthreads();
+            tau = sm.pick[9];
+            ties = sm.pick[10];
+            return;
+        }
     }
-    tau = prefix;
-    ties = remaining;
 }
 
 // This lane's half of one key row of a 32-key sub-block (key = base + lane%32,
@@ -291,10 +370,9 @@ __device__ __forceinline__ float score_sub(const Raw<KFP8> &r, const bf16x8 (&a)
 template <bool KFP8>
 __global__ __launch_bounds__(THREADS, 1) void split_indexer_kernel(
     const uint16_t *__restrict__ Q, const uint8_t *__restrict__ K, const float *__restrict__ Ks,
-    const float *__restrict__ W, int T, int S, long long offset, int topk, int P,
-    uint32_t *__restrict__ ctr, uint32_t *__restrict__ cand_n, uint32_t *__restrict__ cand_t,
-    float *__restrict__ cand_s, int *__restrict__ cand_i, int *__restrict__ idx,
-    float *__restrict__ vals)
+    const float *__restrict__ W, int T, int S, long long offset, int topk, int P, int slots, int s1,
+    uint32_t *__restrict__ ctr, uint64_t *__restrict__ meta, uint64_t *__restrict__ full_list,
+    uint64_t *__restrict__ short_list, int *__restrict__ idx, float *__restrict__ vals)
 {
     __shared__ SplitSmem sm;
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -305,7 +383,11 @@ __global__ __launch_bounds__(THREADS, 1) void split_indexer_kernel(
     const long long pbase = (long long)p * PART;
     const long long nvalid = L - pbase < 0 ? 0 : (L - pbase > PART ? PART : L - pbase);
 
-    // ---- score this wavefront's 1024 keys into sm.sc
+    for (int i = tid; i < HBINS; i += THREADS) sm.hist[i] = 0;
+    if (tid == 0) sm.nl = 0;
+    __syncthreads();
+
+    // ---- score this wavefront's 1024 keys into sm.sc and the histogram
     const long long wbase = pbase + (long long)wid * WAVE_KEYS;
     const long long wkeys = L - wbase < 0 ? 0 : (L - wbase > WAVE_KEYS ? WAVE_KEYS : L - wbase);
     if (wkeys > 0) {
@@ -356,7 +438,9 @@ __global__ __launch_bounds__(THREADS, 1) void split_indexer_kernel(
                         float sc = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
                         if (KFP8) sc *= pscale;
                         const long long key = wbase + 32 * (sb - 1) + lane;
-                        sm.sc[wid][32 * (sb - 1) + lane] = key < L ? ord_key(canon(sc)) : 0u;
+                        const uint32_t ok = ord_key(canon(sc));
+                        sm.sc[wid][32 * (sb - 1) + lane] = key < L ? ok : 0u;
+                        if (key < L && ok != 0u) atomicAdd(&sm.hist[ok >> HSHIFT], 1u);
                     } else {
                         prev = part;
                     }
@@ -365,84 +449,152 @@ __global__ __launch_bounds__(THREADS, 1) void split_indexer_kernel(
         }
     }
     for (int i = (int)(((wkeys + 63) / 64) * 64) + lane; i < WAVE_KEYS; i += 64) sm.sc[wid][i] = 0u;
-    wave_lds_sync();
+    __syncthreads();
     uint32_t u[ROUNDS];
 #pragma unroll
     for (int j = 0; j < ROUNDS; ++j) u[j] = sm.sc[wid][j * 64 + lane];
 
-    // ---- exact top-k of this partition, in index order (wave, round, lane)
-    const uint32_t want = (uint32_t)(nvalid < topk ? nvalid : topk);
-    const bool select_all = nvalid <= topk;
-    uint32_t tau = 0, ties = 0;
-    if (!select_all) {
-        block_select(
+    // ---- bins of the partition's k-th, m-th and c1-th largest keys. The
+    // full partitions of the row (PART keys each) alone hold fullp*m >= k
+    // keys. Only nonzero keys are counted: the all-ones NaN pattern maps to
+    // key 0, which reads as "no key" everywhere.
+    const long long fullp = L / PART;
+    const uint32_t mth = fullp > 0 ? (uint32_t)((topk + fullp - 1) / fullp) : 0u;  // 0: no bound
+    const uint32_t c1 = (uint32_t)(s1 / 4);
+    uint32_t mykmax = 0, kmax;
+#pragma unroll
+    for (int j = 0; j < ROUNDS; ++j) mykmax = u[j] > mykmax ? u[j] : mykmax;
+    Found fd[3];
+    const uint32_t nkeys = hist_find<3, true>(sm, {(uint32_t)topk, mth, c1}, fd, mykmax, &kmax);
+    const Found fk = fd[0], fm = fd[1], f1 = fd[2];
+    const bool has_m = mth > 0 && nkeys >= mth;
+    const bool all = nkeys <= (uint32_t)topk;
+    // Keys at or above `edge` form the full candidate list: all keys when
+    // the partition holds at most k, else everything from the k-th key's bin
+    // up. Keys at or above `edge1` (from the c1-th key's bin up) form the
+    // short list, which serves the merge whenever edge1 <= the row bound.
+    const uint32_t edge = all ? 1u : (fk.bin << HSHIFT);
+    const uint32_t F = all ? nkeys : fk.above + fk.cnt;
+    const uint32_t edge1 = nkeys < c1 ? 1u : (f1.bin << HSHIFT);
+    const uint32_t n1 = nkeys < c1 ? nkeys : f1.above + f1.cnt;
+    const bool short_ok = n1 <= (uint32_t)s1;
+    const bool refine = has_m && fm.cnt <= (uint32_t)NLIST;
+    const long long cb = (r * P + p) * (long long)slots;
+    const long long cb1 = (r * P + p) * (long long)s1;
+    // This partition's m-th largest key (~0: no bound from it), published by
+    // wavefront 0 with the short list's edge and the largest key once the
+    // keys of the m-th key's bin are in sm.lk: exact when that bin is small,
+    // else its lower edge (still m keys at or above it).
+    auto publish_meta = [&]() {
+        if (wid != 0) return;
+        uint32_t tp = ~0u;
+        if (refine) {
+            uint32_t gt;
+            list_rank(sm, fm.cnt, mth - fm.above, tp, gt);
+        } else if (has_m) {
+            tp = fm.bin << HSHIFT;
+        }
+        if (lane == 0) {
+            store_agent(&meta[2 * (r * P + p)], ((uint64_t)(short_ok ? edge1 : ~0u) << 32) | tp);
+            store_agent(&meta[2 * (r * P + p) + 1], (uint64_t)kmax);
+        }
+    };
+    auto gidx = [&](int j) { return pbase + (long long)wid * WAVE_KEYS + j * 64 + lane; };
+    // Per-wavefront counts of the short list, then its ordered write.
+    uint32_t w1 = 0;
+    if (short_ok) {
+#pragma unroll
+        for (int j = 0; j < ROUNDS; ++j) w1 += (uint32_t)__builtin_popcountll(wave_ballot(u[j] >= edge1));
+    }
+    auto write_short = [&]() {
+        if (!short_ok) return;
+        uint32_t out = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) out += (w < wid) ? sm.wcnt[2][w] : 0u;
+#pragma unroll
+        for (int j = 0; j < ROUNDS; ++j) {
+            const bool keep = u[j] >= edge1;
+            const uint64_t mk = wave_ballot(keep);
+            const uint32_t pos = out + lanes_below(mk);
+            if (keep && pos < (uint32_t)s1) store_agent(&short_list[cb1 + pos], slot(u[j], gidx(j)));
+            out += (uint32_t)__builtin_popcountll(mk);
+        }
+        for (int i = (int)n1 + tid; i < s1; i += THREADS) store_agent(&short_list[cb1 + i], (uint64_t)0);
+    };
+    if (F <= (uint32_t)slots) {
+        uint32_t wc = 0;
+#pragma unroll
+        for (int j = 0; j < ROUNDS; ++j) {
+            wc += (uint32_t)__builtin_popcountll(wave_ballot(u[j] >= edge));
+            if (refine) list_append(sm, u[j] != 0u && (u[j] >> HSHIFT) == fm.bin, u[j]);
+        }
+        if (lane == 0) {
+            sm.wcnt[0][wid] = wc;
+            sm.wcnt[2][wid] = w1;
+        }
+        __syncthreads();
+        uint32_t out = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) out += (w < wid) ? sm.wcnt[0][w] : 0u;
+#pragma unroll
+        for (int j = 0; j < ROUNDS; ++j) {
+            const bool keep = u[j] >= edge;
+            const uint64_t mk = wave_ballot(keep);
+            const uint32_t pos = out + lanes_below(mk);
+            if (keep && pos < (uint32_t)slots) store_agent(&full_list[cb + pos], slot(u[j], gidx(j)));
+            out += (uint32_t)__builtin_popcountll(mk);
+        }
+        for (int i = (int)F + tid; i < slots; i += THREADS) store_agent(&full_list[cb + i], (uint64_t)0);
+        write_short();
+        publish_meta();
+    } else {
+        // Too many keys share the k-th key's bin: exact selection of k.
+        if (refine) {
+#pragma unroll
+            for (int j = 0; j < ROUNDS; ++j) list_append(sm, u[j] != 0u && (u[j] >> HSHIFT) == fm.bin, u[j]);
+        }
+        if (lane == 0) sm.wcnt[2][wid] = w1;
+        __syncthreads();
+        write_short();
+        publish_meta();  // before block_kth reuses sm.lk (its first barrier orders the two)
+        uint32_t tau, ties;
+        block_kth(
             [&](auto f) {
 #pragma unroll
                 for (int j = 0; j < ROUNDS; ++j)
                     if (u[j] != 0u) f(u[j]);
             },
             (uint32_t)topk, sm, tau, ties);
-    }
-    uint32_t neq = 0;
+        uint32_t ngt = 0, neq = 0;
 #pragma unroll
-    for (int j = 0; j < ROUNDS; ++j)
-        neq += (uint32_t)__builtin_popcountll(wave_ballot(!select_all && u[j] != 0u && u[j] == tau));
-    uint32_t total;
-    uint32_t eq_before = block_excl_scan(lane == 0 ? neq : 0u, sm, total);
-    eq_before = (uint32_t)__builtin_amdgcn_readlane((int)eq_before, 0);
-    uint32_t keepbits = 0, nkeep = 0;
-#pragma unroll
-    for (int j = 0; j < ROUNDS; ++j) {
-        const bool valid = u[j] != 0u;
-        const bool eq = !select_all && valid && u[j] == tau;
-        const uint64_t meq = wave_ballot(eq);
-        const bool keep = valid && (select_all || u[j] > tau || (eq && eq_before + lanes_below(meq) < ties));
-        eq_before += (uint32_t)__builtin_popcountll(meq);
-        const uint64_t mk = wave_ballot(keep);
-        keepbits |= keep ? (1u << j) : 0u;
-        nkeep += (uint32_t)__builtin_popcountll(mk);
-    }
-    uint32_t out = block_excl_scan(lane == 0 ? nkeep : 0u, sm, total);
-    out = (uint32_t)__builtin_amdgcn_readlane((int)out, 0);
-    const long long cbase = (r * P + p) * (long long)topk;
-#pragma unroll
-    for (int j = 0; j < ROUNDS; ++j) {
-        const bool keep = (keepbits >> j) & 1u;
-        const uint64_t mk = wave_ballot(keep);
-        const uint32_t pos = out + lanes_below(mk);
-        if (keep && pos < want) {
-            store_agent(&cand_s[cbase + pos], key_float(u[j]));
-            store_agent(&cand_i[cbase + pos], (int)(pbase + (long long)wid * WAVE_KEYS + j * 64 + lane));
+        for (int j = 0; j < ROUNDS; ++j) {
+            ngt += (uint32_t)__builtin_popcountll(wave_ballot(u[j] > tau));
+            neq += (uint32_t)__builtin_popcountll(wave_ballot(u[j] != 0u && u[j] == tau));
         }
-        out += (uint32_t)__builtin_popcountll(mk);
-    }
-    if (tid == 0) store_agent(&cand_n[r * P + p], want);
-    // Unused slots hold the key-0 pattern (all bits set), which reads as "no key".
-    for (int i = (int)want + tid; i < topk; i += THREADS) store_agent(&cand_s[cbase + i], __uint_as_float(~0u));
-
-    // ---- this partition's m-th largest key, m = ceil(k / P). With every
-    // partition holding m keys at or above its own m-th, the row holds at
-    // least P*m >= k keys at or above the smallest of them: a lower bound on
-    // the row's k-th key that lets the merge skip most candidates.
-    const int mth = (topk + P - 1) / P;
-    if (mth <= MEXT) {
-        uint32_t top[MEXT];
-        wave_mth_key<ROUNDS>(u, mth, lane, top);  // this wavefront's m largest keys
-        if (lane == 0)
-            for (int i = 0; i < mth; ++i) sm.fin[wid][i] = top[i];
+        if (lane == 0) {
+            sm.wcnt[0][wid] = ngt;
+            sm.wcnt[1][wid] = neq;
+        }
         __syncthreads();
-        if (wid == 0) {
-            uint32_t fu[(NW * MEXT) / 64];
+        uint32_t gtb = 0, eqb = 0;
 #pragma unroll
-            for (int j = 0; j < (NW * MEXT) / 64; ++j) {
-                const int i = j * 64 + lane;
-                fu[j] = (i % MEXT) < mth ? sm.fin[i / MEXT][i % MEXT] : 0u;
-            }
-            const uint32_t tp = wave_mth_key<(NW * MEXT) / 64>(fu, mth, lane, nullptr);
-            if (lane == 0) store_agent(&cand_t[r * P + p], tp);  // 0: fewer than m keys, no bound
+        for (int w = 0; w < NW; ++w) {
+            gtb += (w < wid) ? sm.wcnt[0][w] : 0u;
+            eqb += (w < wid) ? sm.wcnt[1][w] : 0u;
         }
-    } else if (tid == 0) {
-        store_agent(&cand_t[r * P + p], 0u);
+        uint32_t out = gtb + (eqb < ties ? eqb : ties);
+#pragma unroll
+        for (int j = 0; j < ROUNDS; ++j) {
+            const bool eq = u[j] != 0u && u[j] == tau;
+            const uint64_t meq = wave_ballot(eq);
+            const bool keep = u[j] > tau || (eq && eqb + lanes_below(meq) < ties);
+            const uint64_t mk = wave_ballot(keep);
+            const uint32_t pos = out + lanes_below(mk);
+            if (keep && pos < (uint32_t)slots) store_agent(&full_list[cb + pos], slot(u[j], gidx(j)));
+            out += (uint32_t)__builtin_popcountll(mk);
+            eqb += (uint32_t)__builtin_popcountll(meq);
+        }
+        for (int i = topk + tid; i < slots; i += THREADS) store_agent(&full_list[cb + i], (uint64_t)0);
     }
 
     // ---- arrival: the last workgroup of the row merges. The candidate lists
@@ -450,6 +602,8 @@ __global__ __launch_bounds__(THREADS, 1) void split_indexer_kernel(
     // bypass the per-XCD L2's non-coherent lines; waiting for every store to
     // complete before the counter increment orders them, with no cache-wide
     // writeback or invalidate.
+    for (int i = tid; i < HBINS; i += THREADS) sm.hist[i] = 0;  // for the merge
+    if (tid == 0) sm.nl = 0;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (tid == 0)
@@ -458,198 +612,249 @@ __global__ __launch_bounds__(THREADS, 1) void split_indexer_kernel(
     __syncthreads();
     if (!sm.last) return;
 
-    const int E = P * topk;  // <= kSplitMaxParts * DS4IDX_MAX_TOPK
-    const float *rs = cand_s + r * E;
-    const int *ri = cand_i + r * E;
     int *io = idx + r * topk;
     float *vo = vals ? vals + r * topk : nullptr;
-    // Element e = (partition, position) in index order; thread t owns the
-    // contiguous run [t*chunk, (t+1)*chunk), which keeps the output order.
-    const int chunk = (E + THREADS - 1) / THREADS;
-    const int e0 = tid * chunk;
-    uint32_t m_out = 0;  // selected count (the rest of the row is padding)
-    if (chunk <= MREG) {
-        // One batch of device-coherent loads, all in flight before any is used:
-        // every other workgroup's stores completed before its counter increment.
-        // Unused slots carry the no-key pattern, so no per-partition counts.
-        float vs[MREG];
-        int vi[MREG];
+    const uint64_t *rs = short_list + r * P * (long long)s1;
+    const uint64_t *rf = full_list + r * P * (long long)slots;
+    const int G1 = P * (s1 / 64), GF = P * (slots / 64);
+
+    // Survivors of the bound from a slot grid (every partition's list padded
+    // to `per` slots with empty ones) in slot = index order: 64-slot group g,
+    // wavefront w takes groups w + 8i. Returns false when they exceed MSURV.
+    uint32_t Fs = 0;
+    auto collect_batch = [&](const uint64_t (&v)[GB], uint32_t bound) {
+        uint32_t mycnt = 0;
 #pragma unroll
-        for (int j = 0; j < MREG; ++j) {
-            const int e = tid + THREADS * j;
-            vs[j] = e < E ? load_agent(&rs[e]) : __uint_as_float(~0u);
-            vi[j] = e < E ? load_agent(&ri[e]) : 0;
+        for (int i = 0; i < GB; ++i) {
+            const uint32_t key = (uint32_t)v[i];
+            const uint32_t c = (uint32_t)__builtin_popcountll(wave_ballot(key != 0u && key >= bound));
+            mycnt = lane == i ? c : mycnt;
         }
-        const uint32_t ptv = tid < P ? load_agent(&cand_t[r * P + tid]) : ~0u;
-        const uint32_t wb = wave_min(ptv);
-        if (lane == 0) sm.red[0][wid] = wb;
-#pragma unroll
-        for (int j = 0; j < MREG; ++j) {
-            const int e = tid + THREADS * j;
-            if (e < E) {
-                sm.stage[e + (e >> 5)] = ord_key(vs[j]);
-                sm.stage_i[e + (e >> 5)] = vi[j];
-            }
-        }
+        if (lane < GB) sm.gcnt[wid + NW * lane] = mycnt;
         __syncthreads();
-        uint32_t bound = ~0u;  // keys below it cannot be among the row's top k (0: no bound)
+        uint32_t tot;
+        const uint32_t ex = block_excl_scan(tid < NW * GB ? sm.gcnt[tid] : 0u, sm, tot);
+        if (tid < NW * GB) sm.goff[tid] = Fs + ex;
+        __syncthreads();
+        if (Fs + tot > (uint32_t)MSURV) return false;
 #pragma unroll
-        for (int w = 0; w < NW; ++w) bound = sm.red[0][w] < bound ? sm.red[0][w] : bound;
-        uint32_t mu[MREG];
-#pragma unroll
-        for (int i = 0; i < MREG; ++i) {
-            const int e = e0 + i;
-            mu[i] = (i < chunk && e < E) ? sm.stage[e + (e >> 5)] : 0u;
+        for (int i = 0; i < GB; ++i) {
+            const uint32_t key = (uint32_t)v[i];
+            const bool keep = key != 0u && key >= bound;
+            const uint64_t mk = wave_ballot(keep);
+            if (mk != 0) {
+                const uint32_t pos = sm.goff[wid + NW * i] + lanes_below(mk);
+                if (keep) {
+                    sm.sv.key[pos] = key;
+                    sm.sv.idx[pos] = (int)(v[i] >> 32);
+                }
+            }
         }
-        // Survivors of the bound, kept in (partition, position) = index order.
-        uint32_t nsurv = 0;
+        Fs += tot;
+        return true;
+    };
+    auto load_batch = [&](uint64_t (&v)[GB], const uint64_t *grid, int G, int g0) {
 #pragma unroll
-        for (int i = 0; i < MREG; ++i) nsurv += (mu[i] != 0u && mu[i] >= bound) ? 1u : 0u;
-        uint32_t F;
-        const uint32_t sbase = block_excl_scan(nsurv, sm, F);
-        // With a bound, F >= k whenever the row has k keys; without one, F = all keys.
-        const uint32_t m = F < (uint32_t)topk ? F : (uint32_t)topk;
-        const bool all = F <= (uint32_t)topk;
-        m_out = m;
-        if (F <= (uint32_t)topk) {
-            // Everything that survives is selected (F = min(N, k) here).
-            uint32_t pos = sbase;
+        for (int i = 0; i < GB; ++i) {
+            const int g = g0 + wid + NW * i;
+            v[i] = g < G ? load_agent(&grid[(long long)g * 64 + lane]) : (uint64_t)0;
+        }
+    };
+    auto collect = [&](const uint64_t *grid, int G, uint32_t bound) {
+        for (int g0 = 0; g0 < G; g0 += NW * GB) {
+            uint64_t v[GB];
+            load_batch(v, grid, G, g0);
+            if (!collect_batch(v, bound)) return false;
+        }
+        return true;
+    };
+
+    // The first batch of short lists is in flight with the partitions'
+    // bounds. Row bound: the smallest published m-th key; the short lists
+    // serve when every partition's short-list edge is at or below it.
+    uint64_t v0[GB];
+    load_batch(v0, rs, G1, 0);
+    uint32_t tq = ~0u, eq1 = 0u, mq = 0u;
+    for (int q = lane; q < P; q += 64) {
+        const uint64_t a = load_agent(&meta[2 * (r * P + q)]);
+        const uint32_t b = (uint32_t)load_agent(&meta[2 * (r * P + q) + 1]);
+        const uint32_t t = (uint32_t)a, e1 = (uint32_t)(a >> 32);
+        tq = t < tq ? t : tq;
+        eq1 = e1 > eq1 ? e1 : eq1;
+        mq = b > mq ? b : mq;
+    }
+    uint32_t bound = wave_min(tq);
+    if (bound == ~0u) bound = 0u;
+    const uint32_t kmax_row = wave_max(mq);
+    const bool use_short = bound != 0u && wave_max(eq1) <= bound;
+
+    uint32_t m_out;
+    if (use_short && G1 <= NW * GB) {
+        // Select straight from the loaded short lists. Every key in play lies
+        // in [bound, row maximum], so they share the bits above the highest
+        // bit in which those two differ: the 12 bits below it are the first
+        // digit, with no reduction pass.
+        uint32_t kk[GB];
 #pragma unroll
-            for (int i = 0; i < MREG; ++i) {
-                if (mu[i] != 0u && mu[i] >= bound) {
-                    if (pos < m) {
-                        io[pos] = sm.stage_i[(e0 + i) + ((e0 + i) >> 5)];
-                        if (vo) vo[pos] = key_float(mu[i]);
+        for (int i = 0; i < GB; ++i) kk[i] = (uint32_t)v0[i] >= bound ? (uint32_t)v0[i] : 0u;
+        const int hb = 31 - __builtin_clz((bound ^ kmax_row) | 1u);
+        const int lo = hb >= HBITS - 1 ? hb - (HBITS - 1) : 0;
+        const uint32_t dmask = (2u << (hb - lo)) - 1u;
+        const uint32_t prefix = hb == 31 ? 0u : (bound & (~0u << (hb + 1)));
+#pragma unroll
+        for (int i = 0; i < GB; ++i)
+            if (kk[i] != 0u) atomicAdd(&sm.hist[(kk[i] >> lo) & dmask], 1u);
+        __syncthreads();
+        Found fd[1];
+        const uint32_t total = hist_find<1>(sm, {(uint32_t)topk}, fd);
+        uint32_t tau = 0, ties = 0;  // at most k keys in play: all are kept
+        if (total > (uint32_t)topk) {
+            const Found f = fd[0];
+            const uint32_t rem = (uint32_t)topk - f.above;
+            if (lo == 0) {
+                tau = prefix | f.bin;
+                ties = rem;
+            } else if (f.cnt <= (uint32_t)NLIST) {
+#pragma unroll
+                for (int i = 0; i < GB; ++i) list_append(sm, kk[i] != 0u && ((kk[i] >> lo) & dmask) == f.bin, kk[i]);
+                __syncthreads();
+                if (wid == 0) {
+                    uint32_t kth, gt;
+                    list_rank(sm, f.cnt, rem, kth, gt);
+                    if (lane == 0) {
+                        sm.pick[9] = kth;
+                        sm.pick[10] = rem - gt;
                     }
-                    ++pos;
                 }
-            }
-        } else if (F <= (uint32_t)MSURV) {
-            uint32_t pos = sbase;
+                __syncthreads();
+                tau = sm.pick[9];
+                ties = sm.pick[10];
+            } else {
+                block_kth(
+                    [&](auto fn) {
 #pragma unroll
-            for (int i = 0; i < MREG; ++i) {
-                if (mu[i] != 0u && mu[i] >= bound) {
-                    sm.fs[pos] = mu[i];
-                    sm.fe[pos] = sm.stage_i[(e0 + i) + ((e0 + i) >> 5)];
-                    ++pos;
-                }
-            }
-            __syncthreads();
-            if (wid == 0) {  // one wavefront, no block barriers: exact top-k of the survivors
-                uint32_t fu[MSURV / 64];
-#pragma unroll
-                for (int j = 0; j < MSURV / 64; ++j) {
-                    const int i = j * 64 + lane;
-                    fu[j] = i < (int)F ? sm.fs[i] : 0u;
-                }
-                uint32_t ties;
-                const uint32_t tau = wave_kth_key<MSURV / 64>(fu, (uint32_t)topk, sm.hist[0], lane, ties);
-                uint32_t out = 0, tr = 0;
-#pragma unroll
-                for (int j = 0; j < MSURV / 64; ++j) {
-                    const int i = j * 64 + lane;
-                    const bool eq = fu[j] != 0u && fu[j] == tau;
-                    const uint64_t meq = wave_ballot(eq);
-                    const bool keep = fu[j] != 0u && (fu[j] > tau || (eq && tr + lanes_below(meq) < ties));
-                    const uint64_t mk = wave_ballot(keep);
-                    const uint32_t o = out + lanes_below(mk);
-                    if (keep && o < m) {
-                        io[o] = sm.fe[i];
-                        if (vo) vo[o] = key_float(fu[j]);
-                    }
-                    out += (uint32_t)__builtin_popcountll(mk);
-                    tr += (uint32_t)__builtin_popcountll(meq);
-                }
-            }
-        } else {
-            // Too many survivors (adversarial rows): block-wide selection of all.
-            uint32_t mtau = 0, mties = 0;
-            if (!all) {
-                block_select(
-                    [&](auto f) {
-#pragma unroll
-                        for (int i = 0; i < MREG; ++i)
-                            if (mu[i] != 0u) f(mu[i]);
+                        for (int i = 0; i < GB; ++i)
+                            if (kk[i] != 0u) fn(kk[i]);
                     },
-                    (uint32_t)topk, sm, mtau, mties);
+                    (uint32_t)topk, sm, tau, ties);
             }
-            uint32_t my_eq = 0;
+        }
+        // Ordered output: group g = w + 8i holds slots 64g .. 64g+63 in index
+        // order; one scan over per-group (greater, equal) counts places them.
+        uint32_t mycnt = 0;
 #pragma unroll
-            for (int i = 0; i < MREG; ++i) my_eq += (!all && mu[i] != 0u && mu[i] == mtau) ? 1u : 0u;
-            uint32_t run = block_excl_scan(my_eq, sm, total);
-            uint64_t keepmask = 0;
-            uint32_t my_keep = 0;
+        for (int i = 0; i < GB; ++i) {
+            const uint32_t ngt = (uint32_t)__builtin_popcountll(wave_ballot(kk[i] > tau));
+            const uint32_t neq = (uint32_t)__builtin_popcountll(wave_ballot(kk[i] != 0u && kk[i] == tau));
+            mycnt = lane == i ? (ngt | (neq << 16)) : mycnt;  // counts < 2^14
+        }
+        if (lane < GB) sm.gcnt[wid + NW * lane] = mycnt;
+        __syncthreads();
+        uint32_t tot;
+        const uint32_t ex = block_excl_scan(tid < NW * GB ? sm.gcnt[tid] : 0u, sm, tot);
+        if (tid < NW * GB) sm.goff[tid] = ex;
+        __syncthreads();
 #pragma unroll
-            for (int i = 0; i < MREG; ++i) {
-                const bool valid = mu[i] != 0u;
-                const bool eq = !all && valid && mu[i] == mtau;
-                const bool keep = valid && (all || mu[i] > mtau || (eq && run < mties));
-                run += eq ? 1u : 0u;
-                keepmask |= keep ? (1ull << i) : 0ull;
-                my_keep += keep ? 1u : 0u;
+        for (int i = 0; i < GB; ++i) {
+            const uint32_t base = sm.goff[wid + NW * i];
+            const uint32_t eqb = base >> 16;
+            const bool eq = kk[i] != 0u && kk[i] == tau;
+            const uint64_t meq = wave_ballot(eq);
+            const bool keep = kk[i] > tau || (eq && eqb + lanes_below(meq) < ties);
+            const uint64_t mk = wave_ballot(keep);
+            const uint32_t pos = (base & 0xffffu) + (eqb < ties ? eqb : ties) + lanes_below(mk);
+            if (keep && pos < (uint32_t)topk) {
+                io[pos] = (int)(v0[i] >> 32);
+                if (vo) vo[pos] = key_float(kk[i]);
             }
-            uint32_t pos = block_excl_scan(my_keep, sm, total);
-#pragma unroll
+        }
+        m_out = total < (uint32_t)topk ? total : (uint32_t)topk;
+    } else {
+        const bool ok = use_short ? collect(rs, G1, bound) : collect(rf, GF, bound);
+        __syncthreads();
+        if (ok) {
+            // Thread t owns the contiguous run [t*ch, t*ch + ch) of survivors.
+            const int ch = (int)((Fs + THREADS - 1) / THREADS);
+            const int e0 = tid * ch;
+            uint32_t su[MREG];
+    #pragma unroll
             for (int i = 0; i < MREG; ++i) {
-                if ((keepmask >> i) & 1ull) {
-                    if (pos < m) {
-                        io[pos] = sm.stage_i[(e0 + i) + ((e0 + i) >> 5)];
-                        if (vo) vo[pos] = key_float(mu[i]);
-                    }
+                const int e = e0 + i;
+                su[i] = (i < ch && e < (int)Fs) ? sm.sv.key[e] : 0u;
+            }
+            uint32_t tau = 0, ties = 0;  // with at most k survivors every one is kept
+            if (Fs > (uint32_t)topk) {
+                block_kth(
+                    [&](auto f) {
+    #pragma unroll
+                        for (int i = 0; i < MREG; ++i)
+                            if (su[i] != 0u) f(su[i]);
+                    },
+                    (uint32_t)topk, sm, tau, ties);
+            }
+            uint32_t ngt = 0, neq = 0;
+    #pragma unroll
+            for (int i = 0; i < MREG; ++i) {
+                ngt += su[i] > tau ? 1u : 0u;
+                neq += (su[i] != 0u && su[i] == tau) ? 1u : 0u;
+            }
+            uint32_t tot;
+            const uint32_t ex = block_excl_scan(ngt | (neq << 16), sm, tot);  // counts < 2^14
+            uint32_t eqb = ex >> 16;
+            uint32_t pos = (ex & 0xffffu) + (eqb < ties ? eqb : ties);
+    #pragma unroll
+            for (int i = 0; i < MREG; ++i) {
+                bool keep = su[i] > tau;
+                if (su[i] != 0u && su[i] == tau) keep = eqb++ < ties;
+                if (keep && pos < (uint32_t)topk) {
+                    io[pos] = sm.sv.idx[e0 + i];
+                    if (vo) vo[pos] = key_float(su[i]);
                     ++pos;
                 }
             }
-        }
-    } else {
-        // Long candidate lists: the same selection, reading the workspace.
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // drop stale L2 lines, then plain loads
-        for (int q = tid; q < P; q += THREADS) sm.pn[q] = cand_n[r * P + q];
-        __syncthreads();
-        uint32_t N = 0;
-        for (int q = 0; q < P; ++q) N += sm.pn[q];
-        const uint32_t m = N < (uint32_t)topk ? N : (uint32_t)topk;
-        const bool all = N <= (uint32_t)topk;
-        m_out = m;
-        auto valid_at = [&](int e) {
-            const int q = e / topk;
-            return (uint32_t)(e - q * topk) < sm.pn[q];
-        };
-        uint32_t mtau = 0, mties = 0;
-        if (!all) {
-            block_select(
-                [&](auto f) {
-                    for (int e = tid; e < E; e += THREADS)
-                        if (valid_at(e)) f(ord_key(rs[e]));
-                },
-                (uint32_t)topk, sm, mtau, mties);
-        }
-        const int e1 = e0 + chunk < E ? e0 + chunk : E;
-        uint32_t my_eq = 0;
-        for (int e = e0; e < e1; ++e)
-            if (valid_at(e)) my_eq += (!all && ord_key(rs[e]) == mtau) ? 1u : 0u;
-        const uint32_t eq_base = block_excl_scan(my_eq, sm, total);
-        uint32_t my_keep = 0, run = eq_base;
-        for (int e = e0; e < e1; ++e) {
-            if (!valid_at(e)) continue;
-            const uint32_t uu = ord_key(rs[e]);
-            const bool eq = !all && uu == mtau;
-            my_keep += (all || uu > mtau || (eq && run < mties)) ? 1u : 0u;
-            run += eq ? 1u : 0u;
-        }
-        uint32_t pos = block_excl_scan(my_keep, sm, total);
-        run = eq_base;
-        for (int e = e0; e < e1; ++e) {
-            if (!valid_at(e)) continue;
-            const float sv = rs[e];
-            const uint32_t uu = ord_key(sv);
-            const bool eq = !all && uu == mtau;
-            const bool keep = all || uu > mtau || (eq && run < mties);
-            run += eq ? 1u : 0u;
-            if (keep && pos < m) {
-                io[pos] = ri[e];
-                if (vo) vo[pos] = sv;
+            m_out = Fs < (uint32_t)topk ? Fs : (uint32_t)topk;
+        } else {
+            // The bound left too many survivors (many equal scores): the same
+            // selection over every full-list slot, read from the workspace.
+            const int E = P * slots;
+            auto each = [&](auto f) {
+                for (int e = tid; e < E; e += THREADS) {
+                    const uint32_t key = (uint32_t)load_agent(&rf[e]);
+                    if (key != 0u) f(key);
+                }
+            };
+            uint32_t n = 0;
+            each([&](uint32_t) { ++n; });
+            uint32_t N;
+            block_excl_scan(n, sm, N);
+            __syncthreads();
+            uint32_t tau = 0, ties = 0;
+            if (N > (uint32_t)topk) block_kth(each, (uint32_t)topk, sm, tau, ties);
+            const int ch = (E + THREADS - 1) / THREADS;
+            const int e0 = tid * ch, e1 = e0 + ch < E ? e0 + ch : E;
+            uint32_t ngt = 0, neq = 0;
+            for (int e = e0; e < e1; ++e) {
+                const uint32_t key = (uint32_t)load_agent(&rf[e]);
+                ngt += key > tau ? 1u : 0u;
+                neq += (key != 0u && key == tau) ? 1u : 0u;
             }
-            pos += keep ? 1u : 0u;
+            uint32_t tot;
+            const uint32_t gtb = block_excl_scan(ngt, sm, tot);
+            __syncthreads();
+            uint32_t eqb = block_excl_scan(neq, sm, tot);
+            uint32_t pos = gtb + (eqb < ties ? eqb : ties);
+            for (int e = e0; e < e1; ++e) {
+                const uint64_t sv = load_agent(&rf[e]);
+                const uint32_t key = (uint32_t)sv;
+                bool keep = key > tau;
+                if (key != 0u && key == tau) keep = eqb++ < ties;
+                if (keep && pos < (uint32_t)topk) {
+                    io[pos] = (int)(sv >> 32);
+                    if (vo) vo[pos] = key_float(key);
+                    ++pos;
+                }
+            }
+            m_out = N < (uint32_t)topk ? N : (uint32_t)topk;
         }
     }
     for (int j = (int)m_out + tid; j < topk; j += THREADS) {
@@ -668,7 +873,8 @@ hipError_t launch_t(const Problem &p, const void *Q, const void *K, const float 
     SplitWorkspace w = split_workspace(ws, p, k);
     hipLaunchKernelGGL((split_indexer_kernel<KFP8>), dim3(P, rows), dim3(THREADS), 0, st,
                        static_cast<const uint16_t *>(Q), static_cast<const uint8_t *>(K), Ks, W,
-                       p.T, p.S, p.offset, k, P, w.ctr, w.cand_n, w.cand_t, w.cand_s, w.cand_i, idx, vals);
+                       p.T, p.S, p.offset, k, P, split_slots(k), split_short_slots(p, k), w.ctr, w.meta,
+                       w.full_list, w.short_list, idx, vals);
     return hipGetLastError();
 }
 
@@ -680,12 +886,27 @@ int split_parts(const Problem &p)
     return (int)((maxL + PART - 1) / PART);
 }
 
+int split_slots(int k) { return (2 * k + 63) / 64 * 64; }
+
+int split_short_slots(const Problem &p, int k)
+{
+    // Room for the keys from the bin of the c1-th largest up, c1 = 4m (m =
+    // ceil(k / full partitions) of the row with the fewest): the kernel takes
+    // c1 = slots / 4, so the bin may hold up to 3 c1 further keys.
+    const long long fullp = (p.offset + 1) / PART;
+    if (fullp < 1) return 64;
+    const long long m = (k + fullp - 1) / fullp;
+    const long long s = (16 * m + 63) / 64 * 64;
+    return (int)(s < split_slots(k) ? s : split_slots(k));
+}
+
 static size_t align256(size_t n) { return (n + 255) / 256 * 256; }
 
 size_t split_workspace_bytes(const Problem &p, int k)
 {
     const size_t rows = (size_t)p.B * p.T, P = (size_t)split_parts(p);
-    return align256(rows * 4) + 2 * align256(rows * P * 4) + 2 * align256(rows * P * (size_t)k * 4);
+    return align256(rows * 4) + align256(rows * P * 16) + align256(rows * P * (size_t)split_slots(k) * 8) +
+           align256(rows * P * (size_t)split_short_slots(p, k) * 8);
 }
 
 SplitWorkspace split_workspace(void *ws, const Problem &p, int k)
@@ -695,13 +916,11 @@ SplitWorkspace split_workspace(void *ws, const Problem &p, int k)
     SplitWorkspace w;
     w.ctr = reinterpret_cast<uint32_t *>(c);
     c += align256(rows * 4);
-    w.cand_n = reinterpret_cast<uint32_t *>(c);
-    c += align256(rows * P * 4);
-    w.cand_t = reinterpret_cast<uint32_t *>(c);
-    c += align256(rows * P * 4);
-    w.cand_s = reinterpret_cast<float *>(c);
-    c += align256(rows * P * (size_t)k * 4);
-    w.cand_i = reinterpret_cast<int *>(c);
+    w.meta = reinterpret_cast<uint64_t *>(c);
+    c += align256(rows * P * 16);
+    w.full_list = reinterpret_cast<uint64_t *>(c);
+    c += align256(rows * P * (size_t)split_slots(k) * 8);
+    w.short_list = reinterpret_cast<uint64_t *>(c);
     return w;
 }
 

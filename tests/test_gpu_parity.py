@@ -283,3 +283,39 @@ def test_split_int_exact():
     wl = W.prefill_bf16_int(seed=77, T=2, S=50000, offset=49998, topk=512, B=3)
     gi, gv = run_select(wl, poison=True)
     compare_rows(wl, np.arange(6), gi, gv, exact=True)
+
+
+@pytest.mark.parametrize("S", [100000, 300000])
+def test_split_all_equal_scores(S):
+    # K = 0 on a long cache with few rows (the split-key kernel): every score
+    # is 0, so each partition's k-th key shares its bin with all 8192 keys
+    # (exact partition selection), no short list fits, and at 300k keys the
+    # merge holds more candidates than it stages (selection from the lists).
+    B, T = 2, 2
+    wl = W.prefill_fp8(seed=21, T=T, S=S, offset=S - T, topk=512, B=B, chunk=T)
+    wl.chunks = [(0, T, S, S - T)]
+    wl.k[:] = 0
+    _say(f"split all-equal B={B} T={T} S={S}")
+    gi, gv = run_select(wl, poison=True)
+    assert np.array_equal(gi, np.tile(np.arange(512, dtype=gi.dtype), (B * T, 1)))
+    assert np.all(gv == 0)
+
+
+def test_split_hot_partition():
+    # Partition 0 holds every one of the top k scores: its short list lies
+    # above the row bound, so the merge must read the full candidate lists.
+    # Scores are 32 * scale exactly (q = e_0, every key 1.0, w = 0.5) and
+    # distinct, so the answer is the last k keys of partition 0.
+    S = 40000
+    q = np.zeros((1, 1, 64, 128), np.float32)
+    q[..., 0] = 1.0
+    k = np.full((1, S, 128), 0x38, np.uint8)
+    s = np.arange(S)
+    scale = np.where(s < 8192, 2.0 + s * 2.0 ** -20, 1.0 + s * 2.0 ** -20).astype(np.float32).reshape(1, S)
+    w = np.full((1, 1, 64), 0.5, np.float32)
+    wl = W.Workload("hot", W.to_bf16_bits(q), k, scale, w, 1, 1, S, 64, 128, S - 1, 512, W.BF16,
+                    W.FP8, [(0, 1, S, S - 1)])
+    _say("split hot partition S=40000")
+    gi, gv = run_select(wl, poison=True)
+    assert list(gi[0]) == list(range(8192 - 512, 8192))
+    assert np.array_equal(gv[0], (32.0 * scale[0, 8192 - 512:8192]).astype(np.float32))
