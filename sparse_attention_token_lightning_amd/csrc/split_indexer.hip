@@ -50,20 +50,36 @@ constexpr int NLIST = 64;                // keys of one bin that a single wavefr
 constexpr int MSURV = 8192;              // merge survivors held in LDS
 constexpr int MREG = MSURV / THREADS;    // survivors per thread
 constexpr int GB = 16;                   // 64-slot groups per wavefront per merge batch
+constexpr int MAX_SLOTS = 4096;          // full-list slots for k = 2048, the largest k
+constexpr int HWORDS = HBINS + HBINS / 8;  // one pad word after every 8 bins
 static_assert(HBINS == 8 * THREADS, "each thread owns eight histogram bins");
+static_assert(PART == 1 << 13, "partition size is used as a shift");
+
+// LDS word of histogram bin b. The scan gives each thread 8 consecutive bins;
+// padding puts consecutive threads 9 words apart, so their reads fall in
+// different banks (an 8-word stride costs several times the whole scan).
+__device__ __forceinline__ int hidx(uint32_t b) { return (int)(b + (b >> 3)); }
+
+// LDS word of the partition's key i: one pad word per 16 keys, so thread t
+// reads its 16 consecutive keys at 17t .. 17t+15 without bank conflicts.
+__device__ __forceinline__ int scx(int i) { return i + (i >> 4); }
 
 typedef __attribute__((__vector_size__(8 * sizeof(short)))) short bf16x8;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 
 struct SplitSmem {
     union {
-        uint32_t sc[NW][WAVE_KEYS];  // partition score keys, 0 = no key
+        uint32_t sc[PART + PART / 16];  // partition score keys (0 = no key) at scx(i)
         struct {
             uint32_t key[MSURV];     // merge survivors, index order
             int idx[MSURV];
         } sv;
+        struct {
+            uint64_t full[MAX_SLOTS];    // partition lists, compacted before
+            uint64_t shortl[MAX_SLOTS];  // coalesced stores
+        } st;
     };
-    uint32_t hist[HBINS];
+    uint32_t hist[HWORDS];
     uint32_t lk[NLIST];              // keys of one bin, for exact ranking
     uint32_t gcnt[NW * GB];          // merge: survivors per 64-slot group
     uint32_t goff[NW * GB];          // merge: output offset per group
@@ -73,6 +89,7 @@ struct SplitSmem {
     uint32_t red[2][NW];
     uint32_t pick[12];
     uint32_t nl;
+    uint32_t pn[kSplitMaxParts];      // merge: full-list length per partition
     int last;
 };
 
@@ -102,6 +119,23 @@ __device__ __forceinline__ uint32_t cvt2(uint32_t w)
     return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, HI));
 }
 
+// After a barrier that published each wavefront's total in arr[0..NW): the
+// sum over wavefronts below the calling one, and (`all`) over all of them.
+// Lanes 0..7 scan the eight totals with row shifts; two reads pick the
+// results, so no per-wavefront comparison masks stay live in SGPRs.
+__device__ __forceinline__ uint32_t waves_before(const uint32_t *arr, uint32_t &all)
+{
+    const int lane = threadIdx.x & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t v = lane < NW ? arr[lane] : 0u;
+    uint32_t x = v;
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, false);
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, false);
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, false);
+    all = (uint32_t)__builtin_amdgcn_readlane((int)x, NW - 1);
+    return (uint32_t)__builtin_amdgcn_readlane((int)(x - v), wid);
+}
+
 // Block-wide exclusive prefix sum of v; `total` receives the block sum. One
 // barrier: sm.wsum must not be written again before the next barrier.
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, SplitSmem &sm, uint32_t &total)
@@ -110,15 +144,28 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, SplitSmem &sm, u
     const uint32_t x = wave_scan_incl(v, 0u, OpAdd{});
     if (lane == 63) sm.wsum[wid] = x;
     __syncthreads();
-    uint32_t before = 0, tot = 0;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-        const uint32_t c = sm.wsum[w];
-        before += (w < wid) ? c : 0u;
-        tot += c;
-    }
-    total = tot;
+    const uint32_t before = waves_before(sm.wsum, total);
     return before + x - v;
+}
+
+// Two block-wide exclusive prefix sums at once (one barrier, same rule for
+// sm.wsum and sm.wmax as block_excl_scan): returns a's, b's prefix via bex.
+__device__ __forceinline__ uint32_t block_excl_scan2(uint32_t a, uint32_t b, SplitSmem &sm, uint32_t &ta,
+                                                     uint32_t &bex)
+{
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const uint32_t xa = wave_scan_incl(a, 0u, OpAdd{});
+    const uint32_t xb = wave_scan_incl(b, 0u, OpAdd{});
+    if (lane == 63) {
+        sm.wsum[wid] = xa;
+        sm.wmax[wid] = xb;
+    }
+    __syncthreads();
+    uint32_t tb;
+    const uint32_t pa = waves_before(sm.wsum, ta);
+    const uint32_t pb = waves_before(sm.wmax, tb);
+    bex = pb + xb - b;
+    return pa + xa - a;
 }
 
 // Block-wide AND and OR. One barrier.
@@ -159,9 +206,10 @@ __device__ __forceinline__ uint32_t hist_find(SplitSmem &sm, const uint32_t (&tg
 {
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int top = HBINS - 1 - 8 * tid;
-    const uint4 h = *reinterpret_cast<const uint4 *>(&sm.hist[top - 3]);
-    const uint4 l = *reinterpret_cast<const uint4 *>(&sm.hist[top - 7]);
-    const uint32_t c[8] = {h.w, h.z, h.y, h.x, l.w, l.z, l.y, l.x};
+    const uint32_t *hb = &sm.hist[hidx((uint32_t)(top - 7))];
+    uint32_t c[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) c[j] = hb[7 - j];  // descending bins
     uint32_t s = 0;
 #pragma unroll
     for (int j = 0; j < 8; ++j) s += c[j];
@@ -172,25 +220,33 @@ __device__ __forceinline__ uint32_t hist_find(SplitSmem &sm, const uint32_t (&tg
         if (MAX) sm.wmax[wid] = mx;
     }
     __syncthreads();
-    uint32_t run = x - s, total = 0;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-        run += (w < wid) ? sm.wsum[w] : 0u;
-        total += sm.wsum[w];
-        if (MAX) mx = sm.wmax[w] > mx ? sm.wmax[w] : mx;
+    uint32_t total;
+    uint32_t run = x - s + waves_before(sm.wsum, total);
+    if (MAX) {
+        const uint32_t m = lane < NW ? sm.wmax[lane] : 0u;
+        *bmax = wave_max(m);
     }
-    if (MAX) *bmax = mx;
+    uint32_t incl[8];
+    incl[0] = run + c[0];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 1; j < 8; ++j) incl[j] = incl[j - 1] + c[j];
 #pragma unroll
-        for (int q = 0; q < NT; ++q) {
-            if (tgt[q] <= total && run < tgt[q] && tgt[q] <= run + c[j]) {
-                sm.pick[3 * q] = (uint32_t)(top - j);
-                sm.pick[3 * q + 1] = run;
-                sm.pick[3 * q + 2] = c[j];
+    for (int q = 0; q < NT; ++q) {
+        const uint32_t t = tgt[q];
+        if (t <= total && run < t && t <= incl[7]) {  // one thread per target
+            uint32_t j = 0, above = run, cnt = 0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const bool before = incl[i] < t;
+                j += before ? 1u : 0u;
+                above += before ? c[i] : 0u;
             }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) cnt = (uint32_t)i == j ? c[i] : cnt;
+            sm.pick[3 * q] = (uint32_t)top - j;
+            sm.pick[3 * q + 1] = above;
+            sm.pick[3 * q + 2] = cnt;
         }
-        run += c[j];
     }
     __syncthreads();
 #pragma unroll
@@ -244,7 +300,7 @@ __device__ __forceinline__ void block_kth(Each each, uint32_t k, SplitSmem &sm, 
     const int tid = threadIdx.x, wid = tid >> 6;
     uint32_t prefix = 0, pmask = 0, remaining = k;
     for (;;) {
-        for (int b = tid; b < HBINS; b += THREADS) sm.hist[b] = 0;
+        for (int b = tid; b < HWORDS; b += THREADS) sm.hist[b] = 0;
         if (tid == 0) sm.nl = 0;
         uint32_t a = ~0u, o = 0u;
         each([&](uint32_t u) {
@@ -267,7 +323,7 @@ __device__ __forceinline__ void block_kth(Each each, uint32_t k, SplitSmem &sm, 
         const int lo = hb >= HBITS - 1 ? hb - (HBITS - 1) : 0;
         const uint32_t dmask = (2u << (hb - lo)) - 1u;
         each([&](uint32_t u) {
-            if ((u & pmask) == prefix) atomicAdd(&sm.hist[(u >> lo) & dmask], 1u);
+            if ((u & pmask) == prefix) atomicAdd(&sm.hist[hidx((u >> lo) & dmask)], 1u);
         });
         __syncthreads();
         Found fd[1];
@@ -383,7 +439,7 @@ __global__ __launch_bounds__(THREADS, 1) void split_indexer_kernel(
     const long long pbase = (long long)p * PART;
     const long long nvalid = L - pbase < 0 ? 0 : (L - pbase > PART ? PART : L - pbase);
 
-    for (int i = tid; i < HBINS; i += THREADS) sm.hist[i] = 0;
+    for (int i = tid; i < HWORDS; i += THREADS) sm.hist[i] = 0;
     if (tid == 0) sm.nl = 0;
     __syncthreads();
 
@@ -439,8 +495,8 @@ __global__ __launch_bounds__(THREADS, 1) void split_indexer_kernel(
                         if (KFP8) sc *= pscale;
                         const long long key = wbase + 32 * (sb - 1) + lane;
                         const uint32_t ok = ord_key(canon(sc));
-                        sm.sc[wid][32 * (sb - 1) + lane] = key < L ? ok : 0u;
-                        if (key < L && ok != 0u) atomicAdd(&sm.hist[ok >> HSHIFT], 1u);
+                        sm.sc[scx(wid * WAVE_KEYS + 32 * (sb - 1) + lane)] = key < L ? ok : 0u;
+                        if (key < L && ok != 0u) atomicAdd(&sm.hist[hidx(ok >> HSHIFT)], 1u);
                     } else {
                         prev = part;
                     }
@@ -448,22 +504,25 @@ __global__ __launch_bounds__(THREADS, 1) void split_indexer_kernel(
             }
         }
     }
-    for (int i = (int)(((wkeys + 63) / 64) * 64) + lane; i < WAVE_KEYS; i += 64) sm.sc[wid][i] = 0u;
+    for (int i = (int)(((wkeys + 63) / 64) * 64) + lane; i < WAVE_KEYS; i += 64) sm.sc[scx(wid * WAVE_KEYS + i)] = 0u;
     __syncthreads();
-    uint32_t u[ROUNDS];
+    // From here on thread t holds the keys of indices pbase + 16t .. +15.
+    constexpr int KPT = PART / THREADS;  // 16
+    uint32_t u[KPT];
 #pragma unroll
-    for (int j = 0; j < ROUNDS; ++j) u[j] = sm.sc[wid][j * 64 + lane];
+    for (int j = 0; j < KPT; ++j) u[j] = sm.sc[KPT * tid + tid + j];
+    const long long ibase = pbase + (long long)KPT * tid;
 
     // ---- bins of the partition's k-th, m-th and c1-th largest keys. The
     // full partitions of the row (PART keys each) alone hold fullp*m >= k
     // keys. Only nonzero keys are counted: the all-ones NaN pattern maps to
     // key 0, which reads as "no key" everywhere.
-    const long long fullp = L / PART;
-    const uint32_t mth = fullp > 0 ? (uint32_t)((topk + fullp - 1) / fullp) : 0u;  // 0: no bound
+    const uint32_t fullp = (uint32_t)(L >> 13);  // L / PART
+    const uint32_t mth = fullp > 0 ? ((uint32_t)topk + fullp - 1) / fullp : 0u;  // 0: no bound
     const uint32_t c1 = (uint32_t)(s1 / 4);
     uint32_t mykmax = 0, kmax;
 #pragma unroll
-    for (int j = 0; j < ROUNDS; ++j) mykmax = u[j] > mykmax ? u[j] : mykmax;
+    for (int j = 0; j < KPT; ++j) mykmax = u[j] > mykmax ? u[j] : mykmax;
     Found fd[3];
     const uint32_t nkeys = hist_find<3, true>(sm, {(uint32_t)topk, mth, c1}, fd, mykmax, &kmax);
     const Found fk = fd[0], fm = fd[1], f1 = fd[2];
@@ -482,9 +541,10 @@ __global__ __launch_bounds__(THREADS, 1) void split_indexer_kernel(
     const long long cb = (r * P + p) * (long long)slots;
     const long long cb1 = (r * P + p) * (long long)s1;
     // This partition's m-th largest key (~0: no bound from it), published by
-    // wavefront 0 with the short list's edge and the largest key once the
-    // keys of the m-th key's bin are in sm.lk: exact when that bin is small,
-    // else its lower edge (still m keys at or above it).
+    // wavefront 0 with the short list's edge, the largest key and the full
+    // list's length once the keys of the m-th key's bin are in sm.lk: exact
+    // when that bin is small, else its lower edge (still m keys at or above).
+    const uint32_t nfull = F <= (uint32_t)slots ? F : (uint32_t)topk;
     auto publish_meta = [&]() {
         if (wid != 0) return;
         uint32_t tp = ~0u;
@@ -496,105 +556,81 @@ __global__ __launch_bounds__(THREADS, 1) void split_indexer_kernel(
         }
         if (lane == 0) {
             store_agent(&meta[2 * (r * P + p)], ((uint64_t)(short_ok ? edge1 : ~0u) << 32) | tp);
-            store_agent(&meta[2 * (r * P + p) + 1], (uint64_t)kmax);
+            store_agent(&meta[2 * (r * P + p) + 1], ((uint64_t)nfull << 32) | kmax);
         }
     };
-    auto gidx = [&](int j) { return pbase + (long long)wid * WAVE_KEYS + j * 64 + lane; };
-    // Per-wavefront counts of the short list, then its ordered write.
-    uint32_t w1 = 0;
-    if (short_ok) {
+    const bool direct = F <= (uint32_t)slots;
+    // Each thread counts its candidates for both lists and the m-th key's
+    // bin; one scan places them, and the lists are compacted in index order
+    // in LDS, then written with coalesced stores: the full list when it fits
+    // (else below, after an exact selection), the short list with its unused
+    // slots empty.
+    uint32_t cf = 0, cs = 0, cm = 0;
 #pragma unroll
-        for (int j = 0; j < ROUNDS; ++j) w1 += (uint32_t)__builtin_popcountll(wave_ballot(u[j] >= edge1));
+    for (int j = 0; j < KPT; ++j) {
+        cf += u[j] >= edge ? 1u : 0u;
+        cs += u[j] >= edge1 ? 1u : 0u;
+        cm += (u[j] != 0u && (u[j] >> HSHIFT) == fm.bin) ? 1u : 0u;
     }
-    auto write_short = [&]() {
-        if (!short_ok) return;
-        uint32_t out = 0;
+    uint32_t tf, tm;
+    const uint32_t exfs = block_excl_scan2(cf | (cs << 16), refine ? cm : 0u, sm, tf, tm);  // counts < 2^14
+    // The counts are exact, so positions stay below F <= slots, n1 <= s1
+    // and fm.cnt <= NLIST.
+    const uint32_t ib = (uint32_t)ibase;
+    if (direct) {
+        uint32_t pf = exfs & 0xffffu;
 #pragma unroll
-        for (int w = 0; w < NW; ++w) out += (w < wid) ? sm.wcnt[2][w] : 0u;
+        for (int j = 0; j < KPT; ++j)
+            if (u[j] >= edge) sm.st.full[pf++] = ((uint64_t)(ib + j) << 32) | u[j];
+    }
+    if (short_ok) {
+        uint32_t ps = exfs >> 16;
 #pragma unroll
-        for (int j = 0; j < ROUNDS; ++j) {
-            const bool keep = u[j] >= edge1;
-            const uint64_t mk = wave_ballot(keep);
-            const uint32_t pos = out + lanes_below(mk);
-            if (keep && pos < (uint32_t)s1) store_agent(&short_list[cb1 + pos], slot(u[j], gidx(j)));
-            out += (uint32_t)__builtin_popcountll(mk);
-        }
-        for (int i = (int)n1 + tid; i < s1; i += THREADS) store_agent(&short_list[cb1 + i], (uint64_t)0);
-    };
-    if (F <= (uint32_t)slots) {
-        uint32_t wc = 0;
+        for (int j = 0; j < KPT; ++j)
+            if (u[j] >= edge1) sm.st.shortl[ps++] = ((uint64_t)(ib + j) << 32) | u[j];
+    }
+    if (refine) {
+        uint32_t pm = tm;
 #pragma unroll
-        for (int j = 0; j < ROUNDS; ++j) {
-            wc += (uint32_t)__builtin_popcountll(wave_ballot(u[j] >= edge));
-            if (refine) list_append(sm, u[j] != 0u && (u[j] >> HSHIFT) == fm.bin, u[j]);
-        }
-        if (lane == 0) {
-            sm.wcnt[0][wid] = wc;
-            sm.wcnt[2][wid] = w1;
-        }
-        __syncthreads();
-        uint32_t out = 0;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) out += (w < wid) ? sm.wcnt[0][w] : 0u;
-#pragma unroll
-        for (int j = 0; j < ROUNDS; ++j) {
-            const bool keep = u[j] >= edge;
-            const uint64_t mk = wave_ballot(keep);
-            const uint32_t pos = out + lanes_below(mk);
-            if (keep && pos < (uint32_t)slots) store_agent(&full_list[cb + pos], slot(u[j], gidx(j)));
-            out += (uint32_t)__builtin_popcountll(mk);
-        }
-        for (int i = (int)F + tid; i < slots; i += THREADS) store_agent(&full_list[cb + i], (uint64_t)0);
-        write_short();
-        publish_meta();
-    } else {
+        for (int j = 0; j < KPT; ++j)
+            if (u[j] != 0u && (u[j] >> HSHIFT) == fm.bin) sm.lk[pm++] = u[j];
+    }
+    __syncthreads();
+    if (direct)
+        for (int i = tid; i < (int)F; i += THREADS) store_agent(&full_list[cb + i], sm.st.full[i]);
+    if (short_ok)
+        for (int i = tid; i < s1; i += THREADS)
+            store_agent(&short_list[cb1 + i], i < (int)n1 ? sm.st.shortl[i] : (uint64_t)0);
+    publish_meta();  // before block_kth reuses sm.lk (its first barrier orders the two)
+    if (!direct) {
         // Too many keys share the k-th key's bin: exact selection of k.
-        if (refine) {
-#pragma unroll
-            for (int j = 0; j < ROUNDS; ++j) list_append(sm, u[j] != 0u && (u[j] >> HSHIFT) == fm.bin, u[j]);
-        }
-        if (lane == 0) sm.wcnt[2][wid] = w1;
-        __syncthreads();
-        write_short();
-        publish_meta();  // before block_kth reuses sm.lk (its first barrier orders the two)
         uint32_t tau, ties;
         block_kth(
             [&](auto f) {
 #pragma unroll
-                for (int j = 0; j < ROUNDS; ++j)
+                for (int j = 0; j < KPT; ++j)
                     if (u[j] != 0u) f(u[j]);
             },
             (uint32_t)topk, sm, tau, ties);
         uint32_t ngt = 0, neq = 0;
 #pragma unroll
-        for (int j = 0; j < ROUNDS; ++j) {
-            ngt += (uint32_t)__builtin_popcountll(wave_ballot(u[j] > tau));
-            neq += (uint32_t)__builtin_popcountll(wave_ballot(u[j] != 0u && u[j] == tau));
+        for (int j = 0; j < KPT; ++j) {
+            ngt += u[j] > tau ? 1u : 0u;
+            neq += (u[j] != 0u && u[j] == tau) ? 1u : 0u;
         }
-        if (lane == 0) {
-            sm.wcnt[0][wid] = ngt;
-            sm.wcnt[1][wid] = neq;
-        }
-        __syncthreads();
-        uint32_t gtb = 0, eqb = 0;
+        uint32_t tot;
+        const uint32_t ex = block_excl_scan(ngt | (neq << 16), sm, tot);  // counts < 2^14
+        uint32_t eqb = ex >> 16;
+        uint32_t o = (ex & 0xffffu) + (eqb < ties ? eqb : ties);
 #pragma unroll
-        for (int w = 0; w < NW; ++w) {
-            gtb += (w < wid) ? sm.wcnt[0][w] : 0u;
-            eqb += (w < wid) ? sm.wcnt[1][w] : 0u;
+        for (int j = 0; j < KPT; ++j) {
+            bool keep = u[j] > tau;
+            if (u[j] != 0u && u[j] == tau) keep = eqb++ < ties;
+            if (keep) {
+                if (o < (uint32_t)slots) store_agent(&full_list[cb + o], slot(u[j], ibase + j));
+                ++o;
+            }
         }
-        uint32_t out = gtb + (eqb < ties ? eqb : ties);
-#pragma unroll
-        for (int j = 0; j < ROUNDS; ++j) {
-            const bool eq = u[j] != 0u && u[j] == tau;
-            const uint64_t meq = wave_ballot(eq);
-            const bool keep = u[j] > tau || (eq && eqb + lanes_below(meq) < ties);
-            const uint64_t mk = wave_ballot(keep);
-            const uint32_t pos = out + lanes_below(mk);
-            if (keep && pos < (uint32_t)slots) store_agent(&full_list[cb + pos], slot(u[j], gidx(j)));
-            out += (uint32_t)__builtin_popcountll(mk);
-            eqb += (uint32_t)__builtin_popcountll(meq);
-        }
-        for (int i = topk + tid; i < slots; i += THREADS) store_agent(&full_list[cb + i], (uint64_t)0);
     }
 
     // ---- arrival: the last workgroup of the row merges. The candidate lists
@@ -602,7 +638,7 @@ __global__ __launch_bounds__(THREADS, 1) void split_indexer_kernel(
     // bypass the per-XCD L2's non-coherent lines; waiting for every store to
     // complete before the counter increment orders them, with no cache-wide
     // writeback or invalidate.
-    for (int i = tid; i < HBINS; i += THREADS) sm.hist[i] = 0;  // for the merge
+    for (int i = tid; i < HWORDS; i += THREADS) sm.hist[i] = 0;  // for the merge
     if (tid == 0) sm.nl = 0;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -660,11 +696,29 @@ __global__ __launch_bounds__(THREADS, 1) void split_indexer_kernel(
             v[i] = g < G ? load_agent(&grid[(long long)g * 64 + lane]) : (uint64_t)0;
         }
     };
-    auto collect = [&](const uint64_t *grid, int G, uint32_t bound) {
-        for (int g0 = 0; g0 < G; g0 += NW * GB) {
+    // The full lists: slot j of partition q holds a key only for j < sm.pn[q].
+    const int gpp = slots / 64;
+    auto load_full_batch = [&](uint64_t (&v)[GB], int g0) {
+#pragma unroll
+        for (int i = 0; i < GB; ++i) {
+            const int g = g0 + wid + NW * i;
+            const bool in = g < GF && (g % gpp) * 64 + lane < (int)sm.pn[g < GF ? g / gpp : 0];
+            v[i] = in ? load_agent(&rf[(long long)g * 64 + lane]) : (uint64_t)0;
+        }
+    };
+    auto collect_short = [&](uint32_t bnd) {
+        for (int g0 = 0; g0 < G1; g0 += NW * GB) {
             uint64_t v[GB];
-            load_batch(v, grid, G, g0);
-            if (!collect_batch(v, bound)) return false;
+            load_batch(v, rs, G1, g0);
+            if (!collect_batch(v, bnd)) return false;
+        }
+        return true;
+    };
+    auto collect_full = [&](uint32_t bnd) {
+        for (int g0 = 0; g0 < GF; g0 += NW * GB) {
+            uint64_t v[GB];
+            load_full_batch(v, g0);
+            if (!collect_batch(v, bnd)) return false;
         }
         return true;
     };
@@ -677,11 +731,12 @@ __global__ __launch_bounds__(THREADS, 1) void split_indexer_kernel(
     uint32_t tq = ~0u, eq1 = 0u, mq = 0u;
     for (int q = lane; q < P; q += 64) {
         const uint64_t a = load_agent(&meta[2 * (r * P + q)]);
-        const uint32_t b = (uint32_t)load_agent(&meta[2 * (r * P + q) + 1]);
-        const uint32_t t = (uint32_t)a, e1 = (uint32_t)(a >> 32);
+        const uint64_t b = load_agent(&meta[2 * (r * P + q) + 1]);
+        const uint32_t t = (uint32_t)a, e1 = (uint32_t)(a >> 32), km = (uint32_t)b;
         tq = t < tq ? t : tq;
         eq1 = e1 > eq1 ? e1 : eq1;
-        mq = b > mq ? b : mq;
+        mq = km > mq ? km : mq;
+        if (wid == 0) sm.pn[q] = (uint32_t)(b >> 32);  // full-list lengths, for the other paths
     }
     uint32_t bound = wave_min(tq);
     if (bound == ~0u) bound = 0u;
@@ -703,7 +758,7 @@ __global__ __launch_bounds__(THREADS, 1) void split_indexer_kernel(
         const uint32_t prefix = hb == 31 ? 0u : (bound & (~0u << (hb + 1)));
 #pragma unroll
         for (int i = 0; i < GB; ++i)
-            if (kk[i] != 0u) atomicAdd(&sm.hist[(kk[i] >> lo) & dmask], 1u);
+            if (kk[i] != 0u) atomicAdd(&sm.hist[hidx((kk[i] >> lo) & dmask)], 1u);
         __syncthreads();
         Found fd[1];
         const uint32_t total = hist_find<1>(sm, {(uint32_t)topk}, fd);
@@ -770,7 +825,8 @@ __global__ __launch_bounds__(THREADS, 1) void split_indexer_kernel(
         }
         m_out = total < (uint32_t)topk ? total : (uint32_t)topk;
     } else {
-        const bool ok = use_short ? collect(rs, G1, bound) : collect(rf, GF, bound);
+        __syncthreads();  // sm.pn
+        const bool ok = use_short ? collect_short(bound) : collect_full(bound);
         __syncthreads();
         if (ok) {
             // Thread t owns the contiguous run [t*ch, t*ch + ch) of survivors.
@@ -817,9 +873,10 @@ __global__ __launch_bounds__(THREADS, 1) void split_indexer_kernel(
             // The bound left too many survivors (many equal scores): the same
             // selection over every full-list slot, read from the workspace.
             const int E = P * slots;
+            auto valid = [&](int e) { return (uint32_t)(e % slots) < sm.pn[e / slots]; };
             auto each = [&](auto f) {
                 for (int e = tid; e < E; e += THREADS) {
-                    const uint32_t key = (uint32_t)load_agent(&rf[e]);
+                    const uint32_t key = valid(e) ? (uint32_t)load_agent(&rf[e]) : 0u;
                     if (key != 0u) f(key);
                 }
             };
@@ -834,7 +891,7 @@ __global__ __launch_bounds__(THREADS, 1) void split_indexer_kernel(
             const int e0 = tid * ch, e1 = e0 + ch < E ? e0 + ch : E;
             uint32_t ngt = 0, neq = 0;
             for (int e = e0; e < e1; ++e) {
-                const uint32_t key = (uint32_t)load_agent(&rf[e]);
+                const uint32_t key = valid(e) ? (uint32_t)load_agent(&rf[e]) : 0u;
                 ngt += key > tau ? 1u : 0u;
                 neq += (key != 0u && key == tau) ? 1u : 0u;
             }
@@ -844,7 +901,7 @@ __global__ __launch_bounds__(THREADS, 1) void split_indexer_kernel(
             uint32_t eqb = block_excl_scan(neq, sm, tot);
             uint32_t pos = gtb + (eqb < ties ? eqb : ties);
             for (int e = e0; e < e1; ++e) {
-                const uint64_t sv = load_agent(&rf[e]);
+                const uint64_t sv = valid(e) ? load_agent(&rf[e]) : (uint64_t)0;
                 const uint32_t key = (uint32_t)sv;
                 bool keep = key > tau;
                 if (key != 0u && key == tau) keep = eqb++ < ties;
