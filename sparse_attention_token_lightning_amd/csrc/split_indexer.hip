@@ -54,6 +54,7 @@ constexpr int MAX_SLOTS = 4096;          // full-list slots for k = 2048, the la
 constexpr int HWORDS = HBINS + HBINS / 8;  // one pad word after every 8 bins
 static_assert(HBINS == 8 * THREADS, "each thread owns eight histogram bins");
 static_assert(PART == 1 << 13, "partition size is used as a shift");
+static_assert(HWORDS >= 2 * 2048, "the histogram words stage k <= 2048 output pairs");
 
 // LDS word of histogram bin b. The scan gives each thread 8 consecutive bins;
 // padding puts consecutive threads 9 words apart, so their reads fall in
@@ -71,7 +72,7 @@ struct SplitSmem {
     union {
         uint32_t sc[PART + PART / 16];  // partition score keys (0 = no key) at scx(i)
         struct {
-            uint32_t key[MSURV];     // merge survivors, index order
+            uint32_t key[MSURV + MSURV / 16];  // merge survivors, index order (direct path: at scx)
             int idx[MSURV];
         } sv;
         struct {
@@ -79,7 +80,7 @@ struct SplitSmem {
             uint64_t shortl[MAX_SLOTS];  // coalesced stores
         } st;
     };
-    uint32_t hist[HWORDS];
+    alignas(8) uint32_t hist[HWORDS];  // also the merge's output staging (k pairs)
     uint32_t lk[NLIST];              // keys of one bin, for exact ranking
     uint32_t gcnt[NW * GB];          // merge: survivors per 64-slot group
     uint32_t goff[NW * GB];          // merge: output offset per group
@@ -745,20 +746,33 @@ __global__ __launch_bounds__(THREADS, 1) void split_indexer_kernel(
 
     uint32_t m_out;
     if (use_short && G1 <= NW * GB) {
-        // Select straight from the loaded short lists. Every key in play lies
-        // in [bound, row maximum], so they share the bits above the highest
-        // bit in which those two differ: the 12 bits below it are the first
-        // digit, with no reduction pass.
-        uint32_t kk[GB];
+        // Select straight from the loaded short lists, transposed through
+        // LDS so that thread t owns slots 16t .. 16t+15 (index order). Every
+        // key in play lies in [bound, row maximum], so they share the bits
+        // above the highest bit in which those two differ: the 12 bits below
+        // it are the first digit, with no reduction pass.
+        const int nslot = G1 * 64;
 #pragma unroll
-        for (int i = 0; i < GB; ++i) kk[i] = (uint32_t)v0[i] >= bound ? (uint32_t)v0[i] : 0u;
+        for (int i = 0; i < GB; ++i) {
+            const int g = wid + NW * i;
+            if (g < G1) {
+                const uint32_t key = (uint32_t)v0[i];
+                sm.sv.key[scx(g * 64 + lane)] = key >= bound ? key : 0u;
+                sm.sv.idx[g * 64 + lane] = (int)(v0[i] >> 32);
+            }
+        }
+        __syncthreads();
+        constexpr int KPT = PART / THREADS;  // 16 slots per thread
+        uint32_t kk[KPT];
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) kk[j] = KPT * tid + j < nslot ? sm.sv.key[KPT * tid + tid + j] : 0u;
         const int hb = 31 - __builtin_clz((bound ^ kmax_row) | 1u);
         const int lo = hb >= HBITS - 1 ? hb - (HBITS - 1) : 0;
         const uint32_t dmask = (2u << (hb - lo)) - 1u;
         const uint32_t prefix = hb == 31 ? 0u : (bound & (~0u << (hb + 1)));
 #pragma unroll
-        for (int i = 0; i < GB; ++i)
-            if (kk[i] != 0u) atomicAdd(&sm.hist[hidx((kk[i] >> lo) & dmask)], 1u);
+        for (int j = 0; j < KPT; ++j)
+            if (kk[j] != 0u) atomicAdd(&sm.hist[hidx((kk[j] >> lo) & dmask)], 1u);
         __syncthreads();
         Found fd[1];
         const uint32_t total = hist_find<1>(sm, {(uint32_t)topk}, fd);
@@ -770,8 +784,15 @@ __global__ __launch_bounds__(THREADS, 1) void split_indexer_kernel(
                 tau = prefix | f.bin;
                 ties = rem;
             } else if (f.cnt <= (uint32_t)NLIST) {
+                uint32_t cm = 0;
 #pragma unroll
-                for (int i = 0; i < GB; ++i) list_append(sm, kk[i] != 0u && ((kk[i] >> lo) & dmask) == f.bin, kk[i]);
+                for (int j = 0; j < KPT; ++j) cm += (kk[j] != 0u && ((kk[j] >> lo) & dmask) == f.bin) ? 1u : 0u;
+                if (cm != 0u) {
+                    uint32_t pm = atomicAdd(&sm.nl, cm);
+#pragma unroll
+                    for (int j = 0; j < KPT; ++j)
+                        if (kk[j] != 0u && ((kk[j] >> lo) & dmask) == f.bin) sm.lk[pm++] = kk[j];
+                }
                 __syncthreads();
                 if (wid == 0) {
                     uint32_t kth, gt;
@@ -788,40 +809,37 @@ __global__ __launch_bounds__(THREADS, 1) void split_indexer_kernel(
                 block_kth(
                     [&](auto fn) {
 #pragma unroll
-                        for (int i = 0; i < GB; ++i)
-                            if (kk[i] != 0u) fn(kk[i]);
+                        for (int j = 0; j < KPT; ++j)
+                            if (kk[j] != 0u) fn(kk[j]);
                     },
                     (uint32_t)topk, sm, tau, ties);
             }
         }
-        // Ordered output: group g = w + 8i holds slots 64g .. 64g+63 in index
-        // order; one scan over per-group (greater, equal) counts places them.
-        uint32_t mycnt = 0;
+        // Ordered output through LDS (the histogram's words are free now),
+        // then coalesced stores of the whole row.
+        uint32_t ngt = 0, neq = 0;
 #pragma unroll
-        for (int i = 0; i < GB; ++i) {
-            const uint32_t ngt = (uint32_t)__builtin_popcountll(wave_ballot(kk[i] > tau));
-            const uint32_t neq = (uint32_t)__builtin_popcountll(wave_ballot(kk[i] != 0u && kk[i] == tau));
-            mycnt = lane == i ? (ngt | (neq << 16)) : mycnt;  // counts < 2^14
+        for (int j = 0; j < KPT; ++j) {
+            ngt += kk[j] > tau ? 1u : 0u;
+            neq += (kk[j] != 0u && kk[j] == tau) ? 1u : 0u;
         }
-        if (lane < GB) sm.gcnt[wid + NW * lane] = mycnt;
-        __syncthreads();
         uint32_t tot;
-        const uint32_t ex = block_excl_scan(tid < NW * GB ? sm.gcnt[tid] : 0u, sm, tot);
-        if (tid < NW * GB) sm.goff[tid] = ex;
-        __syncthreads();
+        const uint32_t ex = block_excl_scan(ngt | (neq << 16), sm, tot);  // counts < 2^14
+        uint32_t eqb = ex >> 16;
+        uint32_t pos = (ex & 0xffffu) + (eqb < ties ? eqb : ties);
+        uint2 *stage = reinterpret_cast<uint2 *>(sm.hist);  // k <= DS4IDX_MAX_TOPK pairs fit
 #pragma unroll
-        for (int i = 0; i < GB; ++i) {
-            const uint32_t base = sm.goff[wid + NW * i];
-            const uint32_t eqb = base >> 16;
-            const bool eq = kk[i] != 0u && kk[i] == tau;
-            const uint64_t meq = wave_ballot(eq);
-            const bool keep = kk[i] > tau || (eq && eqb + lanes_below(meq) < ties);
-            const uint64_t mk = wave_ballot(keep);
-            const uint32_t pos = (base & 0xffffu) + (eqb < ties ? eqb : ties) + lanes_below(mk);
-            if (keep && pos < (uint32_t)topk) {
-                io[pos] = (int)(v0[i] >> 32);
-                if (vo) vo[pos] = key_float(kk[i]);
-            }
+        for (int j = 0; j < KPT; ++j) {
+            bool keep = kk[j] > tau;
+            if (kk[j] != 0u && kk[j] == tau) keep = eqb++ < ties;
+            if (keep) stage[pos++] = make_uint2((uint32_t)sm.sv.idx[KPT * tid + j], kk[j]);
+        }
+        __syncthreads();
+        const uint32_t nsel = total < (uint32_t)topk ? total : (uint32_t)topk;
+        for (int j = tid; j < (int)nsel; j += THREADS) {
+            const uint2 e = stage[j];
+            io[j] = (int)e.x;
+            if (vo) vo[j] = key_float(e.y);
         }
         m_out = total < (uint32_t)topk ? total : (uint32_t)topk;
     } else {
