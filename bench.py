@@ -45,20 +45,19 @@ def _parse():
 
 
 PROFILES = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles")
-KERNEL_SRC = os.path.join(os.path.dirname(os.path.abspath(__file__)),
-                          "sparse_attention_token_lightning_amd", "csrc", "mfma_indexer.hip")
+CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "sparse_attention_token_lightning_amd", "csrc")
 
 
-def kernel_digest() -> str:
+def kernel_digest(src: str) -> str:
     import hashlib
-    with open(KERNEL_SRC, "rb") as f:
+    with open(os.path.join(CSRC, src), "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per select launch from the committed counter summary, or None
-    when the kernel source changed since the counters were taken."""
-    path = os.path.join(PROFILES, "mfma_select_64k_traffic.txt")
+def measured_traffic(summary: str = "mfma_select_64k_traffic.txt", src: str = "mfma_indexer.hip"):
+    """HBM bytes per launch from a committed counter summary, or None when the
+    kernel source changed since the counters were taken."""
+    path = os.path.join(PROFILES, summary)
     if not os.path.exists(path):
         return None
     kv = {}
@@ -66,7 +65,7 @@ def measured_traffic():
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("kernel_source_sha256_16") != kernel_digest():
+    if kv.get("kernel_source_sha256_16") != kernel_digest(src):
         return None
     try:
         return int(float(kv["hbm_bytes_per_launch"]))
@@ -194,7 +193,9 @@ def main():
         extra["decode_256k"] = {"us_median": round(med, 2), "us_min": round(dus[0], 2),
                                 "alg_bytes": int(dbytes),
                                 "GB_s": round(dbytes / (med * 1e-6) / 1e9, 1),
-                                "hbm_frac": round(dbytes / (med * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+                                "hbm_frac": round(dbytes / (med * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                                "traffic": measured_traffic("split_decode_256k_traffic.txt",
+                                                            "split_indexer.hip")}
         del sets
 
     # ---------------------------------------------------------------- CPU oracle
