@@ -15,14 +15,17 @@
 //    into LDS (exact: every E4M3 value is a bf16 value); the per-token fp32
 //    scale is kept aside and applied once to the head-reduced score (allowed
 //    since the scale is positive, so it commutes with the ReLU).
-//  * Contraction. Heads sit on the M dimension of v_mfma_f32_32x32x16_bf16:
-//    two 32-row head blocks, 32 keys per block on N, 8 k-steps over D = 128,
-//    fp32 accumulation. Two 32-key sub-blocks are scored together: four
-//    independent accumulator chains per k-step.
-//  * Epilogue in registers. Each lane holds 16 head rows of one key per head
-//    block: ReLU (one v_med3), times w[t,h] (fp32), summed in-lane. The two
-//    lane halves hold disjoint head rows; one v_permlane32_swap completes
-//    sub-block A's keys in lanes 0-31 and sub-block B's in lanes 32-63. The
+//  * Contraction. v_mfma_f32_16x16x32_bf16 with heads on M (four 16-head
+//    tiles) and keys on N: a 64-key pair is 2 x 2 tiles of 16 keys, so each
+//    k-step issues 16 independent MFMAs (4 k-steps over D = 128) on four
+//    B fragments read once from LDS, fp32 accumulation. Many short chains
+//    keep the matrix pipe fed while the other wavefront on the SIMD runs its
+//    epilogue (with two 32x32 tiles per head block the epilogue did not
+//    overlap and cost a fifth of the time).
+//  * Epilogue in registers. Each lane holds 4 heads of each of 4 head tiles
+//    for 4 keys: ReLU (one v_med3), times w[t,h] (fp32), summed in-lane.
+//    v_permlane32_swap and v_permlane16_swap then add the other three lane
+//    groups' heads so that lane l holds the score of key l of the pair. The
 //    causal mask (key <= offset + t) is applied per lane.
 //  * Streaming top-k per token. A candidate buffer of 1024 (score, index)
 //    slots per token lives in LDS. A score enters only if it beats the
@@ -53,7 +56,7 @@ constexpr int CAP = 1280;   // candidate slots per token
 constexpr int THREADS = NWAVE * 64;
 
 typedef __attribute__((__vector_size__(8 * sizeof(short)))) short bf16x8;
-typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 
 struct alignas(16) Smem {
     uint16_t k[2][KT * KROW];
@@ -63,9 +66,9 @@ struct alignas(16) Smem {
     uint32_t hist[NWAVE][256];
 };
 
-// Row (head within the 32-row block) that accumulator element i of `lane`
-// holds in the 32x32 MFMA output; the column (key) is lane % 32.
-__device__ __forceinline__ int acc_row(int i, int lane) { return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3); }
+// v_mfma_f32_16x16x32_bf16 operand layout: lane l supplies row (A) or column
+// (B) l % 16 and the 8 contraction elements (l / 16) * 8 .. +7; the result
+// element i of lane l is row 4 * (l / 16) + i, column l % 16.
 
 // max(x, 0) in one instruction (scores stay far below the upper clamp).
 __device__ __forceinline__ float relu(float x) { return __builtin_amdgcn_fmed3f(x, 0.0f, 3.0e38f); }
@@ -236,20 +239,22 @@ __global__ __launch_bounds__(THREADS, 1) void mfma_indexer_kernel(
     const bool tok_ok = tok < T;
     const long long lim = tok_ok ? offset + tok : -1;  // last key this token sees
 
-    // Query as MFMA A operands: a[hb][ks] = Q[tok, head hb*32 + lane%32,
-    // dims ks*16 + (lane/32)*8 .. +7]. B operands use the same dim mapping.
-    bf16x8 a[2][8];
-    float wv[2][16];
+    // Query as MFMA A operands: a[m][ks] = Q[tok, head 16m + lane%16,
+    // dims 32ks + (lane/16)*8 .. +7]. B operands use the same dim mapping.
+    // wv[m][i] = W[tok, head 16m + 4(lane/16) + i], the heads of this lane's
+    // accumulator elements.
+    bf16x8 a[4][4];
+    float wv[4][4];
     {
         const long long qrow = ((long long)b * T + (tok_ok ? tok : 0)) * H;
 #pragma unroll
-        for (int hb = 0; hb < 2; ++hb) {
+        for (int m = 0; m < 4; ++m) {
             const bf16x8 *qp = reinterpret_cast<const bf16x8 *>(
-                Q + (qrow + hb * 32 + (lane & 31)) * D + (lane >> 5) * 8);
+                Q + (qrow + m * 16 + (lane & 15)) * D + (lane >> 4) * 8);
 #pragma unroll
-            for (int ks = 0; ks < 8; ++ks) a[hb][ks] = tok_ok ? qp[ks * 2] : bf16x8{};
+            for (int ks = 0; ks < 4; ++ks) a[m][ks] = tok_ok ? qp[ks * 4] : bf16x8{};
 #pragma unroll
-            for (int i = 0; i < 16; ++i) wv[hb][i] = tok_ok ? W[qrow + hb * 32 + acc_row(i, lane)] : 0.0f;
+            for (int i = 0; i < 4; ++i) wv[m][i] = tok_ok ? W[qrow + m * 16 + 4 * (lane >> 4) + i] : 0.0f;
         }
     }
 
@@ -277,36 +282,52 @@ __global__ __launch_bounds__(THREADS, 1) void mfma_indexer_kernel(
         for (int pp = 0; pp < KT / 64; ++pp) {
             const long long pbase = kbase + pp * 64;  // sub-blocks A = pbase.., B = pbase+32..
             if (pbase <= lim) {
-                f32x16 acc[2][2];
+                // 16 output tiles per pair: acc[s][n][m] = heads 16m.. x keys
+                // 32s + 16n .. (+15), 16 independent chains over 4 k-steps.
+                f32x4 acc[2][2][4];
+                const uint16_t *kp = &sm.k[cur][(pp * 64 + (lane & 15)) * KROW + (lane >> 4) * 8];
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) {
+                    bf16x8 bk[2][2];
+#pragma unroll
+                    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+                        for (int n = 0; n < 2; ++n)
+                            bk[s2][n] = *reinterpret_cast<const bf16x8 *>(kp + (32 * s2 + 16 * n) * KROW + ks * 32);
+#pragma unroll
+                    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+                        for (int n = 0; n < 2; ++n)
+#pragma unroll
+                            for (int m = 0; m < 4; ++m)
+                                acc[s2][n][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                    a[m][ks], bk[s2][n], ks ? acc[s2][n][m] : f32x4{}, 0, 0, 0);
+                }
+                // This lane's 16 heads of each of its 4 keys, then the other
+                // three lane groups' heads: after the 32- and 16-lane swaps,
+                // lane l holds the head sum of key l of the pair.
+                float part[2][2];
 #pragma unroll
                 for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-                    for (int hb = 0; hb < 2; ++hb) acc[s2][hb] = f32x16{};
-                const uint16_t *kp = &sm.k[cur][(pp * 64 + (lane & 31)) * KROW + (lane >> 5) * 8];
+                    for (int n = 0; n < 2; ++n) {
+                        float s4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-                for (int ks = 0; ks < 8; ++ks) {
-                    const bf16x8 bA = *reinterpret_cast<const bf16x8 *>(kp + ks * 16);
-                    const bf16x8 bB = *reinterpret_cast<const bf16x8 *>(kp + 32 * KROW + ks * 16);
+                        for (int m = 0; m < 4; ++m)
 #pragma unroll
-                    for (int hb = 0; hb < 2; ++hb) {
-                        acc[0][hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[hb][ks], bA, acc[0][hb], 0, 0, 0);
-                        acc[1][hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[hb][ks], bB, acc[1][hb], 0, 0, 0);
+                            for (int i = 0; i < 4; ++i) s4[i] = fmaf(wv[m][i], relu(acc[s2][n][m][i]), s4[i]);
+                        part[s2][n] = (s4[0] + s4[1]) + (s4[2] + s4[3]);
                     }
+                float half[2];
+#pragma unroll
+                for (int n = 0; n < 2; ++n) {
+                    const auto w32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0][n]),
+                                                                      __float_as_uint(part[1][n]), false, false);
+                    half[n] = __uint_as_float(w32[0]) + __uint_as_float(w32[1]);
                 }
-                float part[2];
-#pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2) {
-                    float s4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-                    for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-                        for (int i = 0; i < 16; ++i)
-                            s4[i & 3] = fmaf(wv[hb][i], relu(acc[s2][hb][i]), s4[i & 3]);
-                    part[s2] = (s4[0] + s4[1]) + (s4[2] + s4[3]);
-                }
-                const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0]),
-                                                                 __float_as_uint(part[1]), false, false);
-                float sc = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+                const auto w16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(half[0]), __float_as_uint(half[1]),
+                                                                  false, false);
+                float sc = __uint_as_float(w16[0]) + __uint_as_float(w16[1]);
                 const int kin = pp * 64 + lane;
                 if (KFP8) sc *= sm.scale[cur][kin];
                 sc = canon(sc);
