@@ -319,3 +319,16 @@ def test_split_hot_partition():
     gi, gv = run_select(wl, poison=True)
     assert list(gi[0]) == list(range(8192 - 512, 8192))
     assert np.array_equal(gv[0], (32.0 * scale[0, 8192 - 512:8192]).astype(np.float32))
+
+
+@pytest.mark.parametrize("S,topk,B", [
+    (1048576, 512, 2),   # 128 partitions: the largest short-list grid the direct merge takes
+    (262144, 2048, 2),   # k = 2048: short lists beyond one merge batch (the general path)
+    (300000, 96, 3),     # partial last partition, small k
+])
+def test_split_long_cache_decode(S, topk, B):
+    wl = W.decode(seed=40 + B, B=B, S=S, topk=topk)
+    _say(f"split decode B={B} S={S} k={topk}")
+    gi, gv = run_select(wl, poison=True)
+    check_invariants(wl, gi)
+    compare_rows(wl, np.arange(wl.B * wl.T), gi, gv, exact=False)
