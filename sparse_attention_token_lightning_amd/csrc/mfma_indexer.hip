@@ -120,7 +120,7 @@ __device__ __forceinline__ int wave_compact(float *cs, int *ci, const uint32_t (
 // largest order key is found digit by digit: each pass takes the AND and OR
 // of the keys still in play and starts its 8-bit window at their highest
 // differing bit, so shared high bits cost no pass.
-__device__ float wave_keep_topk(float *cs, int *ci, int n, int k, uint32_t *hist, int lane)
+__device__ __forceinline__ float wave_keep_topk(float *cs, int *ci, int n, int k, uint32_t *hist, int lane)
 {
     uint32_t u[CREG];
     int iv[CREG];
@@ -139,7 +139,7 @@ __device__ float wave_keep_topk(float *cs, int *ci, int n, int k, uint32_t *hist
 // Nothing that can still reach the top k is dropped (k entries already sit at
 // or above the edge). Returns the new count (n when no edge frees space);
 // `edge` receives the order key from which later scores are admitted.
-__device__ int wave_raise_threshold(float *cs, int *ci, int n, int k, uint32_t *hist, int lane,
+__device__ __forceinline__ int wave_raise_threshold(float *cs, int *ci, int n, int k, uint32_t *hist, int lane,
                                     uint32_t &edge)
 {
     uint32_t u[CREG];
@@ -274,100 +274,136 @@ __global__ __launch_bounds__(THREADS, 1) void mfma_indexer_kernel(
     store_tile<KFP8>(sm, 0, tr, tsc, tid);
     __syncthreads();
 
+    // Half-pair software pipeline. A 64-key pair is two 32-key halves of 8
+    // output tiles each (acc[s] for keys 32s..32s+31 of the pair). The MFMAs
+    // of one half run while the VALU reduces the other (the previous half),
+    // k-step by k-step with a scheduling fence after each, so the matrix
+    // cores and the VALU of a wavefront overlap; only the usual 64
+    // accumulator registers are live. Pairs past a token's last visible key
+    // are computed and masked (at most the block's 8-token spread).
+    f32x4 acc[2][2][4];  // [half][n][m]
+#pragma unroll
+    for (int n = 0; n < 2; ++n)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) acc[1][n][m] = f32x4{};
+    // MFMAs of half h of the pair at pair offset pp in buffer cur into
+    // acc[h], interleaved with the reduction of acc[h ^ 1] into part[n].
+    auto phase = [&](int h, int cur, int pp, float (&part)[2]) {
+        const uint16_t *kp = &sm.k[cur][(pp * 64 + 32 * h + (lane & 15)) * KROW + (lane >> 4) * 8];
+        const f32x4 (&r)[2][4] = acc[h ^ 1];
+        float s4[2][4] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+        bf16x8 bk[2];
+#pragma unroll
+        for (int n = 0; n < 2; ++n) bk[n] = *reinterpret_cast<const bf16x8 *>(kp + 16 * n * KROW);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            bf16x8 nb[2] = {bk[0], bk[1]};
+            if (ks < 3) {
+#pragma unroll
+                for (int n = 0; n < 2; ++n)
+                    nb[n] = *reinterpret_cast<const bf16x8 *>(kp + 16 * n * KROW + (ks + 1) * 32);
+            }
+#pragma unroll
+            for (int n = 0; n < 2; ++n)
+#pragma unroll
+                for (int m = 0; m < 4; ++m)
+                    acc[h][n][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[m][ks], bk[n],
+                                                                          ks ? acc[h][n][m] : f32x4{}, 0, 0, 0);
+            const int n = ks >> 1;  // 8 of the 32 elements of the half being reduced
+#pragma unroll
+            for (int mm = 0; mm < 2; ++mm) {
+                const int m = 2 * (ks & 1) + mm;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) s4[n][i] = fmaf(wv[m][i], relu(r[n][m][i]), s4[n][i]);
+            }
+            // Pin this step's reduction here (value-only code would otherwise
+            // sink below the fence, to its use after the last step).
+            asm volatile("" : "+v"(s4[n][0]), "+v"(s4[n][1]), "+v"(s4[n][2]), "+v"(s4[n][3]));
+            __builtin_amdgcn_sched_barrier(0);
+            bk[0] = nb[0];
+            bk[1] = nb[1];
+        }
+#pragma unroll
+        for (int n = 0; n < 2; ++n) part[n] = (s4[n][0] + s4[n][1]) + (s4[n][2] + s4[n][3]);
+    };
+    // Scale, mask and insert (or store) the pair at pbase (tile in buffer
+    // cur) from its halves' partial head sums: after the 32- and 16-lane
+    // swaps lane l holds the score of key l of the pair.
+    auto finish_pair = [&](const float (&p0)[2], const float (&p1)[2], long long pbase, int cur) {
+        float hsum[2];
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+            const auto w32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p0[n]), __float_as_uint(p1[n]),
+                                                              false, false);
+            hsum[n] = __uint_as_float(w32[0]) + __uint_as_float(w32[1]);
+        }
+        const auto w16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(hsum[0]), __float_as_uint(hsum[1]),
+                                                          false, false);
+        float sc = __uint_as_float(w16[0]) + __uint_as_float(w16[1]);
+        if (KFP8) sc *= sm.scale[cur][(int)(pbase % KT) + lane];
+        sc = canon(sc);
+        const long long key = pbase + lane;
+        const bool vis = key <= lim;
+        if (SCORE) {
+            if (tok_ok && key < S) scores[((long long)b * T + tok) * S + key] = vis ? sc : -INFINITY;
+        } else {
+            const bool pass = vis && sc >= thr;
+            const uint64_t m = wave_ballot(pass);
+            if (m) {
+                const int pos = cnt + (int)lanes_below(m);
+                if (pass) {
+                    cs[pos] = sc;
+                    ci[pos] = (int)key;
+                }
+                cnt += __builtin_popcountll(m);
+                if (cnt > CAP - 64) {
+                    wave_lds_sync();
+                    uint32_t edge = 0;
+                    const int kept = wave_raise_threshold(cs, ci, cnt, topk, sm.hist[wid], lane, edge);
+                    if (kept <= CAP - 256) {
+                        cnt = kept;
+                        thr = key_float(edge);
+                    } else {  // too little freed: exact k-th, admit strictly above it
+                        const float kth = wave_keep_topk(cs, ci, kept, topk, sm.hist[wid], lane);
+                        cnt = topk;
+                        thr = key_float(ord_key(kth) + 1u);
+                    }
+                }
+            }
+        }
+    };
+
+    float prev0[2] = {0.0f, 0.0f};  // first half's partial sums of the pair in flight
     for (int tile = 0; tile < ntiles; ++tile) {
         const int cur = tile & 1;
         if (tile + 1 < ntiles) load_tile<KFP8>(tr, tsc, Kb, Ksb, S, tile + 1, tid);
         const long long kbase = (long long)tile * KT;
 #pragma unroll
         for (int pp = 0; pp < KT / 64; ++pp) {
-            const long long pbase = kbase + pp * 64;  // sub-blocks A = pbase.., B = pbase+32..
-            if (pbase <= lim) {
-                // 16 output tiles per pair: acc[s][n][m] = heads 16m.. x keys
-                // 32s + 16n .. (+15), 16 independent chains over 4 k-steps.
-                f32x4 acc[2][2][4];
-                const uint16_t *kp = &sm.k[cur][(pp * 64 + (lane & 15)) * KROW + (lane >> 4) * 8];
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks) {
-                    bf16x8 bk[2][2];
-#pragma unroll
-                    for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-                        for (int n = 0; n < 2; ++n)
-                            bk[s2][n] = *reinterpret_cast<const bf16x8 *>(kp + (32 * s2 + 16 * n) * KROW + ks * 32);
-#pragma unroll
-                    for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-                        for (int n = 0; n < 2; ++n)
-#pragma unroll
-                            for (int m = 0; m < 4; ++m)
-                                acc[s2][n][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                    a[m][ks], bk[s2][n], ks ? acc[s2][n][m] : f32x4{}, 0, 0, 0);
-                }
-                // This lane's 16 heads of each of its 4 keys, then the other
-                // three lane groups' heads: after the 32- and 16-lane swaps,
-                // lane l holds the head sum of key l of the pair.
-                float part[2][2];
-#pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-                    for (int n = 0; n < 2; ++n) {
-                        float s4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-                        for (int m = 0; m < 4; ++m)
-#pragma unroll
-                            for (int i = 0; i < 4; ++i) s4[i] = fmaf(wv[m][i], relu(acc[s2][n][m][i]), s4[i]);
-                        part[s2][n] = (s4[0] + s4[1]) + (s4[2] + s4[3]);
-                    }
-                float half[2];
-#pragma unroll
-                for (int n = 0; n < 2; ++n) {
-                    const auto w32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0][n]),
-                                                                      __float_as_uint(part[1][n]), false, false);
-                    half[n] = __uint_as_float(w32[0]) + __uint_as_float(w32[1]);
-                }
-                const auto w16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(half[0]), __float_as_uint(half[1]),
-                                                                  false, false);
-                float sc = __uint_as_float(w16[0]) + __uint_as_float(w16[1]);
-                const int kin = pp * 64 + lane;
-                if (KFP8) sc *= sm.scale[cur][kin];
-                sc = canon(sc);
-                const long long key = kbase + kin;
-                const bool vis = key <= lim;
-                if (SCORE) {
-                    if (tok_ok && key < S) scores[((long long)b * T + tok) * S + key] = vis ? sc : -INFINITY;
-                } else {
-                    const bool pass = vis && sc >= thr;
-                    const uint64_t m = wave_ballot(pass);
-                    if (m) {
-                        const int pos = cnt + (int)lanes_below(m);
-                        if (pass) {
-                            cs[pos] = sc;
-                            ci[pos] = (int)key;
-                        }
-                        cnt += __builtin_popcountll(m);
-                        if (cnt > CAP - 64) {
-                            wave_lds_sync();
-                            uint32_t edge = 0;
-                            const int kept = wave_raise_threshold(cs, ci, cnt, topk, sm.hist[wid], lane, edge);
-                            if (kept <= CAP - 256) {
-                                cnt = kept;
-                                thr = key_float(edge);
-                            } else {  // too little freed: exact k-th, admit strictly above it
-                                const float kth = wave_keep_topk(cs, ci, kept, topk, sm.hist[wid], lane);
-                                cnt = topk;
-                                thr = key_float(ord_key(kth) + 1u);
-                            }
-                        }
-                    }
-                }
-            } else if (SCORE && tok_ok) {
-                float *orow = scores + ((long long)b * T + tok) * S;
-                const long long key = pbase + lane;
-                if (key < S) orow[key] = -INFINITY;
-            }
+            float h1[2], h0[2];
+            phase(0, cur, pp, h1);  // MFMAs of this pair's first half; previous pair's second half reduced
+            if (tile > 0 || pp > 0)
+                finish_pair(prev0, h1, kbase + pp * 64 - 64, pp > 0 ? cur : cur ^ 1);
+            phase(1, cur, pp, h0);  // MFMAs of the second half; this pair's first half reduced
+            prev0[0] = h0[0];
+            prev0[1] = h0[1];
         }
         if (tile + 1 < ntiles) store_tile<KFP8>(sm, cur ^ 1, tr, tsc, tid);
         __syncthreads();
+    }
+    {  // the last pair's second half
+        float h1[2];
+        const f32x4 (&r)[2][4] = acc[1];
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+            float s4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) s4[i] = fmaf(wv[m][i], relu(r[n][m][i]), s4[i]);
+            h1[n] = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+        }
+        finish_pair(prev0, h1, (long long)ntiles * KT - 64, (ntiles - 1) & 1);
     }
 
     if (!SCORE && tok_ok) {
