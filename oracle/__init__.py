@@ -5,7 +5,8 @@ CPU-baseline leg may import this package. It shares no code with the HIP
 library; the two meet only in the seeded inputs of ``workloads``.
 
 The arithmetic lives in ``ds4idx_oracle.c`` (plain C, fp64, OpenMP over rows
-and key blocks); this wrapper only builds it with gcc and marshals arrays.
+and key blocks) and ``ds4idx_kcache_oracle.c`` (the key-cache writer's E4M3
+quantisation); this wrapper only builds them with gcc and marshals arrays.
 """
 from __future__ import annotations
 
@@ -16,17 +17,19 @@ import subprocess
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SRC = os.path.join(_HERE, "ds4idx_oracle.c")
+_SRCS = [os.path.join(_HERE, "ds4idx_oracle.c"), os.path.join(_HERE, "ds4idx_kcache_oracle.c")]
 _LIB = os.path.join(_HERE, "libds4idx_oracle.so")
 _lib = None
 
 
 def build(force: bool = True) -> str:
     """Compile the oracle with gcc (-O2, OpenMP)."""
-    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+    stale = not os.path.exists(_LIB) or \
+        os.path.getmtime(_LIB) < max(os.path.getmtime(s) for s in _SRCS)
+    if force or stale:
         tmp = _LIB + ".tmp"
         subprocess.check_call(["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-std=c11",
-                               "-Wall", "-o", tmp, _SRC, "-lm"])
+                               "-Wall", "-o", tmp, *_SRCS, "-lm"])
         os.replace(tmp, _LIB)
     return _LIB
 
@@ -45,6 +48,10 @@ def _load():
         lib.ds4o_score_pairs.argtypes = [p, i, p, i, p, p, i, i, i, i, i, i64,
                                          p, p, i64, p, i]
         lib.ds4o_score_pairs.restype = i
+        lib.ds4o_e4m3_encode.argtypes = [ctypes.c_double]
+        lib.ds4o_e4m3_encode.restype = i
+        lib.ds4o_quantize_k.argtypes = [p, i, i64, i, p, p]
+        lib.ds4o_quantize_k.restype = i
         _lib = lib
     return _lib
 
@@ -55,6 +62,28 @@ def _ptr(a):
 
 def e4m3_decode(code: int) -> float:
     return _load().ds4o_e4m3_decode(int(code))
+
+
+def e4m3_encode(x: float) -> int:
+    """Nearest OCP E4M3FN code to x (saturating at +-448, ties to the even code)."""
+    return _load().ds4o_e4m3_encode(float(x))
+
+
+def quantize_k(k: np.ndarray, dtype: int):
+    """Per-token E4M3 quantisation of key vectors.
+
+    k: [n, D] float32 values (dtype 0) or uint16 bf16 bit patterns (dtype 1).
+    Returns (codes uint8 [n, D], scale float32 [n]).
+    """
+    k = np.ascontiguousarray(k, dtype=np.float32 if dtype == 0 else np.uint16)
+    if k.ndim != 2:
+        raise ValueError("k must be [n, D]")
+    n, D = k.shape
+    codes = np.empty((n, D), dtype=np.uint8)
+    scale = np.empty(n, dtype=np.float32)
+    if _load().ds4o_quantize_k(_ptr(k), int(dtype), n, D, _ptr(codes), _ptr(scale)) != 0:
+        raise ValueError("oracle rejected the quantisation arguments")
+    return codes, scale
 
 
 def _problem_args(wl):
