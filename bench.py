@@ -11,7 +11,9 @@ select kernel (algorithmic bf16 flop per launch over its HIP-event-timed
 average duration, against the 2.5 PFLOP/s dense bf16 peak), the 256k decode
 latency (8 streams x 1 query x 262144 keys, rotated over 3 copies of the
 inputs so the 256 MB last-level cache cannot hold them), and the CPU oracle
-timed on a bounded sample of the same prefill rows.
+timed on a bounded sample of the same prefill rows. Also reported: the
+key-cache writer (per-token E4M3 quantisation) filling the whole 256k decode
+cache of 8 streams from bf16 keys, against the HBM peak.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -38,6 +40,8 @@ def _parse():
                     help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-writer", action="store_true")
+    ap.add_argument("--writer-iters", type=int, default=20)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, copy 256 MiB once (the reference kernel that "
                          "scales the FETCH_SIZE / WRITE_SIZE counters to bytes)")
@@ -197,6 +201,35 @@ def main():
                                 "traffic": measured_traffic("split_decode_256k_traffic.txt",
                                                             "split_indexer.hip")}
         del sets
+
+    # ---------------------------------------------------------------- key-cache writer
+    if not args.no_writer:
+        kn = W.new_keys()
+        n_tok, kdim = kn.shape
+        kin = torch.from_numpy(kn.view(np.int16)).view(torch.bfloat16).to(dev)
+        del kn
+        cache = torch.empty((n_tok, kdim), dtype=torch.uint8, device=dev)
+        cscale = torch.empty((n_tok,), dtype=torch.float32, device=dev)
+        for _ in range(3):
+            ds.k_cache_write(kin, cache, cscale, stream=stream)
+        torch.cuda.synchronize()
+        wev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
+               for _ in range(args.writer_iters)]
+        for e in wev:
+            e[0].record(stream)
+            ds.k_cache_write(kin, cache, cscale, stream=stream)
+            e[1].record(stream)
+        torch.cuda.synchronize()
+        wus = sorted(e[0].elapsed_time(e[1]) * 1e3 for e in wev)
+        wbytes = n_tok * (2 * kdim + kdim + 4)
+        wmed = wus[len(wus) // 2]
+        extra["k_cache_write_256k"] = {
+            "workload": f"{n_tok} bf16 keys (8 streams x 262144), D={kdim} -> E4M3 + fp32 scale",
+            "us_median": round(wmed, 2), "us_min": round(wus[0], 2), "alg_bytes": int(wbytes),
+            "GB_s": round(wbytes / (wmed * 1e-6) / 1e9, 1),
+            "hbm_frac": round(wbytes / (wmed * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic("k_cache_write_256k_traffic.txt", "k_cache_writer.hip")}
+        del kin, cache, cscale
 
     # ---------------------------------------------------------------- CPU oracle
     cpu = None

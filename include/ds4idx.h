@@ -55,6 +55,7 @@ extern "C" {
 
 #define DS4IDX_ABI_VERSION 1
 #define DS4IDX_MAX_TOPK 2048
+#define DS4IDX_K_CACHE_MAX_D 512 /* largest D ds4idx_k_cache_write takes */
 
 typedef enum {
     DS4IDX_OK = 0,
@@ -127,6 +128,36 @@ int ds4idx_topk(const ds4idx_problem *p, const float *scores, int32_t k, int32_t
 int ds4idx_select(const ds4idx_problem *p, const void *Q, const void *K, const float *K_scale,
                   const float *W, int32_t k, int32_t *idx, float *vals, void *workspace,
                   size_t ws_bytes, void *stream);
+
+/* Key-cache writer, the step upstream of the scorer: quantises n new key
+ * vectors to OCP E4M3FN codes with one fp32 scale per token and stores them in
+ * rows of the key cache that ds4idx_select reads as K and K_scale. The pages
+ * record that the indexer's cache holds E4M3 codes and that reading codes of
+ * one E4M3 variant as the other scales every key by 2 (MI300X write-up, FP8
+ * format mismatch section); they do not print a scale rule. The rule here is
+ * plain absmax scaling into the OCP range:
+ *
+ *     scale[s]  = max(amax_s, 2^-126) / 448      amax_s = max_d |K_new[s,d]|
+ *     code[s,d] = E4M3 round-to-nearest-even of clamp(K_new[s,d] / scale[s], -448, 448)
+ *
+ * both divisions in correctly rounded fp32; a zero result keeps its sign
+ * (-0 gives 0x80). Dequantised keys are scale[s] * decode(code[s,d]).
+ *
+ *   K_new        [n, D] fp32 or bf16 (k_dtype DS4IDX_F32 or DS4IDX_BF16),
+ *                16-byte aligned
+ *   slots        [n] int64 device array: the cache row each token goes to, or
+ *                NULL for rows 0 .. n-1. Tokens whose slot lies outside
+ *                [0, cache_rows) are skipped (nothing written); two tokens
+ *                with the same slot race.
+ *   cache        [cache_rows, D] E4M3 codes, 8-byte aligned
+ *   cache_scale  [cache_rows] fp32
+ *
+ * D must be a multiple of 8 and at most 512, n >= 0 (n = 0 launches nothing),
+ * cache_rows >= 1. Non-finite inputs give undefined codes. Asynchronous on
+ * `stream`, like the other calls; no workspace. */
+int ds4idx_k_cache_write(const void *K_new, int32_t k_dtype, int64_t n, int32_t D,
+                         const int64_t *slots, uint8_t *cache, float *cache_scale,
+                         int64_t cache_rows, void *stream);
 
 #ifdef __cplusplus
 }

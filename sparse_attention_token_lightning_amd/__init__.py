@@ -9,6 +9,10 @@ not built, every call raises.
 
 q [B,T,H,D] bf16/fp32, k [B,S,D] bf16/fp32 or uint8 OCP E4M3 codes (or
 torch.float8_e4m3fn), k_scale [B,S] fp32 for fp8 keys, w [B,T,H] fp32.
+
+    k_cache_write(k_new, cache, cache_scale, slots=None)
+
+quantises new keys [n,D] (bf16/fp32) into E4M3 cache rows with one scale each.
 """
 from __future__ import annotations
 
@@ -26,11 +30,13 @@ F32, BF16, FP8_E4M3 = 0, 1, 2
 OP_SCORE, OP_TOPK, OP_SELECT = 0, 1, 2
 IMPL_AUTO, IMPL_REF, IMPL_OPT = 0, 1, 2
 MAX_TOPK = 2048
+K_CACHE_MAX_D = 512
 ABI_VERSION = 1
 
 # Every symbol include/ds4idx.h declares.
 EXPORTS = ("ds4idx_abi_version", "ds4idx_status_string", "ds4idx_set_impl", "ds4idx_get_impl",
-           "ds4idx_workspace_bytes", "ds4idx_score", "ds4idx_topk", "ds4idx_select")
+           "ds4idx_workspace_bytes", "ds4idx_score", "ds4idx_topk", "ds4idx_select",
+           "ds4idx_k_cache_write")
 
 
 class Problem(ctypes.Structure):
@@ -73,6 +79,9 @@ def lib() -> ctypes.CDLL:
         L.ds4idx_topk.restype = ctypes.c_int
         L.ds4idx_select.argtypes = [P, vp, vp, vp, vp, i32, vp, vp, vp, sz, vp]
         L.ds4idx_select.restype = ctypes.c_int
+        L.ds4idx_k_cache_write.argtypes = [vp, i32, ctypes.c_int64, i32, vp, vp, vp,
+                                           ctypes.c_int64, vp]
+        L.ds4idx_k_cache_write.restype = ctypes.c_int
         if L.ds4idx_abi_version() != ABI_VERSION:
             raise RuntimeError("libds4idx ABI version mismatch; rebuild the library")
         _lib = L
@@ -205,3 +214,31 @@ def select(q, k, k_scale, w, causal_offset: int, topk: int = 512,
     if st != OK:
         raise Ds4idxError(st, "ds4idx_select")
     return idx, vals
+
+
+def k_cache_write(k_new: torch.Tensor, cache: torch.Tensor, cache_scale: torch.Tensor,
+                  slots: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Quantise k_new [n,D] (bf16/fp32) to E4M3 with one fp32 scale per token
+    and store row i into cache[slots[i]] / cache_scale[slots[i]] (rows 0..n-1
+    when slots is None). cache [rows,D] uint8 or float8_e4m3fn, cache_scale
+    [rows] fp32. Slots outside [0, rows) are skipped."""
+    if k_new.dim() != 2 or cache.dim() != 2 or cache_scale.dim() != 1:
+        raise ValueError("k_new must be [n,D], cache [rows,D], cache_scale [rows]")
+    n, D = k_new.shape
+    if cache.shape[1] != D or cache_scale.shape[0] != cache.shape[0]:
+        raise ValueError("cache and cache_scale do not match k_new")
+    if cache.dtype not in (torch.uint8, torch.float8_e4m3fn) or cache_scale.dtype != torch.float32:
+        raise ValueError("cache must be uint8/float8_e4m3fn and cache_scale float32")
+    named = (("k_new", k_new), ("cache", cache), ("cache_scale", cache_scale))
+    if slots is not None:
+        if slots.dtype != torch.int64 or tuple(slots.shape) != (n,):
+            raise ValueError("slots must be int64 [n]")
+        named += (("slots", slots),)
+    for name, t in named:
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    st = lib().ds4idx_k_cache_write(_ptr(k_new), _dtype_code(k_new, False), int(n), int(D),
+                                    _ptr(slots), _ptr(cache), _ptr(cache_scale),
+                                    int(cache.shape[0]), _stream(stream))
+    if st != OK:
+        raise Ds4idxError(st, "ds4idx_k_cache_write")

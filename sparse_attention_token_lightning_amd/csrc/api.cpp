@@ -204,4 +204,24 @@ int ds4idx_select(const ds4idx_problem *p, const void *Q, const void *K, const f
     return launch_status(ds4idx::launch_topk_ref(q, sc, k, idx, vals, s));
 }
 
+int ds4idx_k_cache_write(const void *K_new, int32_t k_dtype, int64_t n, int32_t D,
+                         const int64_t *slots, uint8_t *cache, float *cache_scale,
+                         int64_t cache_rows, void *stream)
+{
+    if (k_dtype != DS4IDX_F32 && k_dtype != DS4IDX_BF16) return DS4IDX_ERR_INVALID_ARG;
+    if (n < 0 || D < 8 || D % 8 != 0 || D > DS4IDX_K_CACHE_MAX_D || cache_rows < 1)
+        return DS4IDX_ERR_INVALID_ARG;
+    if (n == 0) return DS4IDX_OK;
+    if (!K_new || !cache || !cache_scale || !aligned(K_new, 16) || !aligned(cache, 8) ||
+        !aligned(cache_scale, 4) || (slots && !aligned(slots, 8)))
+        return DS4IDX_ERR_INVALID_ARG;
+    // One 256-thread block per 256 / G tokens; the grid's x dimension is 32-bit.
+    if (n > ((int64_t)INT32_MAX / ds4idx::k_cache_lanes(D)) * 256) return DS4IDX_ERR_UNSUPPORTED;
+    static_assert(sizeof(long long) == sizeof(int64_t), "int64 slots");
+    return launch_status(ds4idx::launch_k_cache_write(K_new, k_dtype, n, D,
+                                                      reinterpret_cast<const long long *>(slots),
+                                                      cache, cache_scale, cache_rows,
+                                                      static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -144,3 +144,28 @@ def test_workspace_sizes_and_checks():
                                None) == ds.ERR_UNSUPPORTED
     finally:
         ds.set_impl(prev)
+
+
+FAKE8_MIS = ctypes.c_void_p(0x10004)  # 4-byte aligned, not 8
+
+
+@pytest.mark.parametrize("kw", [dict(dtype=ds.FP8_E4M3), dict(dtype=7), dict(n=-1), dict(D=0),
+                                dict(D=12), dict(D=520), dict(rows=0), dict(kin=None),
+                                dict(cache=None), dict(scale=None), dict(kin=FAKE_MIS),
+                                dict(cache=FAKE8_MIS), dict(slots=FAKE8_MIS)])
+def test_k_cache_write_rejects_bad_arguments(kw):
+    a = dict(kin=FAKE, dtype=ds.BF16, n=4, D=128, slots=None, cache=FAKE, scale=FAKE, rows=16)
+    a.update(kw)
+    st = ds.lib().ds4idx_k_cache_write(a["kin"], a["dtype"], a["n"], a["D"], a["slots"], a["cache"],
+                                       a["scale"], a["rows"], None)
+    assert st == ds.ERR_INVALID_ARG
+
+
+def test_k_cache_write_empty_is_a_no_op():
+    # n = 0 returns before touching any pointer or launching anything
+    assert ds.lib().ds4idx_k_cache_write(None, ds.F32, 0, 128, None, None, None, 1, None) == ds.OK
+
+
+def test_k_cache_write_grid_limit():
+    st = ds.lib().ds4idx_k_cache_write(FAKE, ds.BF16, 1 << 40, 128, None, FAKE, FAKE, 16, None)
+    assert st == ds.ERR_UNSUPPORTED

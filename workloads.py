@@ -238,3 +238,18 @@ def sample_rows(wl: Workload, n: int, seed: int = 7) -> np.ndarray:
             fixed.add(r)
             rows.append(r)
     return np.array(sorted(rows), dtype=np.int64)
+
+
+# --------------------------------------------------------------------------- key-cache writer
+
+def new_keys(seed: int = 6, n: int = 8 * 262144, D: int = 128, log_spread: float = 0.0,
+             dtype: int = BF16) -> np.ndarray:
+    """Key vectors entering the key-cache writer: N(0,1) rows, each optionally
+    multiplied by exp(U(-log_spread, log_spread)) so per-token scales differ.
+    Returns uint16 bf16 bits (dtype BF16) or float32 values (dtype F32), [n, D].
+    The default size is the 256k decode cache of 8 streams, written whole."""
+    gk, gs = _streams(seed, 2)
+    x = gk.standard_normal((n, D), dtype=np.float32)
+    if log_spread > 0:
+        x *= np.exp(gs.uniform(-log_spread, log_spread, (n, 1))).astype(np.float32)
+    return to_bf16_bits(x) if dtype == BF16 else x
