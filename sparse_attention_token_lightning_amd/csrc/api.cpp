@@ -216,7 +216,8 @@ int ds4idx_k_cache_write(const void *K_new, int32_t k_dtype, int64_t n, int32_t 
         !aligned(cache_scale, 4) || (slots && !aligned(slots, 8)))
         return DS4IDX_ERR_INVALID_ARG;
     // One 256-thread block per 256 / G tokens; the grid's x dimension is 32-bit.
-    if (n > ((int64_t)INT32_MAX / ds4idx::k_cache_lanes(D)) * 256) return DS4IDX_ERR_UNSUPPORTED;
+    const int G = ds4idx::k_cache_lanes(D, ds4idx::k_cache_vals_per_lane(D, cache));
+    if (n > ((int64_t)INT32_MAX / G) * 256) return DS4IDX_ERR_UNSUPPORTED;
     static_assert(sizeof(long long) == sizeof(int64_t), "int64 slots");
     return launch_status(ds4idx::launch_k_cache_write(K_new, k_dtype, n, D,
                                                       reinterpret_cast<const long long *>(slots),

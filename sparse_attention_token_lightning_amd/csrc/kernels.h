@@ -49,8 +49,9 @@ SplitWorkspace split_workspace(void *ws, const Problem &p, int k);
 hipError_t launch_split_select(const Problem &p, const void *Q, const void *K, const float *Ks,
                                const float *W, int k, int *idx, float *vals, void *ws, hipStream_t st);
 
-// Key-cache writer: per-token E4M3 quantisation, G lanes per token.
-int k_cache_lanes(int D);
+// Key-cache writer: per-token E4M3 quantisation, V values on each of G lanes per token.
+int k_cache_lanes(int D, int V);
+int k_cache_vals_per_lane(int D, const void *cache);
 hipError_t launch_k_cache_write(const void *kin, int k_dtype, long long n, int D,
                                 const long long *slots, uint8_t *cache, float *cache_scale,
                                 long long rows, hipStream_t st);

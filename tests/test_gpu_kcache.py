@@ -22,10 +22,15 @@ def _dev_keys(k: np.ndarray, dtype: int) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(k, dtype=np.float32)).cuda()
 
 
-def _write(k: np.ndarray, dtype: int, rows=None, slots=None, fill=0xAA):
+def _write(k: np.ndarray, dtype: int, rows=None, slots=None, fill=0xAA, misalign16=False):
     n, D = k.shape
     rows = n if rows is None else rows
-    cache = torch.full((rows, D), fill, dtype=torch.uint8, device="cuda")
+    if misalign16:  # 8-byte but not 16-byte aligned rows: the 8-values-per-lane kernel
+        buf = torch.full((rows * D + 16,), fill, dtype=torch.uint8, device="cuda")
+        cache = buf[8:8 + rows * D].view(rows, D)
+        assert cache.data_ptr() % 16 == 8
+    else:
+        cache = torch.full((rows, D), fill, dtype=torch.uint8, device="cuda")
     scale = torch.full((rows,), -1.0, dtype=torch.float32, device="cuda")
     sl = None if slots is None else torch.from_numpy(np.asarray(slots, np.int64)).cuda()
     ds.k_cache_write(_dev_keys(k, dtype), cache, scale, sl)
@@ -50,8 +55,9 @@ def test_random_tokens_exact(dtype, D, n):
     _exact(k, dtype, codes, scale)
 
 
+@pytest.mark.parametrize("misalign16", [False, True])
 @pytest.mark.parametrize("dtype", [W.BF16, W.F32])
-def test_special_tokens_exact(dtype):
+def test_special_tokens_exact(dtype, misalign16):
     # zeros, -0, one nonzero, fp32 subnormals below the scale floor, huge and
     # tiny magnitudes, heavy tails, all-equal, small integers
     g = np.random.Generator(np.random.PCG64(9))
@@ -71,20 +77,26 @@ def test_special_tokens_exact(dtype):
     k[11] *= 2.0 ** -120
     if dtype == W.BF16:
         k = W.to_bf16_bits(k)
-    _say(f"k-cache writer special tokens dtype={W.DTYPE_NAMES[dtype]}")
-    codes, scale = _write(k, dtype)
+    _say(f"k-cache writer special tokens dtype={W.DTYPE_NAMES[dtype]} misalign16={misalign16}")
+    codes, scale = _write(k, dtype, misalign16=misalign16)
     _exact(k, dtype, codes, scale)
 
 
-def test_quotients_near_every_midpoint_exact():
+@pytest.mark.parametrize("misalign16", [False, True])
+def test_quotients_near_every_midpoint_exact(misalign16):
     # Tokens whose quotients k / scale land on, and a few fp32 steps around,
     # every midpoint between adjacent E4M3 values, under scales that are not
     # powers of two: a division that is off by one step, or rounding that is
-    # not to nearest-even, changes codes here.
+    # not to nearest-even, changes codes here. The scales span both division
+    # paths of the kernel (scale >= 2^-80 and below) and the boundary.
     vals = np.array([oracle.e4m3_decode(c) for c in range(127)])
     mids = ((vals[:-1] + vals[1:]) / 2).astype(np.float32)
     rows = []
-    for amax in (448.0, 1.0, 3.0, 0.1, 1000.0, 7.0e-3, 2.0 ** 20 * 3):
+    edge = 448.0 * 2.0 ** -80
+    for amax in (448.0, 1.0, 3.0, 0.1, 1000.0, 7.0e-3, 2.0 ** 20 * 3, 2.0 ** 100 * 5, edge,
+                 float(np.nextafter(np.float32(edge), np.float32(1))),
+                 float(np.nextafter(np.float32(edge), np.float32(0))), 3.0 * 2.0 ** -85,
+                 5.0 * 2.0 ** -100, 1.5 * 2.0 ** -110):
         sc = np.float32(amax) / np.float32(448.0)
         base = (mids.astype(np.float64) * np.float64(sc)).astype(np.float32)
         for step in (-2, -1, 0, 1, 2):
@@ -97,8 +109,8 @@ def test_quotients_near_every_midpoint_exact():
                 row[1:1 + len(v)] = sign * v
                 rows.append(row)
     k = np.stack(rows)
-    _say(f"k-cache writer near-midpoint quotients: {len(rows)} tokens")
-    codes, scale = _write(k, W.F32)
+    _say(f"k-cache writer near-midpoint quotients: {len(rows)} tokens misalign16={misalign16}")
+    codes, scale = _write(k, W.F32, misalign16=misalign16)
     _exact(k, W.F32, codes, scale)
 
 
