@@ -129,6 +129,47 @@ int ds4idx_select(const ds4idx_problem *p, const void *Q, const void *K, const f
                   const float *W, int32_t k, int32_t *idx, float *vals, void *workspace,
                   size_t ws_bytes, void *stream);
 
+/* Ragged batch: B independent streams (requests) packed along the rows, in
+ * one launch, as a serving step mixes requests with different cache lengths
+ * and different numbers of new tokens (the MI300X write-up's concurrency
+ * sweep and chunked-prefill token budget, "DeepSeek V4 Flash는 단일 AMD
+ * MI300X에서 실행됩니다", production tuning table). Stream b owns query rows
+ * cu_q[b] .. cu_q[b+1]-1 of Q, W, idx and vals (T_b rows) and key rows
+ * cu_k[b] .. cu_k[b+1]-1 of K and K_scale (S_b cached keys). Its new tokens
+ * are the last T_b of its cache, so its query t sees its keys
+ * s <= S_b - T_b + t, and idx holds indices local to the stream (0 .. S_b-1),
+ * ascending, -1 padded, as in ds4idx_select. Each stream's result equals a
+ * ds4idx_select call on that stream alone with causal_offset = S_b - T_b.
+ *
+ * Layouts: Q [total_q, H, D], W [total_q, H], K [total_k, D], K_scale
+ * [total_k], idx and vals [total_q, k]. cu_q (int32) and cu_k (int64) are
+ * device arrays of B + 1 non-decreasing prefix sums from 0 to total_q and
+ * total_k; T_b <= S_b <= max_k is required. Malformed prefix arrays give
+ * undefined results for the rows concerned, but no access outside the
+ * buffers the sizes describe. Only the MFMA shape has ragged kernels (H = 64,
+ * D = 128, bf16 Q, bf16 or E4M3 K); other shapes return
+ * DS4IDX_ERR_UNSUPPORTED, and the kernel-family switch does not apply. */
+typedef struct {
+    int32_t B;           /* streams, >= 1 */
+    int32_t total_q;     /* cu_q[B]: query rows (0: nothing to do) */
+    int64_t total_k;     /* cu_k[B]: key rows */
+    int32_t max_k;       /* >= every S_b: sizes the split-key grid and workspace */
+    int32_t H, D;
+    int32_t q_dtype, k_dtype;
+} ds4idx_varlen_problem;
+
+/* Workspace bytes for ds4idx_select_varlen (0 if none), or (size_t)-1 for an
+ * invalid problem. Same zero-fill and alignment rules as ds4idx_select's. */
+size_t ds4idx_varlen_workspace_bytes(const ds4idx_varlen_problem *p, int32_t k);
+
+/* Fused scorer + top-k over a ragged batch (see above). 1 <= k <= DS4IDX_MAX_TOPK;
+ * k > 512 is served only when the batch has few enough rows for the split-key
+ * kernel (total_q <= 65535). */
+int ds4idx_select_varlen(const ds4idx_varlen_problem *p, const int32_t *cu_q, const int64_t *cu_k,
+                         const void *Q, const void *K, const float *K_scale, const float *W,
+                         int32_t k, int32_t *idx, float *vals, void *workspace, size_t ws_bytes,
+                         void *stream);
+
 /* Key-cache writer, the step upstream of the scorer: quantises n new key
  * vectors to OCP E4M3FN codes with one fp32 scale per token and stores them in
  * rows of the key cache that ds4idx_select reads as K and K_scale. The pages

@@ -36,13 +36,19 @@ ABI_VERSION = 1
 # Every symbol include/ds4idx.h declares.
 EXPORTS = ("ds4idx_abi_version", "ds4idx_status_string", "ds4idx_set_impl", "ds4idx_get_impl",
            "ds4idx_workspace_bytes", "ds4idx_score", "ds4idx_topk", "ds4idx_select",
-           "ds4idx_k_cache_write")
+           "ds4idx_k_cache_write", "ds4idx_varlen_workspace_bytes", "ds4idx_select_varlen")
 
 
 class Problem(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("T", ctypes.c_int32), ("S", ctypes.c_int32),
                 ("H", ctypes.c_int32), ("D", ctypes.c_int32), ("causal_offset", ctypes.c_int64),
                 ("q_dtype", ctypes.c_int32), ("k_dtype", ctypes.c_int32)]
+
+
+class VarlenProblem(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("total_q", ctypes.c_int32), ("total_k", ctypes.c_int64),
+                ("max_k", ctypes.c_int32), ("H", ctypes.c_int32),
+                ("D", ctypes.c_int32), ("q_dtype", ctypes.c_int32), ("k_dtype", ctypes.c_int32)]
 
 
 class Ds4idxError(RuntimeError):
@@ -82,6 +88,11 @@ def lib() -> ctypes.CDLL:
         L.ds4idx_k_cache_write.argtypes = [vp, i32, ctypes.c_int64, i32, vp, vp, vp,
                                            ctypes.c_int64, vp]
         L.ds4idx_k_cache_write.restype = ctypes.c_int
+        VP = ctypes.POINTER(VarlenProblem)
+        L.ds4idx_varlen_workspace_bytes.argtypes = [VP, i32]
+        L.ds4idx_varlen_workspace_bytes.restype = sz
+        L.ds4idx_select_varlen.argtypes = [VP, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, sz, vp]
+        L.ds4idx_select_varlen.restype = ctypes.c_int
         if L.ds4idx_abi_version() != ABI_VERSION:
             raise RuntimeError("libds4idx ABI version mismatch; rebuild the library")
         _lib = L
@@ -213,6 +224,63 @@ def select(q, k, k_scale, w, causal_offset: int, topk: int = 512,
                              _ptr(idx), _ptr(vals), _ptr(workspace), ws_bytes, _stream(stream))
     if st != OK:
         raise Ds4idxError(st, "ds4idx_select")
+    return idx, vals
+
+
+def make_varlen_problem(q, k, cu_q, cu_k, max_k: int) -> VarlenProblem:
+    if q.dim() != 3 or k.dim() != 2:
+        raise ValueError("ragged q must be [total_q,H,D] and k [total_k,D]")
+    total_q, H, D = q.shape
+    if k.shape[1] != D:
+        raise ValueError(f"k shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
+    if cu_q.dim() != 1 or cu_k.dim() != 1 or cu_q.numel() != cu_k.numel() or cu_q.numel() < 2:
+        raise ValueError("cu_q and cu_k must be [B+1] prefix sums")
+    return VarlenProblem(cu_q.numel() - 1, total_q, k.shape[0], int(max_k), H, D,
+                         _dtype_code(q, False), _dtype_code(k, True))
+
+
+def varlen_workspace_bytes(problem: VarlenProblem, k: int) -> int:
+    n = lib().ds4idx_varlen_workspace_bytes(ctypes.byref(problem), int(k))
+    if n == ctypes.c_size_t(-1).value:
+        raise Ds4idxError(ERR_INVALID_ARG, "ds4idx_varlen_workspace_bytes")
+    return n
+
+
+def new_varlen_workspace(problem: VarlenProblem, k: int, device=None) -> Optional[torch.Tensor]:
+    """A zero-filled device workspace big enough for ds4idx_select_varlen (or None)."""
+    n = varlen_workspace_bytes(problem, k)
+    return None if n == 0 else torch.zeros(n, dtype=torch.uint8, device=device or "cuda")
+
+
+def select_varlen(q, k, k_scale, w, cu_q, cu_k, max_k: int, topk: int = 512,
+                  idx: Optional[torch.Tensor] = None, vals: Optional[torch.Tensor] = None,
+                  workspace: Optional[torch.Tensor] = None, with_vals: bool = True,
+                  stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Fused indexer over a ragged batch. q [total_q,H,D], k [total_k,D],
+    k_scale [total_k] (fp8 keys), w [total_q,H]; cu_q int32 / cu_k int64 device
+    prefix sums [B+1]; stream b's query t sees its keys s <= S_b - T_b + t.
+    Returns (idx [total_q,topk] int32, stream-local, ascending, -1 padded; vals)."""
+    for name, t in (("q", q), ("k", k), ("w", w), ("cu_q", cu_q), ("cu_k", cu_k)) + \
+            ((("k_scale", k_scale),) if k_scale is not None else ()):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    if cu_q.dtype != torch.int32 or cu_k.dtype != torch.int64:
+        raise ValueError("cu_q must be int32 and cu_k int64")
+    p = make_varlen_problem(q, k, cu_q, cu_k, max_k)
+    if w.dtype != torch.float32 or tuple(w.shape) != (p.total_q, p.H):
+        raise ValueError("w must be float32 [total_q,H]")
+    if idx is None:
+        idx = torch.empty((p.total_q, topk), dtype=torch.int32, device=q.device)
+    if vals is None and with_vals:
+        vals = torch.empty((p.total_q, topk), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = new_varlen_workspace(p, topk, q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().ds4idx_select_varlen(ctypes.byref(p), _ptr(cu_q), _ptr(cu_k), _ptr(q), _ptr(k),
+                                    _ptr(k_scale), _ptr(w), int(topk), _ptr(idx), _ptr(vals),
+                                    _ptr(workspace), ws_bytes, _stream(stream))
+    if st != OK:
+        raise Ds4idxError(st, "ds4idx_select_varlen")
     return idx, vals
 
 

@@ -89,7 +89,8 @@ int route_select(const ds4idx_problem *p, int32_t k)
     const bool shape = ds4idx::mfma_shape_ok(q);
     const int64_t rows = (int64_t)p->B * p->T;
     const bool prefill_ok = shape && k <= ds4idx::kMfmaMaxK && p->B <= 65535;
-    const bool split_ok = shape && rows <= 65535 && ds4idx::split_parts(q) <= ds4idx::kSplitMaxParts;
+    const bool split_ok =
+        shape && rows <= 65535 && ds4idx::split_parts(ds4idx::split_shape(q)) <= ds4idx::kSplitMaxParts;
     const int64_t prefill_blocks = (int64_t)p->B * ((p->T + 7) / 8);
     int mf = R_NONE;
     if (split_ok && (prefill_blocks < 128 || !prefill_ok)) mf = R_SPLIT;
@@ -108,6 +109,39 @@ size_t ref_select_bytes(const ds4idx_problem *p)
 }
 
 int launch_status(hipError_t e) { return e == hipSuccess ? DS4IDX_OK : DS4IDX_ERR_HIP; }
+
+int check_varlen(const ds4idx_varlen_problem *p)
+{
+    if (!p) return DS4IDX_ERR_INVALID_ARG;
+    if (p->B < 1 || p->total_q < 0 || p->total_k < 0 || p->max_k < 1 || p->H < 1 || p->D < 1)
+        return DS4IDX_ERR_INVALID_ARG;
+    if (p->q_dtype != DS4IDX_F32 && p->q_dtype != DS4IDX_BF16) return DS4IDX_ERR_INVALID_ARG;
+    if (p->k_dtype != DS4IDX_F32 && p->k_dtype != DS4IDX_BF16 && p->k_dtype != DS4IDX_FP8_E4M3)
+        return DS4IDX_ERR_INVALID_ARG;
+    return DS4IDX_OK;
+}
+
+ds4idx::VarlenProblem to_internal(const ds4idx_varlen_problem *p)
+{
+    return ds4idx::VarlenProblem{p->B, p->total_q, (long long)p->total_k, p->max_k, p->H, p->D,
+                                 p->q_dtype, p->k_dtype};
+}
+
+// Ragged select: the split-key kernel for few rows (decode batches), the
+// prefill kernel otherwise; only the MFMA shape has ragged kernels.
+int route_varlen(const ds4idx_varlen_problem *p, int32_t k)
+{
+    const ds4idx::VarlenProblem v = to_internal(p);
+    const bool shape = v.H == ds4idx::kMfmaH && v.D == ds4idx::kMfmaD && v.q_dtype == DS4IDX_BF16 &&
+                       (v.k_dtype == DS4IDX_BF16 || v.k_dtype == DS4IDX_FP8_E4M3);
+    if (!shape) return R_NONE;
+    const long long blocks = ds4idx::mfma_varlen_blocks(v.B, v.total_q);
+    const bool prefill_ok = k <= ds4idx::kMfmaMaxK && blocks <= (long long)INT32_MAX;
+    const bool split_ok = v.total_q <= 65535 &&
+                          ds4idx::split_parts(ds4idx::split_shape(v)) <= ds4idx::kSplitMaxParts;
+    if (split_ok && (blocks < 128 || !prefill_ok)) return R_SPLIT;
+    return prefill_ok ? R_PREFILL : R_NONE;
+}
 
 }  // namespace
 
@@ -144,7 +178,7 @@ size_t ds4idx_workspace_bytes(const ds4idx_problem *p, int32_t k, int32_t op)
     if (op != DS4IDX_OP_SELECT || k < 1 || k > DS4IDX_MAX_TOPK) return (size_t)-1;
     const int r = route_select(p, k);
     if (r == R_REF) return ref_select_bytes(p);
-    if (r == R_SPLIT) return ds4idx::split_workspace_bytes(to_internal(p), k);
+    if (r == R_SPLIT) return ds4idx::split_workspace_bytes(ds4idx::split_shape(to_internal(p)), k);
     return 0;
 }
 
@@ -190,7 +224,7 @@ int ds4idx_select(const ds4idx_problem *p, const void *Q, const void *K, const f
     if (r == R_NONE) return DS4IDX_ERR_UNSUPPORTED;
     const Problem q = to_internal(p);
     const size_t need = r == R_REF ? ref_select_bytes(p)
-                        : r == R_SPLIT ? ds4idx::split_workspace_bytes(q, k) : 0;
+                        : r == R_SPLIT ? ds4idx::split_workspace_bytes(ds4idx::split_shape(q), k) : 0;
     if (need > 0 && (!workspace || !aligned(workspace, 256) || ws_bytes < need))
         return DS4IDX_ERR_WORKSPACE;
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -223,6 +257,40 @@ int ds4idx_k_cache_write(const void *K_new, int32_t k_dtype, int64_t n, int32_t 
                                                       reinterpret_cast<const long long *>(slots),
                                                       cache, cache_scale, cache_rows,
                                                       static_cast<hipStream_t>(stream)));
+}
+
+size_t ds4idx_varlen_workspace_bytes(const ds4idx_varlen_problem *p, int32_t k)
+{
+    if (check_varlen(p) != DS4IDX_OK || k < 1 || k > DS4IDX_MAX_TOPK) return (size_t)-1;
+    if (route_varlen(p, k) != R_SPLIT || p->total_q == 0) return 0;
+    return ds4idx::split_workspace_bytes(ds4idx::split_shape(to_internal(p)), k);
+}
+
+int ds4idx_select_varlen(const ds4idx_varlen_problem *p, const int32_t *cu_q, const int64_t *cu_k,
+                         const void *Q, const void *K, const float *K_scale, const float *W, int32_t k,
+                         int32_t *idx, float *vals, void *workspace, size_t ws_bytes, void *stream)
+{
+    int st = check_varlen(p);
+    if (st != DS4IDX_OK) return st;
+    if (k < 1 || k > DS4IDX_MAX_TOPK) return DS4IDX_ERR_INVALID_ARG;
+    if (!cu_q || !cu_k || !aligned(cu_q, 4) || !aligned(cu_k, 8)) return DS4IDX_ERR_INVALID_ARG;
+    if (!Q || !K || !W || !idx || !aligned(Q, 16) || !aligned(K, 16) || !aligned(W, 4) || !aligned(idx, 4) ||
+        (vals && !aligned(vals, 4)))
+        return DS4IDX_ERR_INVALID_ARG;
+    if (p->k_dtype == DS4IDX_FP8_E4M3 && (!K_scale || !aligned(K_scale, 4))) return DS4IDX_ERR_INVALID_ARG;
+    const int r = route_varlen(p, k);
+    if (r == R_NONE) return DS4IDX_ERR_UNSUPPORTED;
+    if (p->total_q == 0) return DS4IDX_OK;
+    const ds4idx::VarlenProblem v = to_internal(p);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    static_assert(sizeof(long long) == sizeof(int64_t), "int64 prefix sums");
+    const long long *ck = reinterpret_cast<const long long *>(cu_k);
+    if (r == R_PREFILL)
+        return launch_status(ds4idx::launch_mfma_select_varlen(v, cu_q, ck, Q, K, K_scale, W, k, idx, vals, s));
+    const size_t need = ds4idx::split_workspace_bytes(ds4idx::split_shape(v), k);
+    if (!workspace || !aligned(workspace, 256) || ws_bytes < need) return DS4IDX_ERR_WORKSPACE;
+    return launch_status(
+        ds4idx::launch_split_select_varlen(v, cu_q, ck, Q, K, K_scale, W, k, idx, vals, workspace, s));
 }
 
 }  // extern "C"

@@ -88,4 +88,85 @@ __device__ __forceinline__ float e4m3_value(uint32_t c)
 
 __device__ __forceinline__ float bf16_value(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
+// Ragged batches: stream b owns query rows cu_q[b] .. cu_q[b+1]-1 and key rows
+// cu_k[b] .. cu_k[b+1]-1 (prefix arrays in device memory). Query t of the
+// stream sees its keys s <= S - T + t: the new tokens are the last T cached.
+// The bounds are clamped to [0, total] and made non-decreasing, so malformed
+// arrays give wrong rows but no access outside the caller's buffers.
+struct Ragged {
+    const int *cu_q;        // [B + 1]
+    const long long *cu_k;  // [B + 1]
+    int B, total_q;
+    long long total_k;
+};
+
+struct StreamGeo {
+    long long q0;  // first query row
+    long long k0;  // first key row
+    int T;         // query rows
+    long long S;   // cached keys
+};
+
+__device__ __forceinline__ StreamGeo stream_geo(const int *cu_q, const long long *cu_k, int b,
+                                                int total_q, long long total_k)
+{
+    auto clampq = [&](int v) { return v < 0 ? 0 : (v > total_q ? total_q : v); };
+    auto clampk = [&](long long v) { return v < 0 ? 0 : (v > total_k ? total_k : v); };
+    const int qa = clampq(cu_q[b]), qb = clampq(cu_q[b + 1]);
+    const long long ka = clampk(cu_k[b]), kb = clampk(cu_k[b + 1]);
+    StreamGeo g;
+    g.q0 = qa;
+    g.T = qb > qa ? qb - qa : 0;
+    g.k0 = ka;
+    g.S = kb > ka ? kb - ka : 0;
+    return g;
+}
+
+// The stream holding query row r (the first whose clamped range holds it), by
+// a wavefront scan of 64 streams per step; -1 if none. Wave-uniform result.
+__device__ __forceinline__ int wave_row_stream(const int *cu_q, const long long *cu_k, int B,
+                                               int total_q, long long total_k, long long r, int lane)
+{
+    for (int c = 0; c < B; c += 64) {
+        const int s = c + lane;
+        bool hit = false;
+        if (s < B) {
+            const StreamGeo g = stream_geo(cu_q, cu_k, s, total_q, total_k);
+            hit = r >= g.q0 && r < g.q0 + g.T;
+        }
+        const uint64_t m = wave_ballot(hit);
+        if (m) return c + __builtin_ctzll(m);
+    }
+    return -1;
+}
+
+// Block x of a grid giving each stream ceil(min(T, S) / tq) blocks, streams in
+// order: returns the stream (-1 past the last block) and sets j, the block's
+// index within the stream. Wave-uniform result.
+__device__ __forceinline__ int wave_block_stream(const int *cu_q, const long long *cu_k, int B,
+                                                 int total_q, long long total_k, int tq, long long x,
+                                                 int lane, int &j)
+{
+    long long base = 0;
+    for (int c = 0; c < B; c += 64) {
+        const int s = c + lane;
+        uint32_t nb = 0;
+        if (s < B) {
+            const StreamGeo g = stream_geo(cu_q, cu_k, s, total_q, total_k);
+            const long long t = (long long)g.T < g.S ? (long long)g.T : g.S;
+            nb = (uint32_t)((t + tq - 1) / tq);
+        }
+        const uint32_t incl = wave_scan_incl(nb, 0u, OpAdd{});
+        const long long lo = base + (long long)(incl - nb), hi = base + (long long)incl;
+        const uint64_t m = wave_ballot(s < B && x >= lo && x < hi);
+        if (m) {
+            const int src = __builtin_ctzll(m);
+            j = (int)(x - base - (long long)(uint32_t)wave_readlane((int)(incl - nb), src));
+            return c + src;
+        }
+        base += wave_total(incl);
+    }
+    return -1;
+}
+
 }  // namespace ds4idx

@@ -16,6 +16,15 @@ struct Problem {
     int q_dtype, k_dtype;
 };
 
+// Ragged batch: B streams packed along the rows of Q/W/idx (cu_q) and of K
+// (cu_k); stream b's query t sees its keys s <= S_b - T_b + t.
+struct VarlenProblem {
+    int B, total_q;
+    long long total_k;
+    int max_k;  // >= every stream's S_b
+    int H, D, q_dtype, k_dtype;
+};
+
 // Plain kernels: any H, D and dtype (the rollback path).
 constexpr int kRefMaxQFloats = 16384;  // H*D + H floats of one query staged in LDS
 hipError_t launch_score_ref(const Problem &p, const void *Q, const void *K, const float *Ks,
@@ -30,6 +39,10 @@ hipError_t launch_mfma_score(const Problem &p, const void *Q, const void *K, con
                              const float *W, float *scores, hipStream_t st);
 hipError_t launch_mfma_select(const Problem &p, const void *Q, const void *K, const float *Ks,
                               const float *W, int k, int *idx, float *vals, hipStream_t st);
+long long mfma_varlen_blocks(int B, int total_q);
+hipError_t launch_mfma_select_varlen(const VarlenProblem &p, const int *cu_q, const long long *cu_k,
+                                     const void *Q, const void *K, const float *Ks, const float *W,
+                                     int k, int *idx, float *vals, hipStream_t st);
 
 // Split-key kernel for few rows over long caches (decode): partitions of 8192
 // keys, each emitting a superset of its top k plus its m-th largest key; the
@@ -41,13 +54,24 @@ struct SplitWorkspace {
     uint64_t *full_list;   // [rows, P, slots] (index << 32 | order key), key 0 = empty slot
     uint64_t *short_list;  // [rows, P, short slots], same format
 };
+// Rows of a split-key launch, the most keys a row sees, and the row length the
+// merge's short lists are sized for (rows with fewer full partitions fall back
+// to the full lists, which for short rows are few).
+struct SplitShape {
+    long long rows, max_len, short_len;
+};
+SplitShape split_shape(const Problem &p);
+SplitShape split_shape(const VarlenProblem &p);
 int split_slots(int k);
-int split_short_slots(const Problem &p, int k);
-int split_parts(const Problem &p);
-size_t split_workspace_bytes(const Problem &p, int k);
-SplitWorkspace split_workspace(void *ws, const Problem &p, int k);
+int split_short_slots(const SplitShape &sh, int k);
+int split_parts(const SplitShape &sh);
+size_t split_workspace_bytes(const SplitShape &sh, int k);
+SplitWorkspace split_workspace(void *ws, const SplitShape &sh, int k);
 hipError_t launch_split_select(const Problem &p, const void *Q, const void *K, const float *Ks,
                                const float *W, int k, int *idx, float *vals, void *ws, hipStream_t st);
+hipError_t launch_split_select_varlen(const VarlenProblem &p, const int *cu_q, const long long *cu_k,
+                                      const void *Q, const void *K, const float *Ks, const float *W, int k,
+                                      int *idx, float *vals, void *ws, hipStream_t st);
 
 // Key-cache writer: per-token E4M3 quantisation, V values on each of G lanes per token.
 int k_cache_lanes(int D, int V);

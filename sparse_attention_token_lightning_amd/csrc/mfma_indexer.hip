@@ -224,20 +224,44 @@ __device__ __forceinline__ void store_tile(Smem &sm, int buf, const TileRegs<KFP
     }
 }
 
-template <bool KFP8, bool SCORE>
+// Ragged batches (VARLEN): the streams of rg (see StreamGeo); the grid's x
+// dimension covers every stream's 8-token blocks, and blocks past the last
+// one exit at once.
+template <bool KFP8, bool SCORE, bool VARLEN>
 __global__ __launch_bounds__(THREADS, 1) void mfma_indexer_kernel(
     const uint16_t *__restrict__ Q, const uint8_t *__restrict__ K, const float *__restrict__ Ks,
     const float *__restrict__ W, int T, int S, long long offset, int topk, int *__restrict__ idx,
-    float *__restrict__ vals, float *__restrict__ scores)
+    float *__restrict__ vals, float *__restrict__ scores, Ragged rg)
 {
     __shared__ Smem sm;
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-    const int nblk = (T + TQ - 1) / TQ;
-    const int t0 = (nblk - 1 - (int)blockIdx.x) * TQ;  // longest rows first
-    const int b = blockIdx.y;
+    // This block's stream: first query row q0, first key row k0, Tb queries
+    // over Sb cached keys, query t seeing keys <= offb + t.
+    long long q0, k0, offb;
+    int Tb, Sb, t0;
+    if constexpr (VARLEN) {
+        int j = 0;
+        const int bs = wave_block_stream(rg.cu_q, rg.cu_k, rg.B, rg.total_q, rg.total_k, TQ, blockIdx.x, lane, j);
+        if (bs < 0) return;  // the same for every wavefront of the block
+        const StreamGeo g = stream_geo(rg.cu_q, rg.cu_k, bs, rg.total_q, rg.total_k);
+        q0 = g.q0;
+        k0 = g.k0;
+        Sb = (int)(g.S < 0x7fffffffLL ? g.S : 0x7fffffffLL);
+        Tb = g.T < Sb ? g.T : Sb;  // rows past the cache (malformed input) are dropped
+        offb = (long long)g.S - g.T;
+        t0 = ((Tb + TQ - 1) / TQ - 1 - j) * TQ;  // longest rows of the stream first
+    } else {
+        const int nblk = (T + TQ - 1) / TQ;
+        t0 = (nblk - 1 - (int)blockIdx.x) * TQ;  // longest rows first
+        q0 = (long long)blockIdx.y * T;
+        k0 = (long long)blockIdx.y * S;
+        Tb = T;
+        Sb = S;
+        offb = offset;
+    }
     const int tok = t0 + wid;
-    const bool tok_ok = tok < T;
-    const long long lim = tok_ok ? offset + tok : -1;  // last key this token sees
+    const bool tok_ok = tok < Tb;
+    const long long lim = tok_ok ? offb + tok : -1;  // last key this token sees
 
     // Query as MFMA A operands: a[m][ks] = Q[tok, head 16m + lane%16,
     // dims 32ks + (lane/16)*8 .. +7]. B operands use the same dim mapping.
@@ -246,7 +270,7 @@ __global__ __launch_bounds__(THREADS, 1) void mfma_indexer_kernel(
     bf16x8 a[4][4];
     float wv[4][4];
     {
-        const long long qrow = ((long long)b * T + (tok_ok ? tok : 0)) * H;
+        const long long qrow = (q0 + (tok_ok ? tok : 0)) * H;
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             const bf16x8 *qp = reinterpret_cast<const bf16x8 *>(
@@ -258,11 +282,11 @@ __global__ __launch_bounds__(THREADS, 1) void mfma_indexer_kernel(
         }
     }
 
-    const long long blk_last = offset + (t0 + TQ < T ? t0 + TQ : T) - 1;  // last key any token sees
-    const long long nkeys = SCORE ? (long long)S : blk_last + 1;
+    const long long blk_last = offb + (t0 + TQ < Tb ? t0 + TQ : Tb) - 1;  // last key any token sees
+    const long long nkeys = SCORE ? (long long)Sb : blk_last + 1;
     const int ntiles = (int)((nkeys + KT - 1) / KT);
-    const uint8_t *Kb = K + (size_t)b * S * (KFP8 ? D : 2 * D);
-    const float *Ksb = KFP8 ? Ks + (size_t)b * S : nullptr;
+    const uint8_t *Kb = K + (size_t)k0 * (KFP8 ? D : 2 * D);
+    const float *Ksb = KFP8 ? Ks + (size_t)k0 : nullptr;
     float *cs = sm.cs[wid];
     int *ci = sm.ci[wid];
     int cnt = 0;
@@ -270,7 +294,7 @@ __global__ __launch_bounds__(THREADS, 1) void mfma_indexer_kernel(
 
     TileRegs<KFP8> tr;
     float tsc;
-    load_tile<KFP8>(tr, tsc, Kb, Ksb, S, 0, tid);
+    load_tile<KFP8>(tr, tsc, Kb, Ksb, Sb, 0, tid);
     store_tile<KFP8>(sm, 0, tr, tsc, tid);
     __syncthreads();
 
@@ -345,7 +369,7 @@ __global__ __launch_bounds__(THREADS, 1) void mfma_indexer_kernel(
         const long long key = pbase + lane;
         const bool vis = key <= lim;
         if (SCORE) {
-            if (tok_ok && key < S) scores[((long long)b * T + tok) * S + key] = vis ? sc : -INFINITY;
+            if (tok_ok && key < Sb) scores[(q0 + tok) * Sb + key] = vis ? sc : -INFINITY;
         } else {
             const bool pass = vis && sc >= thr;
             const uint64_t m = wave_ballot(pass);
@@ -376,7 +400,7 @@ __global__ __launch_bounds__(THREADS, 1) void mfma_indexer_kernel(
     float prev0[2] = {0.0f, 0.0f};  // first half's partial sums of the pair in flight
     for (int tile = 0; tile < ntiles; ++tile) {
         const int cur = tile & 1;
-        if (tile + 1 < ntiles) load_tile<KFP8>(tr, tsc, Kb, Ksb, S, tile + 1, tid);
+        if (tile + 1 < ntiles) load_tile<KFP8>(tr, tsc, Kb, Ksb, Sb, tile + 1, tid);
         const long long kbase = (long long)tile * KT;
 #pragma unroll
         for (int pp = 0; pp < KT / 64; ++pp) {
@@ -412,7 +436,7 @@ __global__ __launch_bounds__(THREADS, 1) void mfma_indexer_kernel(
             wave_keep_topk(cs, ci, cnt, topk, sm.hist[wid], lane);
             cnt = topk;
         }
-        const long long orow = ((long long)b * T + tok) * topk;
+        const long long orow = (q0 + tok) * topk;
         for (int i = lane; i < topk; i += 64) {
             const bool have = i < cnt;
             idx[orow + i] = have ? ci[i] : -1;
@@ -426,9 +450,9 @@ hipError_t launch(const Problem &p, const void *Q, const void *K, const float *K
                   int k, int *idx, float *vals, float *scores, hipStream_t st)
 {
     const int nblk = (p.T + TQ - 1) / TQ;
-    hipLaunchKernelGGL((mfma_indexer_kernel<KFP8, SCORE>), dim3(nblk, p.B), dim3(THREADS), 0, st,
+    hipLaunchKernelGGL((mfma_indexer_kernel<KFP8, SCORE, false>), dim3(nblk, p.B), dim3(THREADS), 0, st,
                        static_cast<const uint16_t *>(Q), static_cast<const uint8_t *>(K), Ks, W, p.T,
-                       p.S, p.offset, k, idx, vals, scores);
+                       p.S, p.offset, k, idx, vals, scores, Ragged{});
     return hipGetLastError();
 }
 
@@ -451,6 +475,26 @@ hipError_t launch_mfma_select(const Problem &p, const void *Q, const void *K, co
 {
     if (p.k_dtype == FP8) return launch<true, false>(p, Q, K, Ks, W, k, idx, vals, nullptr, st);
     return launch<false, false>(p, Q, K, Ks, W, k, idx, vals, nullptr, st);
+}
+
+long long mfma_varlen_blocks(int B, int total_q) { return ((long long)total_q + TQ - 1) / TQ + B; }
+
+hipError_t launch_mfma_select_varlen(const VarlenProblem &p, const int *cu_q, const long long *cu_k,
+                                     const void *Q, const void *K, const float *Ks, const float *W,
+                                     int k, int *idx, float *vals, hipStream_t st)
+{
+    // Every stream's blocks fit in ceil(total_q / 8) + B.
+    const dim3 grid((unsigned)mfma_varlen_blocks(p.B, p.total_q));
+    const Ragged rg{cu_q, cu_k, p.B, p.total_q, p.total_k};
+    const uint16_t *q = static_cast<const uint16_t *>(Q);
+    const uint8_t *kk = static_cast<const uint8_t *>(K);
+    if (p.k_dtype == FP8)
+        hipLaunchKernelGGL((mfma_indexer_kernel<true, false, true>), grid, dim3(THREADS), 0, st, q, kk, Ks, W, 0, 0,
+                           0LL, k, idx, vals, nullptr, rg);
+    else
+        hipLaunchKernelGGL((mfma_indexer_kernel<false, false, true>), grid, dim3(THREADS), 0, st, q, kk, Ks, W, 0,
+                           0, 0LL, k, idx, vals, nullptr, rg);
+    return hipGetLastError();
 }
 
 }  // namespace ds4idx

@@ -424,19 +424,37 @@ __device__ __forceinline__ float score_sub(const Raw<KFP8> &r, const bf16x8 (&a)
     return (s4[0] + s4[1]) + (s4[2] + s4[3]);
 }
 
-template <bool KFP8>
+// Ragged batches (VARLEN): row r belongs to the stream of rg whose query
+// rows hold it (see StreamGeo); rows of no stream see no keys. Every
+// partition of every row still takes part in the arrival, so the counters
+// return to zero.
+template <bool KFP8, bool VARLEN>
 __global__ __launch_bounds__(THREADS, 1) void split_indexer_kernel(
     const uint16_t *__restrict__ Q, const uint8_t *__restrict__ K, const float *__restrict__ Ks,
     const float *__restrict__ W, int T, int S, long long offset, int topk, int P, int slots, int s1,
     uint32_t *__restrict__ ctr, uint64_t *__restrict__ meta, uint64_t *__restrict__ full_list,
-    uint64_t *__restrict__ short_list, int *__restrict__ idx, float *__restrict__ vals)
+    uint64_t *__restrict__ short_list, int *__restrict__ idx, float *__restrict__ vals, Ragged rg)
 {
     __shared__ SplitSmem sm;
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int p = blockIdx.x;
-    const long long r = blockIdx.y;  // b * T + t
-    const int b = (int)(r / T), t = (int)(r % T);
-    const long long L = offset + t + 1;
+    const long long r = blockIdx.y;  // query row
+    long long L, k0;                 // keys this row sees; first key row of its stream
+    if constexpr (VARLEN) {
+        const int bs = wave_row_stream(rg.cu_q, rg.cu_k, rg.B, rg.total_q, rg.total_k, r, lane);
+        L = 0;
+        k0 = 0;
+        if (bs >= 0) {
+            const StreamGeo g = stream_geo(rg.cu_q, rg.cu_k, bs, rg.total_q, rg.total_k);
+            const long long l = g.S - g.T + (r - g.q0) + 1;
+            L = l < 0 ? 0 : l;  // l <= g.S always
+            k0 = g.k0;
+        }
+    } else {
+        const int b = (int)(r / T), t = (int)(r % T);
+        L = offset + t + 1;
+        k0 = (long long)b * S;
+    }
     const long long pbase = (long long)p * PART;
     const long long nvalid = L - pbase < 0 ? 0 : (L - pbase > PART ? PART : L - pbase);
 
@@ -460,8 +478,8 @@ __global__ __launch_bounds__(THREADS, 1) void split_indexer_kernel(
 #pragma unroll
             for (int i = 0; i < 16; ++i) wv[hb][i] = W[r * H + hb * 32 + acc_row(i, lane)];
         }
-        const uint8_t *Kr = K + (size_t)b * S * (KFP8 ? D : 2 * D);
-        const float *Ksr = KFP8 ? Ks + (size_t)b * S : nullptr;
+        const uint8_t *Kr = K + (size_t)k0 * (KFP8 ? D : 2 * D);
+        const float *Ksr = KFP8 ? Ks + (size_t)k0 : nullptr;
         // Sub-blocks of 32 keys; pairs (2j, 2j+1) share one half swap. A ring
         // of NBUF raw sub-blocks keeps NBUF-1 loads in flight.
         constexpr int NBUF = KFP8 ? 4 : 2;
@@ -939,36 +957,41 @@ __global__ __launch_bounds__(THREADS, 1) void split_indexer_kernel(
     if (tid == 0) ctr[r] = 0u;
 }
 
-template <bool KFP8>
-hipError_t launch_t(const Problem &p, const void *Q, const void *K, const float *Ks, const float *W,
-                    int k, int *idx, float *vals, void *ws, hipStream_t st)
+template <bool KFP8, bool VARLEN>
+hipError_t launch_t(const Problem &p, const SplitShape &sh, const Ragged &rg, const void *Q, const void *K,
+                    const float *Ks, const float *W, int k, int *idx, float *vals, void *ws, hipStream_t st)
 {
-    const int rows = p.B * p.T;
-    const int P = split_parts(p);
-    SplitWorkspace w = split_workspace(ws, p, k);
-    hipLaunchKernelGGL((split_indexer_kernel<KFP8>), dim3(P, rows), dim3(THREADS), 0, st,
+    const int P = split_parts(sh);
+    SplitWorkspace w = split_workspace(ws, sh, k);
+    hipLaunchKernelGGL((split_indexer_kernel<KFP8, VARLEN>), dim3(P, (unsigned)sh.rows), dim3(THREADS), 0, st,
                        static_cast<const uint16_t *>(Q), static_cast<const uint8_t *>(K), Ks, W,
-                       p.T, p.S, p.offset, k, P, split_slots(k), split_short_slots(p, k), w.ctr, w.meta,
-                       w.full_list, w.short_list, idx, vals);
+                       p.T, p.S, p.offset, k, P, split_slots(k), split_short_slots(sh, k), w.ctr, w.meta,
+                       w.full_list, w.short_list, idx, vals, rg);
     return hipGetLastError();
 }
 
 }  // namespace
 
-int split_parts(const Problem &p)
+SplitShape split_shape(const Problem &p)
 {
-    const long long maxL = p.offset + p.T;
-    return (int)((maxL + PART - 1) / PART);
+    return SplitShape{(long long)p.B * p.T, p.offset + p.T, p.offset + 1};
 }
+
+SplitShape split_shape(const VarlenProblem &p)
+{
+    return SplitShape{p.total_q, p.max_k, p.max_k};
+}
+
+int split_parts(const SplitShape &sh) { return (int)((sh.max_len + PART - 1) / PART); }
 
 int split_slots(int k) { return (2 * k + 63) / 64 * 64; }
 
-int split_short_slots(const Problem &p, int k)
+int split_short_slots(const SplitShape &sh, int k)
 {
     // Room for the keys from the bin of the c1-th largest up, c1 = 4m (m =
     // ceil(k / full partitions) of the row with the fewest): the kernel takes
     // c1 = slots / 4, so the bin may hold up to 3 c1 further keys.
-    const long long fullp = (p.offset + 1) / PART;
+    const long long fullp = sh.short_len / PART;
     if (fullp < 1) return 64;
     const long long m = (k + fullp - 1) / fullp;
     const long long s = (16 * m + 63) / 64 * 64;
@@ -977,16 +1000,16 @@ int split_short_slots(const Problem &p, int k)
 
 static size_t align256(size_t n) { return (n + 255) / 256 * 256; }
 
-size_t split_workspace_bytes(const Problem &p, int k)
+size_t split_workspace_bytes(const SplitShape &sh, int k)
 {
-    const size_t rows = (size_t)p.B * p.T, P = (size_t)split_parts(p);
+    const size_t rows = (size_t)sh.rows, P = (size_t)split_parts(sh);
     return align256(rows * 4) + align256(rows * P * 16) + align256(rows * P * (size_t)split_slots(k) * 8) +
-           align256(rows * P * (size_t)split_short_slots(p, k) * 8);
+           align256(rows * P * (size_t)split_short_slots(sh, k) * 8);
 }
 
-SplitWorkspace split_workspace(void *ws, const Problem &p, int k)
+SplitWorkspace split_workspace(void *ws, const SplitShape &sh, int k)
 {
-    const size_t rows = (size_t)p.B * p.T, P = (size_t)split_parts(p);
+    const size_t rows = (size_t)sh.rows, P = (size_t)split_parts(sh);
     char *c = static_cast<char *>(ws);
     SplitWorkspace w;
     w.ctr = reinterpret_cast<uint32_t *>(c);
@@ -1002,8 +1025,20 @@ SplitWorkspace split_workspace(void *ws, const Problem &p, int k)
 hipError_t launch_split_select(const Problem &p, const void *Q, const void *K, const float *Ks,
                                const float *W, int k, int *idx, float *vals, void *ws, hipStream_t st)
 {
-    if (p.k_dtype == FP8) return launch_t<true>(p, Q, K, Ks, W, k, idx, vals, ws, st);
-    return launch_t<false>(p, Q, K, Ks, W, k, idx, vals, ws, st);
+    const SplitShape sh = split_shape(p);
+    if (p.k_dtype == FP8) return launch_t<true, false>(p, sh, Ragged{}, Q, K, Ks, W, k, idx, vals, ws, st);
+    return launch_t<false, false>(p, sh, Ragged{}, Q, K, Ks, W, k, idx, vals, ws, st);
+}
+
+hipError_t launch_split_select_varlen(const VarlenProblem &p, const int *cu_q, const long long *cu_k,
+                                      const void *Q, const void *K, const float *Ks, const float *W, int k,
+                                      int *idx, float *vals, void *ws, hipStream_t st)
+{
+    const SplitShape sh = split_shape(p);
+    const Ragged rg{cu_q, cu_k, p.B, p.total_q, p.total_k};
+    const Problem none{};
+    if (p.k_dtype == FP8) return launch_t<true, true>(none, sh, rg, Q, K, Ks, W, k, idx, vals, ws, st);
+    return launch_t<false, true>(none, sh, rg, Q, K, Ks, W, k, idx, vals, ws, st);
 }
 
 }  // namespace ds4idx

@@ -169,3 +169,68 @@ def test_k_cache_write_empty_is_a_no_op():
 def test_k_cache_write_grid_limit():
     st = ds.lib().ds4idx_k_cache_write(FAKE, ds.BF16, 1 << 40, 128, None, FAKE, FAKE, 16, None)
     assert st == ds.ERR_UNSUPPORTED
+
+
+def _vprob(**kw):
+    d = dict(B=3, total_q=10, total_k=1000, max_k=600, H=64, D=128, q_dtype=ds.BF16,
+             k_dtype=ds.FP8_E4M3)
+    d.update(kw)
+    return ds.VarlenProblem(**d)
+
+
+def _vselect(p, **ptrs):
+    a = dict(cu_q=FAKE, cu_k=FAKE, q=FAKE, k=FAKE, ks=FAKE, w=FAKE, idx=FAKE, k_=512)
+    a.update(ptrs)
+    return ds.lib().ds4idx_select_varlen(ctypes.byref(p), a["cu_q"], a["cu_k"], a["q"], a["k"], a["ks"],
+                                         a["w"], a["k_"], a["idx"], None, None, 0, None)
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(total_q=-1), dict(total_k=-1), dict(max_k=0),
+                                dict(H=0), dict(D=0), dict(q_dtype=2), dict(k_dtype=9)])
+def test_varlen_invalid_problem_rejected(kw):
+    p = _vprob(**kw)
+    assert _vselect(p) == ds.ERR_INVALID_ARG
+    assert ds.lib().ds4idx_varlen_workspace_bytes(ctypes.byref(p), 512) == ctypes.c_size_t(-1).value
+
+
+@pytest.mark.parametrize("which", ["cu_q", "cu_k", "q", "k", "ks", "w", "idx"])
+def test_varlen_null_pointers_rejected(which):
+    assert _vselect(_vprob(), **{which: None}) == ds.ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("which", ["cu_k", "q", "k"])
+def test_varlen_misaligned_rejected(which):
+    assert _vselect(_vprob(), **{which: FAKE_MIS}) == ds.ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("k", [0, 2049])
+def test_varlen_bad_k_rejected(k):
+    assert _vselect(_vprob(), k_=k) == ds.ERR_INVALID_ARG
+
+
+def test_varlen_unsupported_shape_and_routing():
+    assert _vselect(_vprob(H=4)) == ds.ERR_UNSUPPORTED
+    assert _vselect(_vprob(q_dtype=ds.F32)) == ds.ERR_UNSUPPORTED
+    # k > 512 needs the split-key kernel, which takes at most 65535 rows
+    assert _vselect(_vprob(total_q=70000), k_=1024) == ds.ERR_UNSUPPORTED
+    # few rows: split-key kernel with a workspace; missing workspace is reported
+    assert _vselect(_vprob()) == ds.ERR_WORKSPACE
+    p = _vprob()
+    n = ds.lib().ds4idx_varlen_workspace_bytes(ctypes.byref(p), 512)
+    assert n > 0 and n % 256 == 0
+    # many rows: the prefill kernel, no workspace
+    p = _vprob(total_q=4096)
+    assert ds.lib().ds4idx_varlen_workspace_bytes(ctypes.byref(p), 512) == 0
+
+
+def test_varlen_empty_batch_is_a_no_op():
+    assert _vselect(_vprob(total_q=0)) == ds.OK
+
+
+def test_varlen_workspace_matches_uniform_decode():
+    # 8 streams of one query over 262144 keys: the same split-key workspace as
+    # the uniform decode problem
+    v = _vprob(B=8, total_q=8, total_k=8 * 262144, max_k=262144)
+    u = ds.Problem(8, 1, 262144, 64, 128, 262143, ds.BF16, ds.FP8_E4M3)
+    assert ds.lib().ds4idx_varlen_workspace_bytes(ctypes.byref(v), 512) == \
+        ds.lib().ds4idx_workspace_bytes(ctypes.byref(u), 512, ds.OP_SELECT)

@@ -1,0 +1,174 @@
+"""GPU parity of ragged batches (ds4idx_select_varlen) through the C ABI:
+every stream against the CPU oracle (bit-exact on integer inputs, within the
+float tolerance otherwise), and against ds4idx_select on the same stream where
+both calls take the same kernel (then bit-exact on any input)."""
+import numpy as np
+import pytest
+import torch
+
+import sparse_attention_token_lightning_amd as ds
+import workloads as W
+from parity import check_invariants, compare_rows, run_select, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _dev(rg: W.Ragged):
+    q = torch.from_numpy(rg.q.view(np.int16)).view(torch.bfloat16).cuda()
+    if rg.k_dtype == W.BF16:
+        k = torch.from_numpy(rg.k.view(np.int16)).view(torch.bfloat16).cuda()
+    else:
+        k = torch.from_numpy(rg.k).cuda()
+    ks = None if rg.k_scale is None else torch.from_numpy(rg.k_scale).cuda()
+    w = torch.from_numpy(rg.w).cuda()
+    return (q, k, ks, w, torch.from_numpy(rg.cu_q).cuda(), torch.from_numpy(rg.cu_k).cuda())
+
+
+def _max_k(rg):
+    return int(np.diff(rg.cu_k).max())
+
+
+def run_varlen(rg: W.Ragged, topk=None, dev=None, workspace=None, poison=True):
+    topk = rg.topk if topk is None else topk
+    q, k, ks, w, cq, ck = dev if dev is not None else _dev(rg)
+    idx = torch.full((q.shape[0], topk), 0x7F7F7F7F, dtype=torch.int32, device="cuda")
+    vals = torch.full((q.shape[0], topk), float("nan"), dtype=torch.float32, device="cuda")
+    if not poison:
+        idx.zero_()
+        vals.zero_()
+    ds.select_varlen(q, k, ks, w, cq, ck, _max_k(rg), topk, idx=idx, vals=vals, workspace=workspace)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), vals.cpu().numpy()
+
+
+def _route_is_split(rg, topk):
+    q, k, _, _, cq, ck = _dev(rg)
+    p = ds.make_varlen_problem(q, k, cq, ck, _max_k(rg))
+    return ds.varlen_workspace_bytes(p, topk) > 0
+
+
+def _rows_for_oracle(T, n=16):
+    if T <= n:
+        return np.arange(T)
+    g = np.random.Generator(np.random.PCG64(T))
+    return np.unique(np.concatenate([[0, T - 1], g.integers(0, T, n - 2)]))
+
+
+def check_against_oracle(rg: W.Ragged, gi, gv, exact: bool, topk=None, n=16):
+    topk = rg.topk if topk is None else topk
+    for b in range(rg.B):
+        wl = rg.stream(b)
+        if wl.T == 0:
+            continue
+        q0 = int(rg.cu_q[b])
+        check_invariants(wl, gi[q0:q0 + wl.T], topk=topk)
+        rows = _rows_for_oracle(wl.T, n)
+        compare_rows(wl, rows, gi[q0 + rows], gv[q0 + rows], exact=exact, topk=topk)
+
+
+def check_against_single_stream_calls(rg: W.Ragged, gi, gv, topk=None):
+    topk = rg.topk if topk is None else topk
+    for b in range(rg.B):
+        wl = rg.stream(b)
+        if wl.T == 0:
+            continue
+        q0 = int(rg.cu_q[b])
+        si, sv = run_select(wl, topk=topk)
+        np.testing.assert_array_equal(gi[q0:q0 + wl.T], si, err_msg=f"stream {b} indices")
+        np.testing.assert_array_equal(gv[q0:q0 + wl.T], sv, err_msg=f"stream {b} values")
+
+
+DECODE_MIX = [(1, 1), (1, 100), (1, 511), (1, 512), (1, 513), (0, 77), (1, 8191), (1, 8192),
+              (1, 8193), (3, 70000), (1, 262144), (1, 300000), (2, 5)]
+PREFILL_MIX = [(700, 700), (1, 20000), (300, 9000), (0, 50), (129, 129), (5, 4099), (17, 60000)]
+
+
+def test_ragged_decode_batch_fp8():
+    # few rows: the split-key kernel. Each stream equals its own ds4idx_select
+    # call (same kernel) bit for bit, and the oracle within tolerance.
+    rg = W.ragged(41, DECODE_MIX)
+    assert _route_is_split(rg, rg.topk)
+    _say(f"ragged decode fp8 seed=41 streams={DECODE_MIX}")
+    gi, gv = run_varlen(rg)
+    check_against_single_stream_calls(rg, gi, gv)
+    check_against_oracle(rg, gi, gv, exact=False)
+
+
+def test_ragged_decode_batch_int_exact():
+    rg = W.ragged(42, DECODE_MIX, kind="int")
+    _say(f"ragged decode int seed=42 streams={DECODE_MIX}")
+    gi, gv = run_varlen(rg)
+    check_against_oracle(rg, gi, gv, exact=True)
+
+
+def test_ragged_decode_k1024():
+    mix = [(1, 300), (1, 1023), (1, 1024), (1, 1025), (2, 50000), (1, 200000)]
+    rg = W.ragged(43, mix, topk=1024)
+    _say(f"ragged decode k=1024 seed=43 streams={mix}")
+    gi, gv = run_varlen(rg, topk=1024)
+    check_against_single_stream_calls(rg, gi, gv, topk=1024)
+    check_against_oracle(rg, gi, gv, exact=False, topk=1024)
+
+
+def test_ragged_prefill_batch_fp8():
+    # many rows: the prefill kernel, streams of every size mixed
+    rg = W.ragged(44, PREFILL_MIX)
+    assert not _route_is_split(rg, rg.topk)
+    _say(f"ragged prefill fp8 seed=44 streams={PREFILL_MIX}")
+    gi, gv = run_varlen(rg)
+    check_against_oracle(rg, gi, gv, exact=False)
+
+
+def test_ragged_prefill_batch_int_exact():
+    rg = W.ragged(45, PREFILL_MIX, kind="int")
+    _say(f"ragged prefill int seed=45 streams={PREFILL_MIX}")
+    gi, gv = run_varlen(rg)
+    check_against_oracle(rg, gi, gv, exact=True, n=64)
+
+
+def test_ragged_prefill_bf16_keys_and_long_streams_match_single_calls():
+    # streams long enough that their own ds4idx_select also takes the prefill
+    # kernel: bit-identical outputs
+    mix = [(1024, 1024), (2048, 6000), (1100, 1100), (0, 10)]
+    rg = W.ragged(46, mix, kind="bf16")
+    _say(f"ragged prefill bf16 seed=46 streams={mix}")
+    gi, gv = run_varlen(rg)
+    check_against_single_stream_calls(rg, gi, gv)
+    check_against_oracle(rg, gi, gv, exact=False)
+
+
+def test_uniform_decode_as_ragged_is_identical():
+    # the 256k decode problem (8 streams x 1 query x 262144 keys) written as a
+    # ragged batch gives the uniform call's outputs bit for bit
+    wl = W.decode()
+    _say("uniform decode 8 x 262144 as a ragged batch")
+    dev = to_device(wl)
+    ui, uv = run_select(wl, dev=dev)
+    q, k, ks, w = dev
+    cq = torch.arange(0, wl.B + 1, dtype=torch.int32, device="cuda")
+    ck = torch.arange(0, wl.B + 1, dtype=torch.int64, device="cuda") * wl.S
+    idx, vals = ds.select_varlen(q.reshape(wl.B, wl.H, wl.D), k.reshape(wl.B * wl.S, wl.D),
+                                 ks.reshape(-1), w.reshape(wl.B, wl.H), cq, ck, wl.S, wl.topk)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(idx.cpu().numpy(), ui)
+    np.testing.assert_array_equal(vals.cpu().numpy(), uv)
+
+
+def test_workspace_reuse_across_ragged_batches():
+    a = W.ragged(47, DECODE_MIX)
+    b = W.ragged(48, [(1, 40000), (2, 9000), (1, 300000), (1, 64)])
+    _say("ragged workspace reuse")
+    da, db = _dev(a), _dev(b)
+    n = max(ds.varlen_workspace_bytes(ds.make_varlen_problem(d[0], d[1], d[4], d[5], _max_k(r)), 512)
+            for r, d in ((a, da), (b, db)))
+    ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    first = run_varlen(a, dev=da, workspace=ws)
+    other = run_varlen(b, dev=db, workspace=ws)
+    again = run_varlen(a, dev=da, workspace=ws)
+    np.testing.assert_array_equal(first[0], again[0])
+    np.testing.assert_array_equal(first[1], again[1])
+    check_against_oracle(b, other[0], other[1], exact=False)

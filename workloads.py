@@ -253,3 +253,67 @@ def new_keys(seed: int = 6, n: int = 8 * 262144, D: int = 128, log_spread: float
     if log_spread > 0:
         x *= np.exp(gs.uniform(-log_spread, log_spread, (n, 1))).astype(np.float32)
     return to_bf16_bits(x) if dtype == BF16 else x
+
+
+# --------------------------------------------------------------------------- ragged batches
+
+@dataclasses.dataclass
+class Ragged:
+    """A ragged batch: streams packed along the rows.
+
+    q [total_q, H, D] bf16 bits; k [total_k, D] E4M3 codes (or bf16 bits /
+    float32); k_scale [total_k] (fp8 only); w [total_q, H]; cu_q int32 and
+    cu_k int64 prefix sums [B + 1]. Stream b's query t sees its keys
+    s <= S_b - T_b + t."""
+    name: str
+    q: np.ndarray
+    k: np.ndarray
+    k_scale: Optional[np.ndarray]
+    w: np.ndarray
+    cu_q: np.ndarray
+    cu_k: np.ndarray
+    H: int
+    D: int
+    topk: int
+    q_dtype: int
+    k_dtype: int
+
+    @property
+    def B(self) -> int:
+        return len(self.cu_q) - 1
+
+    def stream(self, b: int) -> Workload:
+        """Stream b as a single-stream workload (offset S_b - T_b)."""
+        q0, q1 = int(self.cu_q[b]), int(self.cu_q[b + 1])
+        k0, k1 = int(self.cu_k[b]), int(self.cu_k[b + 1])
+        T, S = q1 - q0, k1 - k0
+        ks = None if self.k_scale is None else self.k_scale[k0:k1][None]
+        return Workload(f"{self.name}/{b}", self.q[q0:q1][None], self.k[k0:k1][None], ks,
+                        self.w[q0:q1][None], 1, T, S, self.H, self.D, S - T, self.topk,
+                        self.q_dtype, self.k_dtype, [(0, T, S, S - T)])
+
+
+def ragged(seed: int, streams, H: int = 64, D: int = 128, topk: int = 512, kind: str = "fp8",
+           name: str = "ragged") -> Ragged:
+    """Streams [(T_b, S_b), ...] with the 64k/decode recipe (kind "fp8": Q
+    bf16(N(0,1)), K E4M3 + per-token scale of N(0,1) rows, w N(0,1)/8), bf16
+    keys (kind "bf16"), or integers in [-4, 4] as bf16 with w in {0.5, 1, 2}
+    (kind "int", every fp32 sum exact)."""
+    T = np.array([t for t, _ in streams], dtype=np.int64)
+    S = np.array([s for _, s in streams], dtype=np.int64)
+    cu_q = np.concatenate([[0], np.cumsum(T)]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(S)]).astype(np.int64)
+    tq, tk = int(cu_q[-1]), int(cu_k[-1])
+    gq, gk, gw = _streams(seed, 3)
+    if kind == "int":
+        q = to_bf16_bits(_int_uniform(gq, (tq, H, D), -4, 4))
+        k = to_bf16_bits(_int_uniform(gk, (tk, D), -4, 4))
+        w = _pick_weights(gw, (tq, H))
+        return Ragged(name, q, k, None, w, cu_q, cu_k, H, D, topk, BF16, BF16)
+    q = to_bf16_bits(gq.standard_normal((tq, H, D), dtype=np.float32))
+    w = (gw.standard_normal((tq, H), dtype=np.float32) * np.float32(H ** -0.5)).astype(np.float32)
+    if kind == "bf16":
+        k = to_bf16_bits(gk.standard_normal((tk, D), dtype=np.float32))
+        return Ragged(name, q, k, None, w, cu_q, cu_k, H, D, topk, BF16, BF16)
+    codes, scale = _fp8_cache(gk, 1, tk, D)
+    return Ragged(name, q, codes[0], scale[0], w, cu_q, cu_k, H, D, topk, BF16, FP8)
