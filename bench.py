@@ -13,7 +13,10 @@ latency (8 streams x 1 query x 262144 keys, rotated over 3 copies of the
 inputs so the 256 MB last-level cache cannot hold them), and the CPU oracle
 timed on a bounded sample of the same prefill rows. Also reported: the
 key-cache writer (per-token E4M3 quantisation) filling the whole 256k decode
-cache of 8 streams from bf16 keys, against the HBM peak.
+cache of 8 streams from bf16 keys, against the HBM peak; and two ragged
+batches in one launch each (ds4idx_select_varlen): 64 decode streams whose
+caches span 4096..61426 keys, and a 2048-token chunked-prefill budget spread
+over four streams.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -41,6 +44,7 @@ def _parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-writer", action="store_true")
+    ap.add_argument("--no-ragged", action="store_true")
     ap.add_argument("--writer-iters", type=int, default=20)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, copy 256 MiB once (the reference kernel that "
@@ -200,7 +204,86 @@ def main():
                                 "hbm_frac": round(dbytes / (med * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                                 "traffic": measured_traffic("split_decode_256k_traffic.txt",
                                                             "split_indexer.hip")}
+        # ragged decode: 64 streams, one query each, cache lengths 4096 + 910 b
+        # keys, packed from the same rotated bytes
+        if not args.no_ragged:
+            lens = 4096 + 910 * np.arange(64, dtype=np.int64)
+            cu_k = torch.from_numpy(np.concatenate([[0], np.cumsum(lens)])).to(dev)
+            cu_q = torch.arange(0, 65, dtype=torch.int32, device=dev)
+            rq = q[0, :64].contiguous()
+            rw = w[0, :64].contiguous()
+            nk = int(lens.sum())
+            rsets = [(rq, a[1].reshape(-1, dl.D)[:nk], a[2].reshape(-1)[:nk]) for a in sets]
+            rp = ds.make_varlen_problem(rq, rsets[0][1], cu_q, cu_k, int(lens.max()))
+            rws = ds.new_varlen_workspace(rp, dl.topk, dev)
+            ridx = torch.empty((64, dl.topk), dtype=torch.int32, device=dev)
+            rvals = torch.empty((64, dl.topk), dtype=torch.float32, device=dev)
+
+            def rstep(i):
+                a = rsets[i % 3]
+                ds.select_varlen(rq, a[1], a[2], rw, cu_q, cu_k, int(lens.max()), dl.topk, idx=ridx,
+                                 vals=rvals, workspace=rws, stream=stream)
+
+            for i in range(6):
+                rstep(i)
+            torch.cuda.synchronize()
+            rev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
+                   for _ in range(args.decode_iters)]
+            for i in range(args.decode_iters):
+                rev[i][0].record(stream)
+                rstep(i)
+                rev[i][1].record(stream)
+            torch.cuda.synchronize()
+            rus = sorted(e[0].elapsed_time(e[1]) * 1e3 for e in rev)
+            rbytes = int(lens.sum()) * (dl.D + 4) + 64 * (dl.H * dl.D * 2 + dl.H * 4) + 64 * dl.topk * 8
+            rmed = rus[len(rus) // 2]
+            extra["ragged_decode_64"] = {
+                "workload": "64 streams x 1 query, caches of 4096 + 910 b keys (2,096,704 in all), "
+                            "H=64, D=128, top-512, E4M3 K, one ds4idx_select_varlen call",
+                "us_median": round(rmed, 2), "us_min": round(rus[0], 2), "alg_bytes": rbytes,
+                "GB_s": round(rbytes / (rmed * 1e-6) / 1e9, 1),
+                "hbm_frac": round(rbytes / (rmed * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
         del sets
+
+    # ---------------------------------------------------------------- ragged prefill
+    # A 2048-token chunked-prefill budget over four streams (1024, 512, 256 and
+    # 256 new tokens on caches of 32768, 16384, 8192 and 8192 keys), packed
+    # from the 64k workload's first 2048 queries and its 65536 cached keys.
+    if not args.no_ragged:
+        Tq = np.array([1024, 512, 256, 256])
+        Sk = np.array([32768, 16384, 8192, 8192])
+        pcu_q = torch.from_numpy(np.concatenate([[0], np.cumsum(Tq)]).astype(np.int32)).to(dev)
+        pcu_k = torch.from_numpy(np.concatenate([[0], np.cumsum(Sk)]).astype(np.int64)).to(dev)
+        pq = q[0, :2048].contiguous()
+        pw = w[0, :2048].contiguous()
+        pk, pks = k[0], ks[0]
+        pidx = torch.empty((2048, wl.topk), dtype=torch.int32, device=dev)
+        pvals = torch.empty((2048, wl.topk), dtype=torch.float32, device=dev)
+
+        def pstep():
+            ds.select_varlen(pq, pk, pks, pw, pcu_q, pcu_k, int(Sk.max()), wl.topk, idx=pidx,
+                             vals=pvals, stream=stream)
+
+        for _ in range(3):
+            pstep()
+        torch.cuda.synchronize()
+        pev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(20)]
+        for e in pev:
+            e[0].record(stream)
+            pstep()
+            e[1].record(stream)
+        torch.cuda.synchronize()
+        pus = sorted(e[0].elapsed_time(e[1]) * 1e3 for e in pev)
+        pairs_r = int(sum(t * (s_ - t) + t * (t + 1) // 2 for t, s_ in zip(Tq, Sk)))
+        pflop = 2 * wl.H * wl.D * pairs_r
+        pmed = pus[len(pus) // 2]
+        extra["ragged_prefill_2048"] = {
+            "workload": "4 streams: 1024/512/256/256 new tokens on caches of 32768/16384/8192/8192 "
+                        "keys, H=64, D=128, top-512, E4M3 K, one ds4idx_select_varlen call",
+            "us_median": round(pmed, 2), "us_min": round(pus[0], 2),
+            "query_tok_s": round(2048 / (pmed * 1e-6), 1), "flop": pflop,
+            "tflops": round(pflop / (pmed * 1e-6) / 1e12, 1),
+            "mfma_frac": round(pflop / (pmed * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4)}
 
     # ---------------------------------------------------------------- key-cache writer
     if not args.no_writer:

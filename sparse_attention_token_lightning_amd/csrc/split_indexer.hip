@@ -437,9 +437,23 @@ __global__ __launch_bounds__(THREADS, 1) void split_indexer_kernel(
 {
     __shared__ SplitSmem sm;
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-    const int p = blockIdx.x;
-    const long long r = blockIdx.y;  // query row
-    long long L, k0;                 // keys this row sees; first key row of its stream
+    // Ragged rows differ in length, so their later partitions are often
+    // partial or empty. Blocks are taken partition-major there (every row's
+    // partition 0, then every row's partition 1, ...): the full partitions
+    // dispatch first, spread over the XCDs (consecutive blocks go to
+    // consecutive XCDs), and the short ones fill the gaps. Uniform rows keep
+    // the plain mapping.
+    int p;
+    long long r;  // query row
+    if constexpr (VARLEN) {
+        const long long i = blockIdx.x + (long long)P * blockIdx.y;
+        p = (int)(i / gridDim.y);
+        r = i % gridDim.y;
+    } else {
+        p = blockIdx.x;
+        r = blockIdx.y;
+    }
+    long long L, k0;  // keys this row sees; first key row of its stream
     if constexpr (VARLEN) {
         const int bs = wave_row_stream(rg.cu_q, rg.cu_k, rg.B, rg.total_q, rg.total_k, r, lane);
         L = 0;
