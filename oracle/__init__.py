@@ -5,8 +5,10 @@ CPU-baseline leg may import this package. It shares no code with the HIP
 library; the two meet only in the seeded inputs of ``workloads``.
 
 The arithmetic lives in ``ds4idx_oracle.c`` (plain C, fp64, OpenMP over rows
-and key blocks) and ``ds4idx_kcache_oracle.c`` (the key-cache writer's E4M3
-quantisation); this wrapper only builds them with gcc and marshals arrays.
+and key blocks), ``ds4idx_kcache_oracle.c`` (the key-cache writer's E4M3
+quantisation) and ``ds4idx_attn_oracle.c`` (sparse attention over the
+selected positions); this wrapper only builds them with gcc and marshals
+arrays.
 """
 from __future__ import annotations
 
@@ -17,7 +19,8 @@ import subprocess
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SRCS = [os.path.join(_HERE, "ds4idx_oracle.c"), os.path.join(_HERE, "ds4idx_kcache_oracle.c")]
+_SRCS = [os.path.join(_HERE, "ds4idx_oracle.c"), os.path.join(_HERE, "ds4idx_kcache_oracle.c"),
+         os.path.join(_HERE, "ds4idx_attn_oracle.c")]
 _LIB = os.path.join(_HERE, "libds4idx_oracle.so")
 _lib = None
 
@@ -52,6 +55,9 @@ def _load():
         lib.ds4o_e4m3_encode.restype = i
         lib.ds4o_quantize_k.argtypes = [p, i, i64, i, p, p]
         lib.ds4o_quantize_k.restype = i
+        lib.ds4o_sparse_attention.argtypes = [p, p, p, i, i, i, i, i, i, i, ctypes.c_double,
+                                              p, i, p, p, i]
+        lib.ds4o_sparse_attention.restype = i
         _lib = lib
     return _lib
 
@@ -84,6 +90,32 @@ def quantize_k(k: np.ndarray, dtype: int):
     if _load().ds4o_quantize_k(_ptr(k), int(dtype), n, D, _ptr(codes), _ptr(scale)) != 0:
         raise ValueError("oracle rejected the quantisation arguments")
     return codes, scale
+
+
+def sparse_attention(q_bits, c_bits, idx, softmax_scale: float, d_v: int, rows=None,
+                     nthreads: int = 0):
+    """Sparse attention of the selected positions.
+
+    q_bits [B,T,H,d_qk] and c_bits [B,S,d_qk] uint16 bf16 patterns, idx
+    [B,T,k] int32 (entries outside [0,S) skipped). Returns (out float64
+    [n,H,d_v], lse float64 [n,H]) for the flat rows b*T + t listed in rows
+    (all rows by default)."""
+    q = np.ascontiguousarray(q_bits, dtype=np.uint16)
+    c = np.ascontiguousarray(c_bits, dtype=np.uint16)
+    ix = np.ascontiguousarray(idx, dtype=np.int32)
+    B, T, H, dqk = q.shape
+    S = c.shape[1]
+    k = ix.shape[2]
+    rows = np.arange(B * T, dtype=np.int64) if rows is None else \
+        np.ascontiguousarray(rows, dtype=np.int64)
+    out = np.empty((len(rows), H, d_v), dtype=np.float64)
+    lse = np.empty((len(rows), H), dtype=np.float64)
+    used = _load().ds4o_sparse_attention(_ptr(q), _ptr(c), _ptr(ix), B, T, S, H, k, dqk, d_v,
+                                         float(softmax_scale), _ptr(rows), len(rows), _ptr(out),
+                                         _ptr(lse), nthreads)
+    if used < 0:
+        raise ValueError("oracle rejected the attention shape")
+    return out, lse
 
 
 def _problem_args(wl):
