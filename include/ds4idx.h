@@ -170,6 +170,39 @@ int ds4idx_select_varlen(const ds4idx_varlen_problem *p, const int32_t *cu_q, co
                          int32_t k, int32_t *idx, float *vals, void *workspace, size_t ws_bytes,
                          void *stream);
 
+/* Sparse attention over the selected positions, the step downstream of the
+ * indexer: each query token attends only to the cache rows its idx row names
+ * (first page, glossary entry on sparse attention). The MI300X write-up keeps
+ * an MLA cache (fp8_ds_mla) and tiles the sparse prefill 64 heads at a time
+ * (BLOCK_H=64 in its production tuning table); it prints no formula. Here
+ * each cache row is one shared latent vector: the whole row (d_qk values) is
+ * the key of every head and its first d_v values the value:
+ *
+ *     z_j        = softmax_scale * sum_d Q[b,t,h,d] * KV[b, idx_j, d]
+ *     O[b,t,h,:] = sum_j exp(z_j) KV[b, idx_j, 0:d_v] / sum_j exp(z_j)
+ *     lse[b,t,h] = log(sum_j exp(z_j))           (natural log)
+ *
+ * over the entries j of idx[b,t,:] with 0 <= idx < S; -1 padding (as
+ * ds4idx_select emits) and other out-of-range entries are skipped, and a
+ * token with none gets O = 0 and lse = -inf.
+ *   Q    [B, T, H, d_qk] bf16, 16-byte aligned
+ *   KV   [B, S, d_qk]    bf16, 16-byte aligned
+ *   idx  [B, T, topk]    int32 (e.g. ds4idx_select's output)
+ *   O    [B, T, H, d_v]  bf16, 16-byte aligned
+ *   lse  [B, T, H]       fp32, may be NULL
+ * Probabilities enter the value sum rounded to bf16 (accumulation in fp32).
+ * The kernel covers d_qk = 576, d_v = 512 (a 512-value latent plus a
+ * 64-value positional part) and H a multiple of 64; other shapes return
+ * DS4IDX_ERR_UNSUPPORTED. 1 <= topk <= DS4IDX_MAX_TOPK. */
+typedef struct {
+    int32_t B, T, S, H, topk;
+    int32_t d_qk, d_v;
+    float softmax_scale;
+} ds4idx_attn_problem;
+
+int ds4idx_sparse_attention(const ds4idx_attn_problem *p, const void *Q, const void *KV,
+                            const int32_t *idx, void *O, float *lse, void *stream);
+
 /* Key-cache writer, the step upstream of the scorer: quantises n new key
  * vectors to OCP E4M3FN codes with one fp32 scale per token and stores them in
  * rows of the key cache that ds4idx_select reads as K and K_scale. The pages

@@ -36,7 +36,8 @@ ABI_VERSION = 1
 # Every symbol include/ds4idx.h declares.
 EXPORTS = ("ds4idx_abi_version", "ds4idx_status_string", "ds4idx_set_impl", "ds4idx_get_impl",
            "ds4idx_workspace_bytes", "ds4idx_score", "ds4idx_topk", "ds4idx_select",
-           "ds4idx_k_cache_write", "ds4idx_varlen_workspace_bytes", "ds4idx_select_varlen")
+           "ds4idx_k_cache_write", "ds4idx_varlen_workspace_bytes", "ds4idx_select_varlen",
+           "ds4idx_sparse_attention")
 
 
 class Problem(ctypes.Structure):
@@ -49,6 +50,12 @@ class VarlenProblem(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("total_q", ctypes.c_int32), ("total_k", ctypes.c_int64),
                 ("max_k", ctypes.c_int32), ("H", ctypes.c_int32),
                 ("D", ctypes.c_int32), ("q_dtype", ctypes.c_int32), ("k_dtype", ctypes.c_int32)]
+
+
+class AttnProblem(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("T", ctypes.c_int32), ("S", ctypes.c_int32), ("H", ctypes.c_int32),
+                ("topk", ctypes.c_int32), ("d_qk", ctypes.c_int32), ("d_v", ctypes.c_int32),
+                ("softmax_scale", ctypes.c_float)]
 
 
 class Ds4idxError(RuntimeError):
@@ -93,6 +100,8 @@ def lib() -> ctypes.CDLL:
         L.ds4idx_varlen_workspace_bytes.restype = sz
         L.ds4idx_select_varlen.argtypes = [VP, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, sz, vp]
         L.ds4idx_select_varlen.restype = ctypes.c_int
+        L.ds4idx_sparse_attention.argtypes = [ctypes.POINTER(AttnProblem), vp, vp, vp, vp, vp, vp]
+        L.ds4idx_sparse_attention.restype = ctypes.c_int
         if L.ds4idx_abi_version() != ABI_VERSION:
             raise RuntimeError("libds4idx ABI version mismatch; rebuild the library")
         _lib = L
@@ -282,6 +291,35 @@ def select_varlen(q, k, k_scale, w, cu_q, cu_k, max_k: int, topk: int = 512,
     if st != OK:
         raise Ds4idxError(st, "ds4idx_select_varlen")
     return idx, vals
+
+
+def sparse_attention(q: torch.Tensor, kv: torch.Tensor, idx: torch.Tensor, softmax_scale: float,
+                     d_v: int = 512, out: Optional[torch.Tensor] = None, with_lse: bool = True,
+                     stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Attention of each query token over its selected cache rows.
+
+    q [B,T,H,d_qk] bf16, kv [B,S,d_qk] bf16 (key = whole row, value = first
+    d_v columns), idx [B,T,k] int32 (-1 padding skipped). Returns
+    (out [B,T,H,d_v] bf16, lse [B,T,H] fp32 or None)."""
+    if q.dim() != 4 or kv.dim() != 3 or idx.dim() != 3:
+        raise ValueError("q must be [B,T,H,d_qk], kv [B,S,d_qk] and idx [B,T,k]")
+    B, T, H, dqk = q.shape
+    if kv.shape[0] != B or kv.shape[2] != dqk or tuple(idx.shape[:2]) != (B, T):
+        raise ValueError("q, kv and idx shapes do not match")
+    if q.dtype != torch.bfloat16 or kv.dtype != torch.bfloat16 or idx.dtype != torch.int32:
+        raise ValueError("q and kv must be bfloat16, idx int32")
+    for name, t in (("q", q), ("kv", kv), ("idx", idx)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    if out is None:
+        out = torch.empty((B, T, H, d_v), dtype=torch.bfloat16, device=q.device)
+    lse = torch.empty((B, T, H), dtype=torch.float32, device=q.device) if with_lse else None
+    p = AttnProblem(B, T, kv.shape[1], H, idx.shape[2], dqk, int(d_v), float(softmax_scale))
+    st = lib().ds4idx_sparse_attention(ctypes.byref(p), _ptr(q), _ptr(kv), _ptr(idx), _ptr(out), _ptr(lse),
+                                       _stream(stream))
+    if st != OK:
+        raise Ds4idxError(st, "ds4idx_sparse_attention")
+    return out, lse
 
 
 def k_cache_write(k_new: torch.Tensor, cache: torch.Tensor, cache_scale: torch.Tensor,

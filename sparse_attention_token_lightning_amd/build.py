@@ -17,7 +17,8 @@ LIB = os.path.join(PKG, "libds4idx.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "ref_kernels.hip", "mfma_indexer.hip", "split_indexer.hip", "k_cache_writer.hip"]
+SOURCES = ["api.cpp", "ref_kernels.hip", "mfma_indexer.hip", "split_indexer.hip", "k_cache_writer.hip",
+           "sparse_attention.hip"]
 HEADERS = ["kernels.h", "device_common.h"]
 
 # Packed fp32 VALU forms are kept out of generated code on this target.

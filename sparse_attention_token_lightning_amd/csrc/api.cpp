@@ -4,6 +4,7 @@
 #include "ds4idx.h"
 
 #include <atomic>
+#include <cmath>
 #include <cstdlib>
 #include <cstring>
 
@@ -291,6 +292,22 @@ int ds4idx_select_varlen(const ds4idx_varlen_problem *p, const int32_t *cu_q, co
     if (!workspace || !aligned(workspace, 256) || ws_bytes < need) return DS4IDX_ERR_WORKSPACE;
     return launch_status(
         ds4idx::launch_split_select_varlen(v, cu_q, ck, Q, K, K_scale, W, k, idx, vals, workspace, s));
+}
+
+int ds4idx_sparse_attention(const ds4idx_attn_problem *p, const void *Q, const void *KV,
+                            const int32_t *idx, void *O, float *lse, void *stream)
+{
+    if (!p || p->B < 1 || p->T < 1 || p->S < 1 || p->H < 1 || p->topk < 1 || p->topk > DS4IDX_MAX_TOPK ||
+        p->d_qk < 1 || p->d_v < 1 || p->d_v > p->d_qk || !std::isfinite(p->softmax_scale))
+        return DS4IDX_ERR_INVALID_ARG;
+    if (!Q || !KV || !idx || !O || !aligned(Q, 16) || !aligned(KV, 16) || !aligned(O, 16) || !aligned(idx, 4) ||
+        (lse && !aligned(lse, 4)))
+        return DS4IDX_ERR_INVALID_ARG;
+    if (p->d_qk != ds4idx::kAttnDqk || p->d_v != ds4idx::kAttnDv || p->H % ds4idx::kAttnHeadTile != 0 ||
+        p->H / ds4idx::kAttnHeadTile > 65535 || (int64_t)p->B * p->T > (int64_t)INT32_MAX)
+        return DS4IDX_ERR_UNSUPPORTED;
+    const ds4idx::AttnProblem a{p->B, p->T, p->S, p->H, p->topk, p->softmax_scale};
+    return launch_status(ds4idx::launch_sparse_attention(a, Q, KV, idx, O, lse, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

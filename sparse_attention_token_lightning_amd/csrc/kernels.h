@@ -73,6 +73,16 @@ hipError_t launch_split_select_varlen(const VarlenProblem &p, const int *cu_q, c
                                       const void *Q, const void *K, const float *Ks, const float *W, int k,
                                       int *idx, float *vals, void *ws, hipStream_t st);
 
+// Sparse attention over selected positions of a shared latent cache: the key
+// is the whole row (576 values), the value its first 512; heads in tiles of 64.
+constexpr int kAttnHeadTile = 64, kAttnDqk = 576, kAttnDv = 512;
+struct AttnProblem {
+    int B, T, S, H, topk;
+    float softmax_scale;
+};
+hipError_t launch_sparse_attention(const AttnProblem &p, const void *Q, const void *KV, const int *idx, void *O,
+                                   float *lse, hipStream_t st);
+
 // Key-cache writer: per-token E4M3 quantisation, V values on each of G lanes per token.
 int k_cache_lanes(int D, int V);
 int k_cache_vals_per_lane(int D, const void *cache);

@@ -234,3 +234,34 @@ def test_varlen_workspace_matches_uniform_decode():
     u = ds.Problem(8, 1, 262144, 64, 128, 262143, ds.BF16, ds.FP8_E4M3)
     assert ds.lib().ds4idx_varlen_workspace_bytes(ctypes.byref(v), 512) == \
         ds.lib().ds4idx_workspace_bytes(ctypes.byref(u), 512, ds.OP_SELECT)
+
+
+def _aprob(**kw):
+    d = dict(B=1, T=4, S=100, H=64, topk=512, d_qk=576, d_v=512, softmax_scale=0.04)
+    d.update(kw)
+    return ds.AttnProblem(**d)
+
+
+def _attn(p, **ptrs):
+    a = dict(q=FAKE, kv=FAKE, idx=FAKE, o=FAKE, lse=None)
+    a.update(ptrs)
+    return ds.lib().ds4idx_sparse_attention(ctypes.byref(p), a["q"], a["kv"], a["idx"], a["o"], a["lse"], None)
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(T=0), dict(S=0), dict(H=0), dict(topk=0), dict(topk=2049),
+                                dict(d_qk=0), dict(d_v=600), dict(softmax_scale=float("nan")),
+                                dict(softmax_scale=float("inf"))])
+def test_attention_invalid_problem_rejected(kw):
+    assert _attn(_aprob(**kw)) == ds.ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("which", ["q", "kv", "idx", "o"])
+def test_attention_null_or_misaligned_rejected(which):
+    assert _attn(_aprob(), **{which: None}) == ds.ERR_INVALID_ARG
+    if which != "idx":
+        assert _attn(_aprob(), **{which: FAKE_MIS}) == ds.ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw", [dict(H=32), dict(H=96), dict(d_qk=512), dict(d_v=256)])
+def test_attention_unsupported_shapes(kw):
+    assert _attn(_aprob(**kw)) == ds.ERR_UNSUPPORTED

@@ -1,0 +1,116 @@
+"""GPU parity of sparse attention (ds4idx_sparse_attention) through the C ABI
+against the CPU oracle.
+
+Tolerance, from the arithmetic: the probabilities enter the value sum as bf16
+(relative error <= 2^-9 each, so the weighted mean moves by <= 2^-9 of the
+largest selected value), and the output is rounded to bf16 (2^-9 relative);
+scores and sums are fp32. Allowed: |out - ref| <= 2^-8 (max_j |v_j| + |ref|);
+lse within 2e-5 + 1e-5 |lse|."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_attention_token_lightning_amd as ds
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _bf16_dev(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def run_attention(a: W.AttnInputs):
+    o, lse = ds.sparse_attention(_bf16_dev(a.q), _bf16_dev(a.kv), torch.from_numpy(a.idx).cuda(),
+                                 a.softmax_scale, a.d_v)
+    torch.cuda.synchronize()
+    B, T, H, _ = a.q.shape
+    o = o.float().cpu().numpy().reshape(B * T, H, a.d_v)
+    return o, lse.cpu().numpy().reshape(B * T, H)
+
+
+def check(a: W.AttnInputs, go, glse, rows=None):
+    B, T, H, _ = a.q.shape
+    rows = np.arange(B * T) if rows is None else np.asarray(rows)
+    ro, rl = oracle.sparse_attention(a.q, a.kv, a.idx, a.softmax_scale, a.d_v, rows=rows)
+    kvf = W.bf16_bits_to_f32(a.kv).astype(np.float64)
+    S = a.kv.shape[1]
+    for n, r in enumerate(rows):
+        b = r // T
+        sel = a.idx.reshape(B * T, -1)[r]
+        sel = sel[(sel >= 0) & (sel < S)]
+        vmax = np.abs(kvf[b, sel, :a.d_v]).max() if len(sel) else 0.0
+        tol = 2.0 ** -8 * (vmax + np.abs(ro[n]))
+        err = np.abs(go[r] - ro[n])
+        assert np.all(err <= tol), f"row {r}: max error {err.max()} (worst head {np.unravel_index(np.argmax(err - tol), err.shape)})"
+        if len(sel) == 0:
+            assert np.all(np.isneginf(glse[r])) and np.all(go[r] == 0)
+        else:
+            np.testing.assert_allclose(glse[r], rl[n], rtol=1e-5, atol=2e-5, err_msg=f"row {r} lse")
+
+
+@pytest.mark.parametrize("seed,B,T,S,H,k,pad", [(11, 2, 5, 700, 64, 64, 0.0), (12, 1, 16, 4096, 128, 512, 0.0),
+                                                (13, 1, 9, 300, 64, 100, 0.3), (14, 3, 2, 50, 64, 33, 0.0),
+                                                (15, 1, 4, 2000, 192, 256, 0.1)])
+def test_random_rows(seed, B, T, S, H, k, pad):
+    a = W.attention(seed=seed, B=B, T=T, S=S, H=H, topk=k, pad_frac=pad)
+    _say(f"sparse attention seed={seed} B={B} T={T} S={S} H={H} k={k} pad={pad}")
+    go, glse = run_attention(a)
+    check(a, go, glse)
+
+
+def test_peaked_scores():
+    # a large scale makes the softmax nearly one-hot: the max subtraction and
+    # the online rescaling carry the whole result
+    a = W.attention(seed=16, T=8, S=3000, topk=512, softmax_scale=0.35)
+    _say("sparse attention peaked scale=0.35")
+    go, glse = run_attention(a)
+    check(a, go, glse)
+
+
+def test_edge_rows():
+    # no valid entry; one valid entry (out is that row's values exactly);
+    # out-of-range entries; duplicates of the same position
+    a = W.attention(seed=17, T=4, S=200, topk=40)
+    a.idx[0, 0, :] = -1
+    a.idx[0, 1, :] = -1
+    a.idx[0, 1, 17] = 123
+    a.idx[0, 2, ::3] = 200
+    a.idx[0, 2, 1::5] = -9
+    a.idx[0, 3, :10] = 77
+    _say("sparse attention edge rows")
+    go, glse = run_attention(a)
+    check(a, go, glse)
+    assert np.all(go[0] == 0) and np.all(np.isneginf(glse[0]))
+    v = W.bf16_bits_to_f32(a.kv)[0, 123, :512]
+    assert np.array_equal(go[1], np.broadcast_to(v, go[1].shape))
+
+
+def test_indexer_output_feeds_attention():
+    # the indexer's selection over a bf16 cache (its first 128 dims as the
+    # indexer keys) drives the attention; both checked against the oracle
+    B, T, S, H = 1, 64, 4096, 64
+    wl = W.prefill_bf16(seed=18, T=T, S=S, offset=S - T)
+    from parity import run_select
+    gi, _ = run_select(wl)
+    a = W.attention(seed=19, B=B, T=T, S=S, H=H, topk=512)
+    a.idx[:] = gi.reshape(B, T, 512)
+    _say("indexer selection feeding sparse attention")
+    go, glse = run_attention(a)
+    check(a, go, glse)
+
+
+def test_prefill_chunk_full_size_sampled():
+    # one 4096-query chunk of a long prefill: 4096 tokens x 64 heads attending
+    # to 512 of 65536 cached rows; 24 sampled rows checked
+    a = W.attention(seed=20, T=4096, S=65536, H=64, topk=512)
+    _say("sparse attention T=4096 S=65536 H=64 k=512")
+    go, glse = run_attention(a)
+    g = np.random.Generator(np.random.PCG64(21))
+    rows = np.unique(np.concatenate([[0, 4095], g.integers(0, 4096, 22)]))
+    check(a, go, glse, rows=rows)

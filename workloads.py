@@ -317,3 +317,40 @@ def ragged(seed: int, streams, H: int = 64, D: int = 128, topk: int = 512, kind:
         return Ragged(name, q, k, None, w, cu_q, cu_k, H, D, topk, BF16, BF16)
     codes, scale = _fp8_cache(gk, 1, tk, D)
     return Ragged(name, q, codes[0], scale[0], w, cu_q, cu_k, H, D, topk, BF16, FP8)
+
+
+# --------------------------------------------------------------------------- sparse attention
+
+@dataclasses.dataclass
+class AttnInputs:
+    """Sparse attention inputs: q [B,T,H,d_qk] and kv [B,S,d_qk] bf16 bits,
+    idx [B,T,k] int32 (ascending selected positions, -1 padded)."""
+    q: np.ndarray
+    kv: np.ndarray
+    idx: np.ndarray
+    softmax_scale: float
+    d_v: int
+
+
+def attention(seed: int = 9, B: int = 1, T: int = 64, S: int = 4096, H: int = 64, topk: int = 512,
+              d_qk: int = 576, d_v: int = 512, softmax_scale: Optional[float] = None,
+              pad_frac: float = 0.0, causal_offset: Optional[int] = None) -> AttnInputs:
+    """q, kv = bf16(N(0,1)); idx row t picks min(k, L) distinct positions
+    uniformly from the L = offset + t + 1 visible ones (offset = S - T by
+    default), ascending, -1 padded, then a fraction pad_frac of entries is
+    replaced by -1. The default scale is d_qk^-1/2."""
+    gq, gc, gi = _streams(seed, 3)
+    q = to_bf16_bits(gq.standard_normal((B, T, H, d_qk), dtype=np.float32))
+    kv = to_bf16_bits(gc.standard_normal((B, S, d_qk), dtype=np.float32))
+    off = S - T if causal_offset is None else causal_offset
+    idx = np.full((B, T, topk), -1, np.int32)
+    for b in range(B):
+        for t in range(T):
+            L = off + t + 1
+            n = min(topk, L)
+            sel = np.sort(gi.choice(L, n, replace=False)) if L > n else np.arange(L)
+            idx[b, t, :n] = sel
+    if pad_frac > 0:
+        idx[gi.random(idx.shape) < pad_frac] = -1
+    scale = d_qk ** -0.5 if softmax_scale is None else softmax_scale
+    return AttnInputs(q, kv, idx, float(scale), d_v)
