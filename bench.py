@@ -16,7 +16,9 @@ key-cache writer (per-token E4M3 quantisation) filling the whole 256k decode
 cache of 8 streams from bf16 keys, against the HBM peak; and two ragged
 batches in one launch each (ds4idx_select_varlen): 64 decode streams whose
 caches span 4096..61426 keys, and a 2048-token chunked-prefill budget spread
-over four streams.
+over four streams; and sparse attention (ds4idx_sparse_attention) of one
+4096-query prefill chunk over 512 selected rows of a 65536-row latent cache,
+64 heads, against the bf16 MFMA peak.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -45,6 +47,8 @@ def _parse():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-writer", action="store_true")
     ap.add_argument("--no-ragged", action="store_true")
+    ap.add_argument("--no-attention", action="store_true")
+    ap.add_argument("--attention-iters", type=int, default=10)
     ap.add_argument("--writer-iters", type=int, default=20)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, copy 256 MiB once (the reference kernel that "
@@ -284,6 +288,36 @@ def main():
             "query_tok_s": round(2048 / (pmed * 1e-6), 1), "flop": pflop,
             "tflops": round(pflop / (pmed * 1e-6) / 1e12, 1),
             "mfma_frac": round(pflop / (pmed * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+
+    # ---------------------------------------------------------------- sparse attention
+    if not args.no_attention:
+        at = W.attention(seed=20, T=4096, S=65536, H=64, topk=512)
+        aq = torch.from_numpy(at.q.view(np.int16)).view(torch.bfloat16).to(dev)
+        akv = torch.from_numpy(at.kv.view(np.int16)).view(torch.bfloat16).to(dev)
+        aidx = torch.from_numpy(at.idx).to(dev)
+        aout = torch.empty((1, 4096, 64, at.d_v), dtype=torch.bfloat16, device=dev)
+        for _ in range(2):
+            ds.sparse_attention(aq, akv, aidx, at.softmax_scale, at.d_v, out=aout, stream=stream)
+        torch.cuda.synchronize()
+        aev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.attention_iters)]
+        for e in aev:
+            e[0].record(stream)
+            ds.sparse_attention(aq, akv, aidx, at.softmax_scale, at.d_v, out=aout, stream=stream)
+            e[1].record(stream)
+        torch.cuda.synchronize()
+        aus = sorted(e[0].elapsed_time(e[1]) * 1e3 for e in aev)
+        nsel = int((at.idx >= 0).sum())
+        aflop = 2 * 64 * nsel * (at.q.shape[-1] + at.d_v)
+        amed = aus[len(aus) // 2]
+        extra["sparse_attention_4096"] = {
+            "workload": "4096 queries x 64 heads, 512 selected rows each of a 65536-row bf16 latent cache "
+                        "(key 576, value 512), bf16 out + fp32 lse",
+            "us_median": round(amed, 2), "us_min": round(aus[0], 2),
+            "query_tok_s": round(4096 / (amed * 1e-6), 1), "flop": aflop,
+            "tflops": round(aflop / (amed * 1e-6) / 1e12, 1),
+            "mfma_frac": round(aflop / (amed * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "gathered_GB_s": round(nsel * at.q.shape[-1] * 2 / (amed * 1e-6) / 1e9, 1)}
+        del aq, akv, aidx, aout
 
     # ---------------------------------------------------------------- key-cache writer
     if not args.no_writer:

@@ -75,7 +75,7 @@ hipError_t launch_split_select_varlen(const VarlenProblem &p, const int *cu_q, c
 
 // Sparse attention over selected positions of a shared latent cache: the key
 // is the whole row (576 values), the value its first 512; heads in tiles of 64.
-constexpr int kAttnHeadTile = 64, kAttnDqk = 576, kAttnDv = 512;
+constexpr int kAttnHeadTile = 64, kAttnDqk = 576, kAttnDv = 512, kAttnMaxK = 2048;
 struct AttnProblem {
     int B, T, S, H, topk;
     float softmax_scale;

@@ -13,9 +13,13 @@
 //
 // Layout on CDNA4. A 512-thread workgroup owns one query token and one tile of
 // 64 heads; the selected rows stream through LDS in chunks of 32:
-//  * Rows are gathered global -> registers (issued one chunk ahead) -> LDS,
-//    twice: row-major for the scores and transposed (value dims x keys) for the
-//    weighted sum, so that both contractions read 16-byte MFMA fragments.
+//  * Gather. The rows of a chunk go straight from global memory into LDS
+//    (global_load_lds_dwordx4: each wavefront instruction moves 64 x 16 bytes,
+//    one 1 KB row head or the 128-byte tails of 8 rows), into a ring of four
+//    chunk buffers, three chunks ahead of the one being computed, so a CU
+//    keeps ~110 KB of gathers in flight without holding them in registers.
+//    The 16-byte pieces of a row are XOR-swizzled by the row number so the
+//    MFMA fragment reads below are bank-conflict free.
 //  * Scores transposed, S^T = C Q^T (v_mfma_f32_16x16x32_bf16, keys on M,
 //    heads on N): wavefront w computes the 16-key x 16-head tile (w & 1,
 //    w >> 1) over 18 k-steps of the 576 dims, with its 16 heads of Q resident
@@ -23,12 +27,11 @@
 //  * Online softmax in the log2 domain: per-head chunk maxima and sums go
 //    through LDS; every wavefront keeps the running max and sum of the heads
 //    its outputs cover.
-//  * The S^T accumulator already has the layout of a B operand of the value
-//    contraction O^T = V^T P^T (lane = head, 4 consecutive keys per lane group)
-//    under a fixed permutation of the 32 keys of a chunk; the transposed value
-//    copy is stored in that permuted key order, so P needs no transpose.
-//    Wavefront w owns value tiles 4w .. 4w+3 of all four head tiles: 16
-//    accumulator tiles.
+//  * Values, O^T = V^T P^T. The S^T accumulator already has the layout of a
+//    B operand (lane = head, 4 consecutive keys per lane group) under a fixed
+//    permutation of the chunk's 32 keys; the V^T fragments are read from the
+//    raw rows in that key order (one 2-byte LDS read per element). Wavefront w
+//    owns value tiles 4w .. 4w+3 of all four head tiles: 16 accumulators.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -38,37 +41,83 @@ namespace {
 constexpr int AH = kAttnHeadTile;  // heads per workgroup
 constexpr int DQK = kAttnDqk, DV = kAttnDv;
 constexpr int CK = 32;             // selected rows per chunk
+constexpr int NBUF = 4;            // chunk buffers: three in flight, one in use
 constexpr int ATHREADS = 512;
-constexpr int KSTR = DQK + 8;      // bf16 per LDS key row (16-byte aligned rows)
-constexpr int VSTR = CK + 8;       // bf16 per LDS transposed value row
-constexpr int NPIECE = DQK / 8;    // 16-byte pieces per cache row
+constexpr int MAIN16 = DV / 8;     // 16-byte pieces of a row's first 512 values (64)
+constexpr int TAIL16 = (DQK - DV) / 8;  // pieces of the rest (8)
 constexpr int NQK = DQK / 32;      // k-steps of the score contraction
+
+static_assert(MAIN16 == 64 && TAIL16 == 8, "one wavefront instruction per row head, per 8 row tails");
 
 typedef __attribute__((__vector_size__(8 * sizeof(short)))) short bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 
 struct AttnSmem {
-    uint16_t k[CK * KSTR];   // chunk rows, row-major
-    uint16_t vt[DV * VSTR];  // value dims x keys (permuted order)
-    uint16_t p[4][64][8];    // P^T B fragments per head tile and lane
-    float pmax[2][AH];       // chunk maxima per key tile and head
+    uint4 head[NBUF][CK * MAIN16];  // row r, piece p at [r * 64 + (p ^ (r & 15))]
+    uint4 tail[NBUF][CK * TAIL16];  // row r, piece q at [r * 8 + (q ^ (r & 7))]
+    int sel[kAttnMaxK];             // the token's rows, -1 where the entry is not valid
+    uint16_t p[4][64][8];           // P^T B fragments per head tile and lane
+    float pmax[2][AH];              // chunk maxima per key tile and head
     float psum[2][AH];
-    int valid[CK];
 };
 
-// Key s of a chunk sits at position pos(s) of the permuted order: lane group
-// g = (s % 16) / 4 of the score tile holds keys 4g..4g+3 of each 16-key tile,
-// and a value-contraction fragment of group g takes those 8 keys.
-__device__ __forceinline__ int perm_pos(int s) { return 8 * ((s & 15) >> 2) + 4 * (s >> 4) + (s & 3); }
+// Key s of a chunk, in the order shared by the score tiles and the value
+// fragments: lane group g of a score tile holds keys 4g..4g+3 of each 16-key
+// tile, and a value fragment of group g takes those 8 keys.
+__device__ __forceinline__ int perm_key(int g, int e) { return e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4); }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b)
 {
-    // round to nearest even (inputs are finite probabilities in [0, 1])
+    // round to nearest even (finite inputs)
     auto rne = [](float x) {
         const uint32_t u = __float_as_uint(x);
         return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
     };
     return rne(a) | (rne(b) << 16);
+}
+
+// One 16-byte gather per lane straight into LDS (global_load_lds_dwordx4):
+// lane i's bytes land at LDS address lds + 16 i. Issued as inline assembly
+// so that the compiler does not treat it as an LDS store it must drain
+// (vmcnt(0)) before every later LDS read; completion is awaited explicitly
+// with wait_vm, and no other vector-memory instruction runs in the main
+// loop. M0 carries the (wavefront-uniform) LDS address; this kernel uses M0
+// for nothing else.
+__device__ __forceinline__ uint32_t lds_addr(const void *p)
+{
+    return (uint32_t)(size_t)(const __attribute__((address_space(3))) void *)p;
+}
+
+__device__ __forceinline__ void gather16(const void *src, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory", "m0");
+}
+
+// Max / sum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (one head of a
+// 16 x 16 accumulator tile) with the permlane swaps, VALU only.
+__device__ __forceinline__ float quad_max(float x)
+{
+    auto w = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(w[0]), __uint_as_float(w[1]));
+    w = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(w[0]), __uint_as_float(w[1]));
+}
+
+__device__ __forceinline__ float quad_sum(float x)
+{
+    auto w = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(w[0]) + __uint_as_float(w[1]);
+    w = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(w[0]) + __uint_as_float(w[1]);
+}
+
+// Wait until at most N of this wavefront's vector-memory operations are
+// outstanding (expcnt and lgkmcnt left free).
+template <int N>
+__device__ __forceinline__ void wait_vm()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 
 __global__ __launch_bounds__(ATHREADS, 1) void sparse_attention_kernel(
@@ -79,10 +128,16 @@ __global__ __launch_bounds__(ATHREADS, 1) void sparse_attention_kernel(
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const long long row = blockIdx.x;  // b * T + t
     const int h0 = blockIdx.y * AH;
-    const uint16_t *Cb = C + (row / T) * (long long)S * DQK;
+    const char *Cb = reinterpret_cast<const char *>(C + (row / T) * (long long)S * DQK);
     const int *ir = idx + row * topk;
     const int kt = wid & 1, ht = wid >> 1;
+    const int nchunk = (topk + CK - 1) / CK;
 
+    // The selected rows, validated once.
+    for (int j = tid; j < nchunk * CK; j += ATHREADS) {
+        const int e = j < topk ? ir[j] : -1;
+        sm.sel[j] = (e >= 0 && e < S) ? e : -1;
+    }
     // Q^T fragments of head tile ht: head h0 + 16 ht + lane % 16, dims 32 ks + 8 (lane / 16) ..
     bf16x8 qf[NQK];
     {
@@ -91,6 +146,33 @@ __global__ __launch_bounds__(ATHREADS, 1) void sparse_attention_kernel(
 #pragma unroll
         for (int ks = 0; ks < NQK; ++ks) qf[ks] = qp[ks * 4];
     }
+    // Finish the Q loads here, so that no wait for them is left to the main
+    // loop (where vmcnt counts only the gathers).
+    wait_vm<0>();
+#pragma unroll
+    for (int ks = 0; ks < NQK; ++ks) asm volatile("" : "+v"(qf[ks]));
+    __syncthreads();
+
+    // Gather of chunk c into buffer c % NBUF: wavefront w loads the heads of
+    // rows 4w..4w+3 (lane i takes piece i ^ (r & 15) of row r into slot i),
+    // wavefronts 0..3 also the tails of rows 8w..8w+7. Invalid entries load
+    // row 0, so every value read is finite; their scores are masked.
+    auto issue = [&](int c) {
+        const int b = c % NBUF;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = 4 * wid + j;
+            const int e = sm.sel[c * CK + r];
+            const char *src = Cb + (long long)(e < 0 ? 0 : e) * (DQK * 2) + ((lane ^ (r & 15)) * 16);
+            gather16(src, __builtin_amdgcn_readfirstlane(lds_addr(&sm.head[b][r * MAIN16])));
+        }
+        if (wid < 4) {
+            const int r = 8 * wid + (lane >> 3);
+            const int e = sm.sel[c * CK + r];
+            const char *src = Cb + (long long)(e < 0 ? 0 : e) * (DQK * 2) + DV * 2 + (((lane & 7) ^ (r & 7)) * 16);
+            gather16(src, __builtin_amdgcn_readfirstlane(lds_addr(&sm.tail[b][wid * 64])));
+        }
+    };
 
     f32x4 o[4][4];  // [head tile][value tile 4 wid + j]
 #pragma unroll
@@ -104,63 +186,43 @@ __global__ __launch_bounds__(ATHREADS, 1) void sparse_attention_kernel(
         l_run[a] = 0.0f;
     }
 
-    // Staging: lanes 0..31 and 32..63 of wavefront w take pieces 2w and 2w+1
-    // (+16 j) of chunk row lane % 32.
-    const int skey = lane & 31;
-    uint4 stg[5];
-    bool sok = false;
-    auto prefetch = [&](int c) {
-        const int j0 = c * CK + skey;
-        const int s = j0 < topk ? ir[j0] : -1;
-        sok = s >= 0 && s < S;
-        const uint4 *src = reinterpret_cast<const uint4 *>(Cb + (long long)(sok ? s : 0) * DQK);
-#pragma unroll
-        for (int j = 0; j < 5; ++j) {
-            const int p = 2 * wid + (lane >> 5) + 16 * j;
-            stg[j] = (sok && p < NPIECE) ? src[p] : make_uint4(0, 0, 0, 0);
-        }
-    };
-    auto stage = [&]() {
-        const int pos = perm_pos(skey);
-#pragma unroll
-        for (int j = 0; j < 5; ++j) {
-            const int p = 2 * wid + (lane >> 5) + 16 * j;
-            if (p < NPIECE) {
-                *reinterpret_cast<uint4 *>(&sm.k[skey * KSTR + p * 8]) = stg[j];
-                if (p < DV / 8) {
-                    const uint32_t w[4] = {stg[j].x, stg[j].y, stg[j].z, stg[j].w};
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        sm.vt[(p * 8 + e) * VSTR + pos] = (uint16_t)((e & 1) ? (w[e >> 1] >> 16) : w[e >> 1]);
-                }
-            }
-        }
-        if (wid == 0 && lane < 32) sm.valid[lane] = sok ? 1 : 0;
-    };
-
-    const int nchunk = (topk + CK - 1) / CK;
-    prefetch(0);
+    for (int c = 0; c < NBUF - 1 && c < nchunk; ++c) issue(c);
     for (int c = 0; c < nchunk; ++c) {
-        stage();
-        __syncthreads();
-        if (c + 1 < nchunk) prefetch(c + 1);
+        const int b = c % NBUF;
+        // this wavefront's gathers of chunk c are done once at most those of
+        // the chunks issued after it remain (4 or 5 per chunk)
+        const int ahead = (c + NBUF - 2 < nchunk - 1 ? c + NBUF - 2 : nchunk - 1) - c;
+        if (ahead >= 2) {
+            if (wid < 4) wait_vm<10>(); else wait_vm<8>();
+        } else if (ahead == 1) {
+            if (wid < 4) wait_vm<5>(); else wait_vm<4>();
+        } else {
+            wait_vm<0>();
+        }
+        __syncthreads();  // chunk c visible; every wavefront is past chunk c - 1
+        if (c + NBUF - 1 < nchunk) issue(c + NBUF - 1);
 
         // scores of key tile kt x head tile ht
         f32x4 s = f32x4{};
-        const uint16_t *kp = &sm.k[(kt * 16 + (lane & 15)) * KSTR + (lane >> 4) * 8];
+        {
+            const int r = kt * 16 + (lane & 15);
+            const uint4 *hr = &sm.head[b][r * MAIN16];
+            const uint4 *tr = &sm.tail[b][r * TAIL16];
 #pragma unroll
-        for (int ks = 0; ks < NQK; ++ks)
-            s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8 *>(kp + ks * 32), qf[ks],
-                                                        s, 0, 0, 0);
+            for (int ks = 0; ks < NQK; ++ks) {
+                const int pc = ks * 4 + (lane >> 4);
+                const uint4 v = pc < MAIN16 ? hr[pc ^ (r & 15)] : tr[(pc - MAIN16) ^ (r & 7)];
+                s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v), qf[ks], s, 0, 0, 0);
+            }
+        }
         float z[4], mx = -INFINITY;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int key = kt * 16 + 4 * (lane >> 4) + i;
-            z[i] = sm.valid[key] ? s[i] * scale_log2 : -INFINITY;
+            z[i] = sm.sel[c * CK + key] >= 0 ? s[i] * scale_log2 : -INFINITY;
             mx = fmaxf(mx, z[i]);
         }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mx = quad_max(mx);
         if (lane < 16) sm.pmax[kt][ht * 16 + lane] = mx;
         __syncthreads();
 
@@ -178,34 +240,50 @@ __global__ __launch_bounds__(ATHREADS, 1) void sparse_attention_kernel(
             pr[i] = exp2f(z[i] - m_use[ht]);
             ps += pr[i];
         }
-        ps += __shfl_xor(ps, 16);
-        ps += __shfl_xor(ps, 32);
+        ps = quad_sum(ps);
         if (lane < 16) sm.psum[kt][ht * 16 + lane] = ps;
         *reinterpret_cast<uint2 *>(&sm.p[ht][lane][kt * 4]) =
             make_uint2(pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]));
         __syncthreads();
 
+        bool moved = false;
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
             const int hh = a * 16 + (lane & 15);
             l_run[a] = l_run[a] * alpha[a] + (sm.psum[0][hh] + sm.psum[1][hh]);
             m_run[a] = m_new[a];
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) o[a][j][i] *= alpha[a];
+            moved = moved || alpha[a] != 1.0f;
         }
-        bf16x8 pb[4];
+        if (wave_ballot(moved)) {  // a head's running max rose: rescale
 #pragma unroll
-        for (int a = 0; a < 4; ++a) pb[a] = *reinterpret_cast<const bf16x8 *>(&sm.p[a][lane][0]);
+            for (int a = 0; a < 4; ++a)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) o[a][j][i] *= alpha[a];
+        }
+        // One value fragment at a time (its 8 keys read from the raw rows),
+        // the P fragments re-read from LDS for each: short live ranges keep
+        // the kernel within its 256 registers with nothing spilled, so no
+        // vector-memory instruction but the gathers runs in this loop.
+        const int ln = lane;
+        const int g = ln >> 4;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const bf16x8 va =
-                *reinterpret_cast<const bf16x8 *>(&sm.vt[((4 * wid + j) * 16 + (lane & 15)) * VSTR + (lane >> 4) * 8]);
+            const int dv = (4 * wid + j) * 16 + (ln & 15);
+            bf16x8 va;
 #pragma unroll
-            for (int a = 0; a < 4; ++a) o[a][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[a], o[a][j], 0, 0, 0);
+            for (int e = 0; e < 8; ++e) {
+                const int key = perm_key(g, e);
+                const uint16_t *pc = reinterpret_cast<const uint16_t *>(&sm.head[b][key * MAIN16 + ((dv >> 3) ^ (key & 15))]);
+                va[e] = (short)pc[dv & 7];
+            }
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+                o[a][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    va, *reinterpret_cast<const bf16x8 *>(&sm.p[a][ln][0]), o[a][j], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
         }
-        __syncthreads();
     }
 
     // O^T tile (value tile 4 wid + j, head tile a): lane holds head 16 a +
