@@ -18,7 +18,9 @@ batches in one launch each (ds4idx_select_varlen): 64 decode streams whose
 caches span 4096..61426 keys, and a 2048-token chunked-prefill budget spread
 over four streams; and sparse attention (ds4idx_sparse_attention) of one
 4096-query prefill chunk over 512 selected rows of a 65536-row latent cache,
-64 heads, against the bf16 MFMA peak.
+64 heads, against the bf16 MFMA peak; and the fp8 x fp8 variant of the 64k
+prefill (queries quantised per token and head by the key-cache writer, inside
+the timed step), with its recall of the exact selection on sampled rows.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -32,6 +34,7 @@ import time
 
 METRIC = "indexer query-tok/s at 64k causal prefill (score+top-512); decode µs at 256k"
 BF16_PEAK_TFLOPS = 2516.6   # 256 CU x 2.4 GHz x 4096 dense bf16 flop/clk/CU
+FP8_PEAK_TFLOPS = 5033.2    # dense fp8
 HBM_PEAK_GBS = 8000.0
 
 
@@ -48,6 +51,7 @@ def _parse():
     ap.add_argument("--no-writer", action="store_true")
     ap.add_argument("--no-ragged", action="store_true")
     ap.add_argument("--no-attention", action="store_true")
+    ap.add_argument("--no-qfp8", action="store_true")
     ap.add_argument("--attention-iters", type=int, default=10)
     ap.add_argument("--writer-iters", type=int, default=20)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -168,6 +172,36 @@ def main():
 
     extra = {"kernel_ms_per_step": round(sum(launch_ms) / args.steps, 3),
              "bf16_tflops_step_wall": round(flops / (ms_per_step * 1e-3) / 1e12, 1)}
+
+    # ---------------------------------------------------------------- fp8 x fp8 prefill
+    idx8 = None
+    if not args.no_qfp8:
+        q8 = torch.empty((1, wl.T, wl.H, wl.D), dtype=torch.uint8, device=dev)
+        qs8 = torch.empty((1, wl.T, wl.H), dtype=torch.float32, device=dev)
+        idx8 = torch.empty((1, wl.T, wl.topk), dtype=torch.int32, device=dev)
+        vals8 = torch.empty((1, wl.T, wl.topk), dtype=torch.float32, device=dev)
+
+        def qstep():
+            for (t0, tc, sc, oc) in wl.chunks:
+                ds.k_cache_write(q[0, t0:t0 + tc].reshape(tc * wl.H, wl.D), q8[0, t0:t0 + tc].reshape(tc * wl.H, wl.D),
+                                 qs8[0, t0:t0 + tc].reshape(tc * wl.H), stream=stream)
+                ds.select_qfp8(q8[:, t0:t0 + tc], qs8[:, t0:t0 + tc], k[:, :sc], ks[:, :sc], w[:, t0:t0 + tc], oc,
+                               wl.topk, idx=idx8[:, t0:t0 + tc], vals=vals8[:, t0:t0 + tc], stream=stream)
+
+        qstep()
+        torch.cuda.synchronize()
+        qe = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        qe[0].record(stream)
+        for _ in range(3):
+            qstep()
+        qe[1].record(stream)
+        torch.cuda.synchronize()
+        qms = qe[0].elapsed_time(qe[1]) / 3
+        extra["select_qfp8_64k"] = {
+            "workload": "the 64k prefill with E4M3 queries (one scale per token and head, quantised in the step)",
+            "ms_per_step": round(qms, 3), "query_tok_s": round(wl.T / (qms * 1e-3), 1),
+            "tflops": round(flops / (qms * 1e-3) / 1e12, 1),
+            "fp8_frac": round(flops / (qms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4)}
 
     # ---------------------------------------------------------------- 256k decode
     if not args.no_decode:
@@ -367,6 +401,13 @@ def main():
         t_cpu = time.perf_counter() - t0
         keys = int(sum(wl.offset + r + 1 for r in rows))
         full_s = t_cpu * pairs / keys
+        if idx8 is not None:  # parity cost of the fp8 queries: overlap with the exact selection
+            prow = np.sort(rng.choice(wl.T, 8, replace=False)).astype(np.int64)
+            oi, _, _, _, _ = oracle.select(wl, rows=prow)
+            g8 = idx8.reshape(wl.T, wl.topk).cpu().numpy()[prow]
+            rec = [len(set(g8[n]) & set(oi[n])) / float(wl.topk) for n in range(len(prow))]
+            extra["select_qfp8_64k"]["recall_of_exact_top512"] = round(float(np.mean(rec)), 4)
+            extra["select_qfp8_64k"]["recall_rows"] = [int(r) for r in prow]
         cpu = {"value": round(wl.T / full_s, 2), "unit": "query-tok/s", "cores": int(used),
                "kind": "oracle",
                "sample": f"{n} uniformly drawn query rows of the 64k prefill ({keys} visible keys, "

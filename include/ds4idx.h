@@ -170,6 +170,23 @@ int ds4idx_select_varlen(const ds4idx_varlen_problem *p, const int32_t *cu_q, co
                          int32_t k, int32_t *idx, float *vals, void *workspace, size_t ws_bytes,
                          void *stream);
 
+/* fp8 x fp8 scorer + top-k: ds4idx_select with the queries, too, in OCP
+ * E4M3, one fp32 scale per (token, head), and the E4M3 matrix-core path
+ * (twice the bf16 peak on gfx950). The score is computed from the dequantised
+ * queries Q_scale[b,t,h] * decode(Q8[b,t,h,d]); rounding Q to a 3-bit
+ * mantissa moves scores by about 2%, so the selection is close to, not equal
+ * to, the bf16-query selection (the survey's fp8 x fp8 variant; the parity
+ * cost is measured and reported beside the benchmark). Quantise the queries
+ * with ds4idx_k_cache_write over their B*T*H rows of D values.
+ *   Q8       [B, T, H, D] E4M3 codes, 16-byte aligned
+ *   Q_scale  [B, T, H]    fp32, positive finite
+ * Other arguments as for ds4idx_select; p->q_dtype and p->k_dtype must both be
+ * DS4IDX_FP8_E4M3. Kernel shape: H = 64, D = 128, k <= 512 (otherwise
+ * DS4IDX_ERR_UNSUPPORTED); no workspace. */
+int ds4idx_select_qfp8(const ds4idx_problem *p, const void *Q8, const float *Q_scale, const void *K,
+                       const float *K_scale, const float *W, int32_t k, int32_t *idx, float *vals,
+                       void *stream);
+
 /* Sparse attention over the selected positions, the step downstream of the
  * indexer: each query token attends only to the cache rows its idx row names
  * (first page, glossary entry on sparse attention). The MI300X write-up keeps

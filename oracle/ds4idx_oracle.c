@@ -50,7 +50,7 @@
 #include <omp.h>
 #endif
 
-enum { O_F32 = 0, O_BF16 = 1, O_FP8 = 2 };
+enum { O_F32 = 0, O_BF16 = 1, O_FP8 = 2, O_F64 = 3 };
 
 /* OCP E4M3FN code -> exact value. */
 double ds4o_e4m3_decode(int code)
@@ -76,8 +76,12 @@ static double bf16_value(uint16_t b)
     return (double)f;
 }
 
+/* O_F64 holds exact values given as doubles (e.g. dequantised E4M3 queries:
+ * a 4-bit significand times an fp32 scale fits a double). */
 static double load_elem(const void *base, int dtype, int64_t i)
 {
+    if (dtype == O_F64)
+        return ((const double *)base)[i];
     if (dtype == O_F32)
         return (double)((const float *)base)[i];
     if (dtype == O_BF16)

@@ -37,7 +37,7 @@ ABI_VERSION = 1
 EXPORTS = ("ds4idx_abi_version", "ds4idx_status_string", "ds4idx_set_impl", "ds4idx_get_impl",
            "ds4idx_workspace_bytes", "ds4idx_score", "ds4idx_topk", "ds4idx_select",
            "ds4idx_k_cache_write", "ds4idx_varlen_workspace_bytes", "ds4idx_select_varlen",
-           "ds4idx_sparse_attention")
+           "ds4idx_sparse_attention", "ds4idx_select_qfp8")
 
 
 class Problem(ctypes.Structure):
@@ -102,6 +102,8 @@ def lib() -> ctypes.CDLL:
         L.ds4idx_select_varlen.restype = ctypes.c_int
         L.ds4idx_sparse_attention.argtypes = [ctypes.POINTER(AttnProblem), vp, vp, vp, vp, vp, vp]
         L.ds4idx_sparse_attention.restype = ctypes.c_int
+        L.ds4idx_select_qfp8.argtypes = [P, vp, vp, vp, vp, vp, i32, vp, vp, vp]
+        L.ds4idx_select_qfp8.restype = ctypes.c_int
         if L.ds4idx_abi_version() != ABI_VERSION:
             raise RuntimeError("libds4idx ABI version mismatch; rebuild the library")
         _lib = L
@@ -290,6 +292,35 @@ def select_varlen(q, k, k_scale, w, cu_q, cu_k, max_k: int, topk: int = 512,
                                     _ptr(workspace), ws_bytes, _stream(stream))
     if st != OK:
         raise Ds4idxError(st, "ds4idx_select_varlen")
+    return idx, vals
+
+
+def select_qfp8(q8, q_scale, k, k_scale, w, causal_offset: int, topk: int = 512,
+                idx: Optional[torch.Tensor] = None, vals: Optional[torch.Tensor] = None,
+                with_vals: bool = True, stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """fp8 x fp8 indexer: q8 [B,T,H,D] E4M3 codes (uint8 / float8_e4m3fn) with
+    q_scale [B,T,H] fp32, k [B,S,D] E4M3 with k_scale [B,S], w [B,T,H] fp32."""
+    for name, t in (("q8", q8), ("q_scale", q_scale), ("k", k), ("k_scale", k_scale), ("w", w)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    if q8.dtype not in (torch.uint8, torch.float8_e4m3fn) or k.dtype not in (torch.uint8, torch.float8_e4m3fn):
+        raise ValueError("q8 and k must hold E4M3 codes")
+    B, T, H, D = q8.shape
+    if tuple(q_scale.shape) != (B, T, H) or q_scale.dtype != torch.float32:
+        raise ValueError("q_scale must be float32 [B,T,H]")
+    if tuple(w.shape) != (B, T, H) or w.dtype != torch.float32:
+        raise ValueError("w must be float32 [B,T,H]")
+    if k.dim() != 3 or k.shape[0] != B or k.shape[2] != D or tuple(k_scale.shape) != tuple(k.shape[:2]):
+        raise ValueError("k must be [B,S,D] with k_scale [B,S]")
+    p = Problem(B, T, k.shape[1], H, D, int(causal_offset), FP8_E4M3, FP8_E4M3)
+    if idx is None:
+        idx = torch.empty((B, T, topk), dtype=torch.int32, device=q8.device)
+    if vals is None and with_vals:
+        vals = torch.empty((B, T, topk), dtype=torch.float32, device=q8.device)
+    st = lib().ds4idx_select_qfp8(ctypes.byref(p), _ptr(q8), _ptr(q_scale), _ptr(k), _ptr(k_scale), _ptr(w),
+                                  int(topk), _ptr(idx), _ptr(vals), _stream(stream))
+    if st != OK:
+        raise Ds4idxError(st, "ds4idx_select_qfp8")
     return idx, vals
 
 

@@ -294,6 +294,24 @@ int ds4idx_select_varlen(const ds4idx_varlen_problem *p, const int32_t *cu_q, co
         ds4idx::launch_split_select_varlen(v, cu_q, ck, Q, K, K_scale, W, k, idx, vals, workspace, s));
 }
 
+int ds4idx_select_qfp8(const ds4idx_problem *p, const void *Q8, const float *Q_scale, const void *K,
+                       const float *K_scale, const float *W, int32_t k, int32_t *idx, float *vals, void *stream)
+{
+    if (!p || p->B < 1 || p->T < 1 || p->S < 1 || p->H < 1 || p->D < 1 || p->causal_offset < 0 ||
+        p->causal_offset + (int64_t)p->T > (int64_t)p->S || p->q_dtype != DS4IDX_FP8_E4M3 ||
+        p->k_dtype != DS4IDX_FP8_E4M3)
+        return DS4IDX_ERR_INVALID_ARG;
+    if (k < 1 || k > DS4IDX_MAX_TOPK) return DS4IDX_ERR_INVALID_ARG;
+    if (!Q8 || !Q_scale || !K || !K_scale || !W || !idx || !aligned(Q8, 16) || !aligned(K, 16) ||
+        !aligned(Q_scale, 4) || !aligned(K_scale, 4) || !aligned(W, 4) || !aligned(idx, 4) || (vals && !aligned(vals, 4)))
+        return DS4IDX_ERR_INVALID_ARG;
+    if (p->H != ds4idx::kMfmaH || p->D != ds4idx::kMfmaD || k > ds4idx::kMfmaMaxK || p->B > 65535)
+        return DS4IDX_ERR_UNSUPPORTED;
+    const Problem q = to_internal(p);
+    return launch_status(ds4idx::launch_mfma_select_qfp8(q, Q8, Q_scale, K, K_scale, W, k, idx, vals,
+                                                         static_cast<hipStream_t>(stream)));
+}
+
 int ds4idx_sparse_attention(const ds4idx_attn_problem *p, const void *Q, const void *KV,
                             const int32_t *idx, void *O, float *lse, void *stream)
 {

@@ -39,6 +39,9 @@ hipError_t launch_mfma_score(const Problem &p, const void *Q, const void *K, con
                              const float *W, float *scores, hipStream_t st);
 hipError_t launch_mfma_select(const Problem &p, const void *Q, const void *K, const float *Ks,
                               const float *W, int k, int *idx, float *vals, hipStream_t st);
+// fp8 x fp8 scorer: E4M3 queries with one fp32 scale per (token, head), E4M3 keys.
+hipError_t launch_mfma_select_qfp8(const Problem &p, const void *Q8, const float *QS, const void *K, const float *Ks,
+                                   const float *W, int k, int *idx, float *vals, hipStream_t st);
 long long mfma_varlen_blocks(int B, int total_q);
 hipError_t launch_mfma_select_varlen(const VarlenProblem &p, const int *cu_q, const long long *cu_k,
                                      const void *Q, const void *K, const float *Ks, const float *W,

@@ -57,6 +57,9 @@ constexpr int THREADS = NWAVE * 64;
 
 typedef __attribute__((__vector_size__(8 * sizeof(short)))) short bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8;
+
+constexpr int KROW8 = D + 16;  // bytes per LDS key row of raw E4M3 codes (fp8 x fp8 scorer)
 
 struct alignas(16) Smem {
     uint16_t k[2][KT * KROW];
@@ -203,6 +206,17 @@ __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w)
     return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w, 1.0f, HI));
 }
 
+// fp8 x fp8 scorer: the codes stay raw, 144-byte rows (32-byte fragment reads
+// of 8 consecutive rows fall in distinct banks).
+__device__ __forceinline__ void store_tile_raw(Smem &sm, int buf, const TileRegs<true> &r, float sc, int tid)
+{
+    const int key = tid >> 2, part = tid & 3;
+    uint4 *dst = reinterpret_cast<uint4 *>(reinterpret_cast<uint8_t *>(&sm.k[buf][0]) + key * KROW8 + part * 32);
+    dst[0] = r.v[0];
+    dst[1] = r.v[1];
+    if (part == 0) sm.scale[buf][key] = sc;
+}
+
 template <bool KFP8>
 __device__ __forceinline__ void store_tile(Smem &sm, int buf, const TileRegs<KFP8> &r, float sc, int tid)
 {
@@ -227,12 +241,19 @@ __device__ __forceinline__ void store_tile(Smem &sm, int buf, const TileRegs<KFP
 // Ragged batches (VARLEN): the streams of rg (see StreamGeo); the grid's x
 // dimension covers every stream's 8-token blocks, and blocks past the last
 // one exit at once.
-template <bool KFP8, bool SCORE, bool VARLEN>
+// QFP8: the fp8 x fp8 scorer. Q holds E4M3 codes with one fp32 scale per
+// (token, head) in QS; the scale is positive, so it commutes with the ReLU and
+// joins the head weight. Keys stay raw E4M3 in LDS and each 16 x 16 tile is
+// one v_mfma_scale_f32_16x16x128_f8f6f4 over all 128 dims (unit block
+// scales): the same lane mapping for both operands (lane l: row or column
+// l % 16, bytes 32 (l / 16) .. +31) pairs their contraction elements.
+template <bool KFP8, bool SCORE, bool VARLEN, bool QFP8>
 __global__ __launch_bounds__(THREADS, 1) void mfma_indexer_kernel(
     const uint16_t *__restrict__ Q, const uint8_t *__restrict__ K, const float *__restrict__ Ks,
     const float *__restrict__ W, int T, int S, long long offset, int topk, int *__restrict__ idx,
-    float *__restrict__ vals, float *__restrict__ scores, Ragged rg)
+    float *__restrict__ vals, float *__restrict__ scores, const float *__restrict__ QS, Ragged rg)
 {
+    static_assert(!QFP8 || (KFP8 && !SCORE && !VARLEN), "the fp8 x fp8 scorer is the E4M3-key select");
     __shared__ Smem sm;
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     // This block's stream: first query row q0, first key row k0, Tb queries
@@ -268,17 +289,29 @@ __global__ __launch_bounds__(THREADS, 1) void mfma_indexer_kernel(
     // wv[m][i] = W[tok, head 16m + 4(lane/16) + i], the heads of this lane's
     // accumulator elements.
     bf16x8 a[4][4];
+    i32x8 a8[4];  // QFP8: a8[m] = codes of head 16m + lane%16, dims 32 (lane/16) .. +31
     float wv[4][4];
     {
         const long long qrow = (q0 + (tok_ok ? tok : 0)) * H;
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-            const bf16x8 *qp = reinterpret_cast<const bf16x8 *>(
-                Q + (qrow + m * 16 + (lane & 15)) * D + (lane >> 4) * 8);
+            if constexpr (QFP8) {
+                const uint4 *qp = reinterpret_cast<const uint4 *>(reinterpret_cast<const uint8_t *>(Q) +
+                                                                  (qrow + m * 16 + (lane & 15)) * D + (lane >> 4) * 32);
+                const uint4 lo = tok_ok ? qp[0] : make_uint4(0, 0, 0, 0);
+                const uint4 hi = tok_ok ? qp[1] : make_uint4(0, 0, 0, 0);
+                a8[m] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+            } else {
+                const bf16x8 *qp = reinterpret_cast<const bf16x8 *>(
+                    Q + (qrow + m * 16 + (lane & 15)) * D + (lane >> 4) * 8);
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) a[m][ks] = tok_ok ? qp[ks * 4] : bf16x8{};
+                for (int ks = 0; ks < 4; ++ks) a[m][ks] = tok_ok ? qp[ks * 4] : bf16x8{};
+            }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) wv[m][i] = tok_ok ? W[qrow + m * 16 + 4 * (lane >> 4) + i] : 0.0f;
+            for (int i = 0; i < 4; ++i) {
+                const long long hrow = qrow + m * 16 + 4 * (lane >> 4) + i;
+                wv[m][i] = tok_ok ? (QFP8 ? W[hrow] * QS[hrow] : W[hrow]) : 0.0f;
+            }
         }
     }
 
@@ -295,7 +328,8 @@ __global__ __launch_bounds__(THREADS, 1) void mfma_indexer_kernel(
     TileRegs<KFP8> tr;
     float tsc;
     load_tile<KFP8>(tr, tsc, Kb, Ksb, Sb, 0, tid);
-    store_tile<KFP8>(sm, 0, tr, tsc, tid);
+    if constexpr (QFP8) store_tile_raw(sm, 0, tr, tsc, tid);
+    else store_tile<KFP8>(sm, 0, tr, tsc, tid);
     __syncthreads();
 
     // Half-pair software pipeline. A 64-key pair is two 32-key halves of 8
@@ -313,6 +347,32 @@ __global__ __launch_bounds__(THREADS, 1) void mfma_indexer_kernel(
     // MFMAs of half h of the pair at pair offset pp in buffer cur into
     // acc[h], interleaved with the reduction of acc[h ^ 1] into part[n].
     auto phase = [&](int h, int cur, int pp, float (&part)[2]) {
+        if constexpr (QFP8) {
+            // one MFMA per output tile; the reduction of the other half's key
+            // tile n follows the four MFMAs of key tile n
+            const uint8_t *kp8 = reinterpret_cast<const uint8_t *>(&sm.k[cur][0]) +
+                                 (pp * 64 + 32 * h + (lane & 15)) * KROW8 + (lane >> 4) * 32;
+            const f32x4 (&r)[2][4] = acc[h ^ 1];
+            float s4[2][4] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+#pragma unroll
+            for (int n = 0; n < 2; ++n) {
+                const uint4 *bp = reinterpret_cast<const uint4 *>(kp8 + 16 * n * KROW8);
+                const uint4 lo = bp[0], hi = bp[1];
+                const i32x8 bk8 = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+#pragma unroll
+                for (int m = 0; m < 4; ++m)
+                    acc[h][n][m] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8[m], bk8, f32x4{}, 0, 0, 0, 127, 0, 127);
+#pragma unroll
+                for (int m = 0; m < 4; ++m)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) s4[n][i] = fmaf(wv[m][i], relu(r[n][m][i]), s4[n][i]);
+                asm volatile("" : "+v"(s4[n][0]), "+v"(s4[n][1]), "+v"(s4[n][2]), "+v"(s4[n][3]));
+                __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int n = 0; n < 2; ++n) part[n] = (s4[n][0] + s4[n][1]) + (s4[n][2] + s4[n][3]);
+            return;
+        }
         const uint16_t *kp = &sm.k[cur][(pp * 64 + 32 * h + (lane & 15)) * KROW + (lane >> 4) * 8];
         const f32x4 (&r)[2][4] = acc[h ^ 1];
         float s4[2][4] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
@@ -412,7 +472,10 @@ __global__ __launch_bounds__(THREADS, 1) void mfma_indexer_kernel(
             prev0[0] = h0[0];
             prev0[1] = h0[1];
         }
-        if (tile + 1 < ntiles) store_tile<KFP8>(sm, cur ^ 1, tr, tsc, tid);
+        if (tile + 1 < ntiles) {
+            if constexpr (QFP8) store_tile_raw(sm, cur ^ 1, tr, tsc, tid);
+            else store_tile<KFP8>(sm, cur ^ 1, tr, tsc, tid);
+        }
         __syncthreads();
     }
     {  // the last pair's second half
@@ -450,9 +513,9 @@ hipError_t launch(const Problem &p, const void *Q, const void *K, const float *K
                   int k, int *idx, float *vals, float *scores, hipStream_t st)
 {
     const int nblk = (p.T + TQ - 1) / TQ;
-    hipLaunchKernelGGL((mfma_indexer_kernel<KFP8, SCORE, false>), dim3(nblk, p.B), dim3(THREADS), 0, st,
+    hipLaunchKernelGGL((mfma_indexer_kernel<KFP8, SCORE, false, false>), dim3(nblk, p.B), dim3(THREADS), 0, st,
                        static_cast<const uint16_t *>(Q), static_cast<const uint8_t *>(K), Ks, W, p.T,
-                       p.S, p.offset, k, idx, vals, scores, Ragged{});
+                       p.S, p.offset, k, idx, vals, scores, nullptr, Ragged{});
     return hipGetLastError();
 }
 
@@ -477,6 +540,16 @@ hipError_t launch_mfma_select(const Problem &p, const void *Q, const void *K, co
     return launch<false, false>(p, Q, K, Ks, W, k, idx, vals, nullptr, st);
 }
 
+hipError_t launch_mfma_select_qfp8(const Problem &p, const void *Q8, const float *QS, const void *K, const float *Ks,
+                                   const float *W, int k, int *idx, float *vals, hipStream_t st)
+{
+    const int nblk = (p.T + TQ - 1) / TQ;
+    hipLaunchKernelGGL((mfma_indexer_kernel<true, false, false, true>), dim3(nblk, p.B), dim3(THREADS), 0, st,
+                       static_cast<const uint16_t *>(Q8), static_cast<const uint8_t *>(K), Ks, W, p.T, p.S, p.offset,
+                       k, idx, vals, nullptr, QS, Ragged{});
+    return hipGetLastError();
+}
+
 long long mfma_varlen_blocks(int B, int total_q) { return ((long long)total_q + TQ - 1) / TQ + B; }
 
 hipError_t launch_mfma_select_varlen(const VarlenProblem &p, const int *cu_q, const long long *cu_k,
@@ -489,11 +562,11 @@ hipError_t launch_mfma_select_varlen(const VarlenProblem &p, const int *cu_q, co
     const uint16_t *q = static_cast<const uint16_t *>(Q);
     const uint8_t *kk = static_cast<const uint8_t *>(K);
     if (p.k_dtype == FP8)
-        hipLaunchKernelGGL((mfma_indexer_kernel<true, false, true>), grid, dim3(THREADS), 0, st, q, kk, Ks, W, 0, 0,
-                           0LL, k, idx, vals, nullptr, rg);
+        hipLaunchKernelGGL((mfma_indexer_kernel<true, false, true, false>), grid, dim3(THREADS), 0, st, q, kk, Ks, W, 0,
+                           0, 0LL, k, idx, vals, nullptr, nullptr, rg);
     else
-        hipLaunchKernelGGL((mfma_indexer_kernel<false, false, true>), grid, dim3(THREADS), 0, st, q, kk, Ks, W, 0,
-                           0, 0LL, k, idx, vals, nullptr, rg);
+        hipLaunchKernelGGL((mfma_indexer_kernel<false, false, true, false>), grid, dim3(THREADS), 0, st, q, kk, Ks, W,
+                           0, 0, 0LL, k, idx, vals, nullptr, nullptr, rg);
     return hipGetLastError();
 }
 

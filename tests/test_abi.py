@@ -15,7 +15,7 @@ HEADER = os.path.join(ROOT, "include", "ds4idx.h")
 def _declared():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(ds4idx_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(ds4idx_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_and_binding_agree():
@@ -265,3 +265,30 @@ def test_attention_null_or_misaligned_rejected(which):
 @pytest.mark.parametrize("kw", [dict(H=32), dict(H=96), dict(d_qk=512), dict(d_v=256)])
 def test_attention_unsupported_shapes(kw):
     assert _attn(_aprob(**kw)) == ds.ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("kw", [dict(q_dtype=ds.BF16), dict(k_dtype=ds.BF16), dict(T=0), dict(causal_offset=17)])
+def test_qfp8_invalid_problem_rejected(kw):
+    p = _prob(q_dtype=ds.FP8_E4M3, **{k: v for k, v in kw.items() if k != "q_dtype"})
+    if "q_dtype" in kw:
+        p.q_dtype = kw["q_dtype"]
+    st = ds.lib().ds4idx_select_qfp8(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, 512, FAKE, None, None)
+    assert st == ds.ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("which", [1, 2, 3, 4, 5, 7])
+def test_qfp8_null_pointers_rejected(which):
+    p = _prob(q_dtype=ds.FP8_E4M3)
+    args = [ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, 512, FAKE, None, None]
+    args[which] = None
+    assert ds.lib().ds4idx_select_qfp8(*args) == ds.ERR_INVALID_ARG
+
+
+def test_qfp8_unsupported_shapes():
+    for kw in (dict(H=32), dict(D=64)):
+        p = _prob(q_dtype=ds.FP8_E4M3, **kw)
+        assert ds.lib().ds4idx_select_qfp8(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, 512, FAKE, None,
+                                           None) == ds.ERR_UNSUPPORTED
+    p = _prob(q_dtype=ds.FP8_E4M3)
+    assert ds.lib().ds4idx_select_qfp8(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, 1024, FAKE, None,
+                                       None) == ds.ERR_UNSUPPORTED

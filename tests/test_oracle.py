@@ -370,3 +370,15 @@ def test_integer_config_scores_are_exact_halves():
     v = val[~np.isnan(val)]
     assert np.all(v * 2 == np.round(v * 2))
     assert np.all(np.abs(v) <= 4 * 2 * 64 * 9)
+
+
+def test_fp64_query_path_equals_fp32_path():
+    # queries given as exact doubles (the fp8 x fp8 scorer's dequantised
+    # queries) reduce to the pinned fp32 path on fp32-representable values
+    wl = W.tiny(seed=5, T=64, S=64)
+    a = oracle.select(wl)
+    q64 = W.Workload(wl.name, wl.q.astype(np.float64), wl.k, wl.k_scale, wl.w, wl.B, wl.T, wl.S, wl.H, wl.D,
+                     wl.offset, wl.topk, 3, wl.k_dtype, wl.chunks)
+    b = oracle.select(q64)
+    np.testing.assert_array_equal(a[0], b[0])
+    np.testing.assert_array_equal(a[1], b[1])

@@ -354,3 +354,24 @@ def attention(seed: int = 9, B: int = 1, T: int = 64, S: int = 4096, H: int = 64
         idx[gi.random(idx.shape) < pad_frac] = -1
     scale = d_qk ** -0.5 if softmax_scale is None else softmax_scale
     return AttnInputs(q, kv, idx, float(scale), d_v)
+
+
+# --------------------------------------------------------------------------- fp8 queries
+
+def fp8_queries(wl: Workload) -> Tuple[np.ndarray, np.ndarray]:
+    """The workload's queries in the storage encoding of the fp8 x fp8 scorer:
+    one E4M3 row of D codes per (stream, token, head) with its fp32 scale, by
+    the same per-row encoding as the fp8 key caches. Returns (codes uint8
+    [B,T,H,D], scale float32 [B,T,H])."""
+    q = bf16_bits_to_f32(wl.q) if wl.q_dtype == BF16 else np.asarray(wl.q, dtype=np.float32)
+    B, T, H, D = q.shape
+    codes, scale = quantize_e4m3_per_token(q.reshape(B * T * H, D))
+    return codes.reshape(B, T, H, D), scale.reshape(B, T, H)
+
+
+def integer_fp8_queries(seed: int, B: int, T: int, H: int, D: int, lo: int = -4, hi: int = 4):
+    """Integer query values in [lo, hi] as exact E4M3 codes with scale 1."""
+    g = _streams(seed, 1)[0]
+    v = _int_uniform(g, (B, T, H, D), lo, hi)
+    codes = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
+    return codes, np.ones((B, T, H), np.float32)
