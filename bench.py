@@ -20,7 +20,10 @@ over four streams; and sparse attention (ds4idx_sparse_attention) of one
 4096-query prefill chunk over 512 selected rows of a 65536-row latent cache,
 64 heads, against the bf16 MFMA peak; and the fp8 x fp8 variant of the 64k
 prefill (queries quantised per token and head by the key-cache writer, inside
-the timed step), with its recall of the exact selection on sampled rows.
+the timed step), with its recall of the exact selection on sampled rows; and
+the remaining indexer workloads, one ds4idx_select call each: the tiny fp32
+prefill (T = S = 1024, H = 4, D = 64), the 8k bf16 prefill and the 1M chunked
+prefill (2048 queries after 1,046,528 cached E4M3 keys).
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -52,6 +55,8 @@ def _parse():
     ap.add_argument("--no-ragged", action="store_true")
     ap.add_argument("--no-attention", action="store_true")
     ap.add_argument("--no-qfp8", action="store_true")
+    ap.add_argument("--no-others", action="store_true",
+                    help="skip the tiny, 8k and 1M prefill workloads")
     ap.add_argument("--attention-iters", type=int, default=10)
     ap.add_argument("--writer-iters", type=int, default=20)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -87,6 +92,20 @@ def measured_traffic(summary: str = "mfma_select_64k_traffic.txt", src: str = "m
         return int(float(kv["hbm_bytes_per_launch"]))
     except (KeyError, ValueError):
         return None
+
+
+def _to_device(wl, dev):
+    """A workload's host arrays as device tensors (bf16 bits viewed as bf16)."""
+    import numpy as np
+    import torch
+
+    import workloads as W
+
+    def cv(a, dt):
+        t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16) if dt == W.BF16 else torch.from_numpy(a)
+        return t.to(dev)
+    ks = None if wl.k_scale is None else torch.from_numpy(wl.k_scale).to(dev)
+    return cv(wl.q, wl.q_dtype), cv(wl.k, wl.k_dtype), ks, torch.from_numpy(wl.w).to(dev)
 
 
 def _flops_64k(wl):
@@ -381,6 +400,49 @@ def main():
             "hbm_frac": round(wbytes / (wmed * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
             "traffic": measured_traffic("k_cache_write_256k_traffic.txt", "k_cache_writer.hip")}
         del kin, cache, cscale
+
+    # ---------------------------------------------------------------- the other workloads
+    # The tiny fp32 prefill, the 8k bf16 prefill and the 1M chunked prefill
+    # (2048 queries after 1,046,528 cached E4M3 keys), one ds4idx_select call
+    # each, timed with HIP events on the launch stream.
+    if not args.no_others:
+        for name, make in (("tiny_1024", W.tiny), ("prefill_8k", W.prefill_bf16),
+                           ("prefill_1m", W.long_prefill)):
+            ow = make()
+            oq, ok_, oks, ow_ = _to_device(ow, dev)
+            host_bytes = ow.nbytes()
+            oidx = torch.empty((ow.B, ow.T, ow.topk), dtype=torch.int32, device=dev)
+            ovals = torch.empty((ow.B, ow.T, ow.topk), dtype=torch.float32, device=dev)
+            ows = ds.new_workspace(ds.make_problem(oq, ok_, ow.offset), ow.topk, dev)
+            iters = 3 if name == "prefill_1m" else 20
+
+            def ostep():
+                ds.select(oq, ok_, oks, ow_, ow.offset, ow.topk, idx=oidx, vals=ovals, workspace=ows,
+                          stream=stream)
+
+            ostep()
+            torch.cuda.synchronize()
+            oev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(iters)]
+            for e in oev:
+                e[0].record(stream)
+                ostep()
+                e[1].record(stream)
+            torch.cuda.synchronize()
+            ous = sorted(e[0].elapsed_time(e[1]) * 1e3 for e in oev)
+            omed = ous[len(ous) // 2]
+            opairs = ow.B * (ow.T * ow.offset + ow.T * (ow.T + 1) // 2)
+            oflop = 2 * ow.H * ow.D * opairs
+            extra[name] = {
+                "workload": f"B={ow.B} T={ow.T} S={ow.S} offset={ow.offset} H={ow.H} D={ow.D} "
+                            f"top-{ow.topk}, Q {W.DTYPE_NAMES[ow.q_dtype]}, K {W.DTYPE_NAMES[ow.k_dtype]}",
+                "us_median": round(omed, 2), "us_min": round(ous[0], 2),
+                "query_tok_s": round(ow.B * ow.T / (omed * 1e-6), 1), "flop": oflop,
+                "tflops": round(oflop / (omed * 1e-6) / 1e12, 1),
+                "mfma_frac": round(oflop / (omed * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                "input_bytes": int(host_bytes)}
+            if name == "prefill_1m":
+                extra[name]["traffic"] = measured_traffic("mfma_select_1m_kernel_stats.txt", "mfma_indexer.hip")
+            del oq, ok_, oks, ow_, oidx, ovals, ows, ow
 
     # ---------------------------------------------------------------- CPU oracle
     cpu = None
