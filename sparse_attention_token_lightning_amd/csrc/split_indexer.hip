@@ -12,7 +12,12 @@
 //    h*64 + ks*8 .. +7, which makes every lane read 64 contiguous bytes of its
 //    key (four 16-byte loads; the two halves of a wave cover each 128-byte fp8
 //    row). Queries use the same assignment. E4M3 widens to bf16 in registers.
-//    The next round's keys are in flight while the current one is scored.
+//    A ring of sub-blocks keeps three rounds of keys in flight while one is
+//    scored; the loop is fully unrolled and every load is unconditional, so
+//    the compiler's wait counts stay exact instead of draining the ring.
+//  * The row's query (16 KB) and head weights are staged once in LDS and the
+//    MFMA A operands read from there: the 96 registers this frees let the
+//    compiler keep the loads in flight (registers, not memory, limited it).
 //  * While the keys stream, every score's order key adds one count to a
 //    4096-bin LDS histogram of its top 12 bits (sign, exponent, 3 mantissa
 //    bits: eight bins per octave). These adds hide under the HBM wait. One
@@ -68,9 +73,15 @@ __device__ __forceinline__ int scx(int i) { return i + (i >> 4); }
 typedef __attribute__((__vector_size__(8 * sizeof(short)))) short bf16x8;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 
+constexpr int QROW = D + 8;  // bf16 per LDS query row: 272 B keeps 16-byte reads conflict-free
+
 struct SplitSmem {
     union {
-        uint32_t sc[PART + PART / 16];  // partition score keys (0 = no key) at scx(i)
+        struct {
+            uint32_t sc[PART + PART / 16];  // partition score keys (0 = no key) at scx(i)
+            uint16_t q[H * QROW];           // the row's query, head-major (scoring only)
+            float wl[H];                    // the row's head weights (scoring only)
+        };
         struct {
             uint32_t key[MSURV + MSURV / 16];  // merge survivors, index order (direct path: at scx)
             int idx[MSURV];
@@ -366,6 +377,11 @@ struct Raw {
     float scale;
 };
 
+// Every lane loads, whatever its key: keys at or past L read row L - 1
+// instead (L >= 1 wherever this is called), and their scores are dropped
+// when stored. With no branch around the loads, every ring slot is filled
+// by the same number of load instructions, so the compiler's wait counts
+// before a slot is read stay exact instead of draining all loads in flight.
 template <bool KFP8, bool SCALE>
 __device__ __forceinline__ void load_sub(Raw<KFP8> &r, const uint8_t *Kr, const float *Ksr,
                                          long long kbase, long long L, int lane)
@@ -373,17 +389,13 @@ __device__ __forceinline__ void load_sub(Raw<KFP8> &r, const uint8_t *Kr, const 
     constexpr int NV = KFP8 ? 4 : 8;
     constexpr int ROWB = KFP8 ? D : 2 * D;
     const long long key = kbase + (lane & 31);
-    if (key < L) {
-        const uint4 *src = reinterpret_cast<const uint4 *>(Kr + key * ROWB + (lane >> 5) * (ROWB / 2));
+    const long long kc = key < L ? key : L - 1;
+    const uint4 *src = reinterpret_cast<const uint4 *>(Kr + kc * ROWB + (lane >> 5) * (ROWB / 2));
 #pragma unroll
-        for (int j = 0; j < NV; ++j) r.v[j] = src[j];
-    } else {
-#pragma unroll
-        for (int j = 0; j < NV; ++j) r.v[j] = make_uint4(0, 0, 0, 0);
-    }
+    for (int j = 0; j < NV; ++j) r.v[j] = src[j];
     if (KFP8 && SCALE) {
         const long long sk = kbase + lane;
-        r.scale = sk < L ? Ksr[sk] : 1.0f;
+        r.scale = Ksr[sk < L ? sk : L - 1];
     }
 }
 
@@ -404,8 +416,7 @@ __device__ __forceinline__ bf16x8 b_operand(const Raw<KFP8> &r, int ks)
 
 // Partial score of one sub-block: this lane's 16 head rows of each head block.
 template <bool KFP8>
-__device__ __forceinline__ float score_sub(const Raw<KFP8> &r, const bf16x8 (&a)[2][8],
-                                           const float (&wv)[2][16])
+__device__ __forceinline__ float score_sub(const Raw<KFP8> &r, const uint16_t *qa, const float *wq)
 {
     f32x16 acc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
@@ -413,14 +424,16 @@ __device__ __forceinline__ float score_sub(const Raw<KFP8> &r, const bf16x8 (&a)
         const bf16x8 bk = b_operand<KFP8>(r, ks);
 #pragma unroll
         for (int hb = 0; hb < 2; ++hb)
-            acc[hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[hb][ks], bk, acc[hb], 0, 0, 0);
+            acc[hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                *reinterpret_cast<const bf16x8 *>(qa + hb * 32 * QROW + ks * 8), bk, acc[hb], 0, 0, 0);
     }
     float s4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-            s4[i & 3] = fmaf(wv[hb][i], __builtin_amdgcn_fmed3f(acc[hb][i], 0.0f, 3.0e38f), s4[i & 3]);
+            s4[i & 3] = fmaf(wq[hb * 32 + 8 * (i >> 2) + (i & 3)], __builtin_amdgcn_fmed3f(acc[hb][i], 0.0f, 3.0e38f),
+                             s4[i & 3]);
     return (s4[0] + s4[1]) + (s4[2] + s4[3]);
 }
 
@@ -474,53 +487,59 @@ __global__ __launch_bounds__(THREADS, 1) void split_indexer_kernel(
 
     for (int i = tid; i < HWORDS; i += THREADS) sm.hist[i] = 0;
     if (tid == 0) sm.nl = 0;
+    // The row's query (H x D bf16, 16 KB) into LDS: thread t copies two
+    // 16-byte pieces, 16 per head row.
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int piece = tid + THREADS * j;  // 0 .. H * D / 8 - 1
+        const int h = piece >> 4, d8 = piece & 15;
+        *reinterpret_cast<uint4 *>(&sm.q[h * QROW + d8 * 8]) =
+            *reinterpret_cast<const uint4 *>(Q + (r * H + h) * D + d8 * 8);
+    }
+    if (tid < H) sm.wl[tid] = W[r * H + tid];
     __syncthreads();
 
     // ---- score this wavefront's 1024 keys into sm.sc and the histogram
     const long long wbase = pbase + (long long)wid * WAVE_KEYS;
     const long long wkeys = L - wbase < 0 ? 0 : (L - wbase > WAVE_KEYS ? WAVE_KEYS : L - wbase);
     if (wkeys > 0) {
-        bf16x8 a[2][8];
-        float wv[2][16];
-        const int half = lane >> 5;
-#pragma unroll
-        for (int hb = 0; hb < 2; ++hb) {
-            const bf16x8 *qp = reinterpret_cast<const bf16x8 *>(
-                Q + ((r * H + hb * 32 + (lane & 31)) * D + half * 64));
-#pragma unroll
-            for (int ks = 0; ks < 8; ++ks) a[hb][ks] = qp[ks];
-#pragma unroll
-            for (int i = 0; i < 16; ++i) wv[hb][i] = W[r * H + hb * 32 + acc_row(i, lane)];
-        }
+        // accumulator row i of head block hb is head hb * 32 + acc_row(i, lane)
+        const float *wq = &sm.wl[4 * (lane >> 5)];
+        // A operands: head hb * 32 + lane % 32, dims (lane / 32) * 64 + ks * 8.
+        const uint16_t *qa = &sm.q[(lane & 31) * QROW + (lane >> 5) * 64];
+
         const uint8_t *Kr = K + (size_t)k0 * (KFP8 ? D : 2 * D);
         const float *Ksr = KFP8 ? Ks + (size_t)k0 : nullptr;
         // Sub-blocks of 32 keys; pairs (2j, 2j+1) share one half swap. A ring
         // of NBUF raw sub-blocks keeps NBUF-1 loads in flight.
         constexpr int NBUF = KFP8 ? 4 : 2;
         const int nsub = (int)((wkeys + 63) / 64) * 2;
+        // Slots past the wave's last sub-block reload that sub-block (cached)
+        // rather than skip the load, for the same reason.
         Raw<KFP8> buf[NBUF];
 #pragma unroll
         for (int i = 0; i < NBUF - 1; ++i) {
-            if (i < nsub) {
-                if (i & 1) load_sub<KFP8, false>(buf[i], Kr, Ksr, wbase + 32 * i, L, lane);
-                else load_sub<KFP8, true>(buf[i], Kr, Ksr, wbase + 32 * i, L, lane);
-            }
+            const int ic = i < nsub ? i : nsub - 1;
+            if (i & 1) load_sub<KFP8, false>(buf[i], Kr, Ksr, wbase + 32 * ic, L, lane);
+            else load_sub<KFP8, true>(buf[i], Kr, Ksr, wbase + 32 * ic, L, lane);
         }
         float prev = 0.0f, pscale = 1.0f;
-        for (int sb0 = 0; sb0 < nsub; sb0 += NBUF) {
+        // Fully unrolled over the wave's 2 * ROUNDS sub-blocks: with no loop
+        // back-edge the compiler counts the loads in flight exactly.
+#pragma unroll
+        for (int sb0 = 0; sb0 < 2 * ROUNDS; sb0 += NBUF) {
+            if (sb0 >= nsub) break;
 #pragma unroll
             for (int i = 0; i < NBUF; ++i) {
                 const int sb = sb0 + i;
+                const int nx = sb + NBUF - 1 < nsub ? sb + NBUF - 1 : nsub - 1;
+                if ((i + NBUF - 1) & 1)
+                    load_sub<KFP8, false>(buf[(i + NBUF - 1) % NBUF], Kr, Ksr, wbase + 32 * nx, L, lane);
+                else
+                    load_sub<KFP8, true>(buf[(i + NBUF - 1) % NBUF], Kr, Ksr, wbase + 32 * nx, L, lane);
                 if (sb < nsub) {
                     if (!(i & 1)) pscale = buf[i].scale;
-                    const int nx = sb + NBUF - 1;
-                    if (nx < nsub) {
-                        if ((i + NBUF - 1) & 1)
-                            load_sub<KFP8, false>(buf[(i + NBUF - 1) % NBUF], Kr, Ksr, wbase + 32 * nx, L, lane);
-                        else
-                            load_sub<KFP8, true>(buf[(i + NBUF - 1) % NBUF], Kr, Ksr, wbase + 32 * nx, L, lane);
-                    }
-                    const float part = score_sub<KFP8>(buf[i], a, wv);
+                    const float part = score_sub<KFP8>(buf[i], qa, wq);
                     if (i & 1) {
                         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(prev),
                                                                          __float_as_uint(part), false, false);
