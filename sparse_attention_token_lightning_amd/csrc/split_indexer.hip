@@ -25,10 +25,10 @@
 //    largest key and of its m-th largest (m = ceil(k / full partitions)).
 //  * The partition emits, in index order, every key at or above the lower
 //    edge of the k-th key's bin: a superset of its top k, usually ~15% more,
-//    with no exact selection. The m-th key is refined exactly from the few
-//    keys of its bin. Every partition that holds m keys publishes that key;
-//    the smallest of them is a lower bound on the row's k-th key, because
-//    the full partitions alone hold at least k keys at or above it.
+//    with no exact selection. Every partition that holds m keys publishes
+//    the lower edge of its m-th key's bin; the smallest of these is a lower
+//    bound on the row's k-th key, because the full partitions alone hold at
+//    least k keys at or above it.
 //  * The last workgroup of a row to finish (device-scope arrival counter)
 //    loads every candidate slot of the row in one batch, keeps those at or
 //    above the bound (index order preserved by a block scan over 64-slot
@@ -158,26 +158,6 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, SplitSmem &sm, u
     __syncthreads();
     const uint32_t before = waves_before(sm.wsum, total);
     return before + x - v;
-}
-
-// Two block-wide exclusive prefix sums at once (one barrier, same rule for
-// sm.wsum and sm.wmax as block_excl_scan): returns a's, b's prefix via bex.
-__device__ __forceinline__ uint32_t block_excl_scan2(uint32_t a, uint32_t b, SplitSmem &sm, uint32_t &ta,
-                                                     uint32_t &bex)
-{
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-    const uint32_t xa = wave_scan_incl(a, 0u, OpAdd{});
-    const uint32_t xb = wave_scan_incl(b, 0u, OpAdd{});
-    if (lane == 63) {
-        sm.wsum[wid] = xa;
-        sm.wmax[wid] = xb;
-    }
-    __syncthreads();
-    uint32_t tb;
-    const uint32_t pa = waves_before(sm.wsum, ta);
-    const uint32_t pb = waves_before(sm.wmax, tb);
-    bex = pb + xb - b;
-    return pa + xa - a;
 }
 
 // Block-wide AND and OR. One barrier.
@@ -589,45 +569,38 @@ __global__ __launch_bounds__(THREADS, 1) void split_indexer_kernel(
     const uint32_t edge1 = nkeys < c1 ? 1u : (f1.bin << HSHIFT);
     const uint32_t n1 = nkeys < c1 ? nkeys : f1.above + f1.cnt;
     const bool short_ok = n1 <= (uint32_t)s1;
-    const bool refine = has_m && fm.cnt <= (uint32_t)NLIST;
     const long long cb = (r * P + p) * (long long)slots;
     const long long cb1 = (r * P + p) * (long long)s1;
-    // This partition's m-th largest key (~0: no bound from it), published by
-    // wavefront 0 with the short list's edge, the largest key and the full
-    // list's length once the keys of the m-th key's bin are in sm.lk: exact
-    // when that bin is small, else its lower edge (still m keys at or above).
+    // This partition's bound, published with the short list's edge, the
+    // largest key and the full list's length: the lower edge of its m-th
+    // key's bin (m keys at or above it; ~0 = no bound from this partition).
+    // Ranking that bin's keys for the exact m-th key gave a slightly higher
+    // bound, but cost ~1.5 us on the last partition's critical path, while
+    // the merge reads every short-list slot whatever the bound.
     const uint32_t nfull = F <= (uint32_t)slots ? F : (uint32_t)topk;
     auto publish_meta = [&]() {
         if (wid != 0) return;
-        uint32_t tp = ~0u;
-        if (refine) {
-            uint32_t gt;
-            list_rank(sm, fm.cnt, mth - fm.above, tp, gt);
-        } else if (has_m) {
-            tp = fm.bin << HSHIFT;
-        }
+        const uint32_t tp = has_m ? (fm.bin << HSHIFT) : ~0u;
         if (lane == 0) {
             store_agent(&meta[2 * (r * P + p)], ((uint64_t)(short_ok ? edge1 : ~0u) << 32) | tp);
             store_agent(&meta[2 * (r * P + p) + 1], ((uint64_t)nfull << 32) | kmax);
         }
     };
     const bool direct = F <= (uint32_t)slots;
-    // Each thread counts its candidates for both lists and the m-th key's
-    // bin; one scan places them, and the lists are compacted in index order
+    // Each thread counts its candidates for both lists; one scan places
+    // them, and the lists are compacted in index order
     // in LDS, then written with coalesced stores: the full list when it fits
     // (else below, after an exact selection), the short list with its unused
     // slots empty.
-    uint32_t cf = 0, cs = 0, cm = 0;
+    uint32_t cf = 0, cs = 0;
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
         cf += u[j] >= edge ? 1u : 0u;
         cs += u[j] >= edge1 ? 1u : 0u;
-        cm += (u[j] != 0u && (u[j] >> HSHIFT) == fm.bin) ? 1u : 0u;
     }
-    uint32_t tf, tm;
-    const uint32_t exfs = block_excl_scan2(cf | (cs << 16), refine ? cm : 0u, sm, tf, tm);  // counts < 2^14
-    // The counts are exact, so positions stay below F <= slots, n1 <= s1
-    // and fm.cnt <= NLIST.
+    uint32_t tf;
+    const uint32_t exfs = block_excl_scan(cf | (cs << 16), sm, tf);  // counts < 2^14
+    // The counts are exact, so positions stay below F <= slots and n1 <= s1.
     const uint32_t ib = (uint32_t)ibase;
     if (direct) {
         uint32_t pf = exfs & 0xffffu;
@@ -641,19 +614,13 @@ __global__ __launch_bounds__(THREADS, 1) void split_indexer_kernel(
         for (int j = 0; j < KPT; ++j)
             if (u[j] >= edge1) sm.st.shortl[ps++] = ((uint64_t)(ib + j) << 32) | u[j];
     }
-    if (refine) {
-        uint32_t pm = tm;
-#pragma unroll
-        for (int j = 0; j < KPT; ++j)
-            if (u[j] != 0u && (u[j] >> HSHIFT) == fm.bin) sm.lk[pm++] = u[j];
-    }
     __syncthreads();
     if (direct)
         for (int i = tid; i < (int)F; i += THREADS) store_agent(&full_list[cb + i], sm.st.full[i]);
     if (short_ok)
         for (int i = tid; i < s1; i += THREADS)
             store_agent(&short_list[cb1 + i], i < (int)n1 ? sm.st.shortl[i] : (uint64_t)0);
-    publish_meta();  // before block_kth reuses sm.lk (its first barrier orders the two)
+    publish_meta();
     if (!direct) {
         // Too many keys share the k-th key's bin: exact selection of k.
         uint32_t tau, ties;
