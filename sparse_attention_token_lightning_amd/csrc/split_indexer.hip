@@ -463,7 +463,28 @@ __global__ __launch_bounds__(THREADS, 1) void split_indexer_kernel(
         k0 = (long long)b * S;
     }
     const long long pbase = (long long)p * PART;
-    const long long nvalid = L - pbase < 0 ? 0 : (L - pbase > PART ? PART : L - pbase);
+
+    // This wavefront's keys. The first ring slots are loaded before the query
+    // staging below, so the key stream starts at once. Sub-blocks of 32 keys;
+    // pairs (2j, 2j+1) share one half swap. A ring of NBUF raw sub-blocks
+    // keeps NBUF-1 loads in flight. Slots past the wave's last sub-block
+    // reload that sub-block (cached) rather than skip the load, so that every
+    // slot is filled by the same instructions (see load_sub).
+    const long long wbase = pbase + (long long)wid * WAVE_KEYS;
+    const long long wkeys = L - wbase < 0 ? 0 : (L - wbase > WAVE_KEYS ? WAVE_KEYS : L - wbase);
+    const uint8_t *Kr = K + (size_t)k0 * (KFP8 ? D : 2 * D);
+    const float *Ksr = KFP8 ? Ks + (size_t)k0 : nullptr;
+    constexpr int NBUF = KFP8 ? 4 : 2;
+    const int nsub = (int)((wkeys + 63) / 64) * 2;
+    Raw<KFP8> buf[NBUF];
+    if (wkeys > 0) {
+#pragma unroll
+        for (int i = 0; i < NBUF - 1; ++i) {
+            const int ic = i < nsub ? i : nsub - 1;
+            if (i & 1) load_sub<KFP8, false>(buf[i], Kr, Ksr, wbase + 32 * ic, L, lane);
+            else load_sub<KFP8, true>(buf[i], Kr, Ksr, wbase + 32 * ic, L, lane);
+        }
+    }
 
     for (int i = tid; i < HWORDS; i += THREADS) sm.hist[i] = 0;
     if (tid == 0) sm.nl = 0;
@@ -480,29 +501,11 @@ __global__ __launch_bounds__(THREADS, 1) void split_indexer_kernel(
     __syncthreads();
 
     // ---- score this wavefront's 1024 keys into sm.sc and the histogram
-    const long long wbase = pbase + (long long)wid * WAVE_KEYS;
-    const long long wkeys = L - wbase < 0 ? 0 : (L - wbase > WAVE_KEYS ? WAVE_KEYS : L - wbase);
     if (wkeys > 0) {
         // accumulator row i of head block hb is head hb * 32 + acc_row(i, lane)
         const float *wq = &sm.wl[4 * (lane >> 5)];
         // A operands: head hb * 32 + lane % 32, dims (lane / 32) * 64 + ks * 8.
         const uint16_t *qa = &sm.q[(lane & 31) * QROW + (lane >> 5) * 64];
-
-        const uint8_t *Kr = K + (size_t)k0 * (KFP8 ? D : 2 * D);
-        const float *Ksr = KFP8 ? Ks + (size_t)k0 : nullptr;
-        // Sub-blocks of 32 keys; pairs (2j, 2j+1) share one half swap. A ring
-        // of NBUF raw sub-blocks keeps NBUF-1 loads in flight.
-        constexpr int NBUF = KFP8 ? 4 : 2;
-        const int nsub = (int)((wkeys + 63) / 64) * 2;
-        // Slots past the wave's last sub-block reload that sub-block (cached)
-        // rather than skip the load, for the same reason.
-        Raw<KFP8> buf[NBUF];
-#pragma unroll
-        for (int i = 0; i < NBUF - 1; ++i) {
-            const int ic = i < nsub ? i : nsub - 1;
-            if (i & 1) load_sub<KFP8, false>(buf[i], Kr, Ksr, wbase + 32 * ic, L, lane);
-            else load_sub<KFP8, true>(buf[i], Kr, Ksr, wbase + 32 * ic, L, lane);
-        }
         float prev = 0.0f, pscale = 1.0f;
         // Fully unrolled over the wave's 2 * ROUNDS sub-blocks: with no loop
         // back-edge the compiler counts the loads in flight exactly.
