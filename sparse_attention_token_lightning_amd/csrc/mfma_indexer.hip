@@ -27,18 +27,18 @@
 //    v_permlane32_swap and v_permlane16_swap then add the other three lane
 //    groups' heads so that lane l holds the score of key l of the pair. The
 //    causal mask (key <= offset + t) is applied per lane.
-//  * Streaming top-k per token. A candidate buffer of 1024 (score, index)
-//    slots per token lives in LDS. A score enters only if it beats the
+//  * Streaming top-k per token. A candidate buffer of CAP (score, index)
+//    slots per token lives in LDS. A score enters only if it reaches the
 //    token's running threshold (ballot + mbcnt place it in ascending key
-//    order). When the buffer is nearly full, the wavefront finds the k-th
-//    largest key by radix selection over the buffer (four 8-bit digits of an
-//    order-preserving key) and compacts it stably to exactly k entries: those
-//    above the k-th key, plus the lowest-index entries equal to it. The k-th
-//    score becomes the new threshold. A new key, with a higher index than
-//    everything seen, can only enter the top-k by beating that score
-//    strictly, so no candidate is lost and equal scores keep going to the
-//    lower index. At the end the same selection runs once more and the
-//    buffer, already in index order, is the output. No sort anywhere.
+//    order). When the buffer is nearly full, the wavefront raises the
+//    threshold to the highest 8-bit histogram edge that keeps k entries at
+//    or above it, and compacts the buffer stably; nothing that can still
+//    reach the top k is dropped. If that frees too little, the exact k-th
+//    key is found by radix selection and the buffer cut to exactly k
+//    entries; later keys, all with higher indices, must then beat it
+//    strictly, so equal scores keep going to the lower index. At the end the
+//    exact selection runs once more and the buffer, already in index order,
+//    is the output. No sort anywhere.
 #include "device_common.h"
 #include "kernels.h"
 #include "wave_select.h"
