@@ -108,6 +108,32 @@ def _to_device(wl, dev):
     return cv(wl.q, wl.q_dtype), cv(wl.k, wl.k_dtype), ks, torch.from_numpy(wl.w).to(dev)
 
 
+def _hold_calibrate():
+    """Cycles of torch.cuda._sleep per millisecond on this GPU."""
+    import torch
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda._sleep(1 << 20)
+    e[0].record()
+    torch.cuda._sleep(1 << 22)
+    e[1].record()
+    torch.cuda.synchronize()
+    return (1 << 22) / max(e[0].elapsed_time(e[1]), 1e-3)
+
+
+_HOLD_CYCLES_PER_MS = None
+
+
+def _hold(ms: float = 8.0):
+    """Keep the GPU busy for `ms` on the current stream, so the host can queue
+    a timed loop of short calls before the first of them runs: their HIP
+    events then time the device, not the host's Python and launch latency."""
+    import torch
+    global _HOLD_CYCLES_PER_MS
+    if _HOLD_CYCLES_PER_MS is None:
+        _HOLD_CYCLES_PER_MS = _hold_calibrate()
+    torch.cuda._sleep(int(_HOLD_CYCLES_PER_MS * ms))
+
+
 def _flops_64k(wl):
     """Algorithmic work of one step: 2*H*D flop per visible (query, key) pair;
     chunk c's query j (of T_c) sees offset_c + j + 1 keys."""
@@ -247,6 +273,7 @@ def main():
         torch.cuda.synchronize()
         dev_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
                   for _ in range(args.decode_iters)]
+        _hold()
         for i in range(args.decode_iters):
             dev_ev[i][0].record(stream)
             dstep(i)
@@ -286,6 +313,7 @@ def main():
             torch.cuda.synchronize()
             rev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
                    for _ in range(args.decode_iters)]
+            _hold()
             for i in range(args.decode_iters):
                 rev[i][0].record(stream)
                 rstep(i)
@@ -325,6 +353,7 @@ def main():
             pstep()
         torch.cuda.synchronize()
         pev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(20)]
+        _hold()
         for e in pev:
             e[0].record(stream)
             pstep()
@@ -353,6 +382,7 @@ def main():
             ds.sparse_attention(aq, akv, aidx, at.softmax_scale, at.d_v, out=aout, stream=stream)
         torch.cuda.synchronize()
         aev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.attention_iters)]
+        _hold()
         for e in aev:
             e[0].record(stream)
             ds.sparse_attention(aq, akv, aidx, at.softmax_scale, at.d_v, out=aout, stream=stream)
@@ -385,6 +415,7 @@ def main():
         torch.cuda.synchronize()
         wev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
                for _ in range(args.writer_iters)]
+        _hold()
         for e in wev:
             e[0].record(stream)
             ds.k_cache_write(kin, cache, cscale, stream=stream)
@@ -423,6 +454,7 @@ def main():
             ostep()
             torch.cuda.synchronize()
             oev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(iters)]
+            _hold()
             for e in oev:
                 e[0].record(stream)
                 ostep()
