@@ -123,6 +123,8 @@ __device__ __forceinline__ uint64_t slot(uint32_t key, long long index)
     return ((uint64_t)(uint32_t)index << 32) | key;
 }
 
+// Row (head within the 32-head block) of accumulator element i of a lane in
+// a 32 x 32 MFMA result.
 __device__ __forceinline__ int acc_row(int i, int lane) { return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3); }
 
 template <bool HI>
@@ -396,7 +398,7 @@ __device__ __forceinline__ bf16x8 b_operand(const Raw<KFP8> &r, int ks)
 
 // Partial score of one sub-block: this lane's 16 head rows of each head block.
 template <bool KFP8>
-__device__ __forceinline__ float score_sub(const Raw<KFP8> &r, const uint16_t *qa, const float *wq)
+__device__ __forceinline__ float score_sub(const Raw<KFP8> &r, const uint16_t *qa, const float *wl, int lane)
 {
     f32x16 acc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
@@ -412,7 +414,7 @@ __device__ __forceinline__ float score_sub(const Raw<KFP8> &r, const uint16_t *q
     for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-            s4[i & 3] = fmaf(wq[hb * 32 + 8 * (i >> 2) + (i & 3)], __builtin_amdgcn_fmed3f(acc[hb][i], 0.0f, 3.0e38f),
+            s4[i & 3] = fmaf(wl[hb * 32 + acc_row(i, lane)], __builtin_amdgcn_fmed3f(acc[hb][i], 0.0f, 3.0e38f),
                              s4[i & 3]);
     return (s4[0] + s4[1]) + (s4[2] + s4[3]);
 }
@@ -502,8 +504,6 @@ __global__ __launch_bounds__(THREADS, 1) void split_indexer_kernel(
 
     // ---- score this wavefront's 1024 keys into sm.sc and the histogram
     if (wkeys > 0) {
-        // accumulator row i of head block hb is head hb * 32 + acc_row(i, lane)
-        const float *wq = &sm.wl[4 * (lane >> 5)];
         // A operands: head hb * 32 + lane % 32, dims (lane / 32) * 64 + ks * 8.
         const uint16_t *qa = &sm.q[(lane & 31) * QROW + (lane >> 5) * 64];
         float prev = 0.0f, pscale = 1.0f;
@@ -522,7 +522,7 @@ __global__ __launch_bounds__(THREADS, 1) void split_indexer_kernel(
                     load_sub<KFP8, true>(buf[(i + NBUF - 1) % NBUF], Kr, Ksr, wbase + 32 * nx, L, lane);
                 if (sb < nsub) {
                     if (!(i & 1)) pscale = buf[i].scale;
-                    const float part = score_sub<KFP8>(buf[i], qa, wq);
+                    const float part = score_sub<KFP8>(buf[i], qa, sm.wl, lane);
                     if (i & 1) {
                         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(prev),
                                                                          __float_as_uint(part), false, false);
