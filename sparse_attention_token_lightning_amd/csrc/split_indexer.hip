@@ -13,8 +13,9 @@
 //    key (four 16-byte loads; the two halves of a wave cover each 128-byte fp8
 //    row). Queries use the same assignment. E4M3 widens to bf16 in registers.
 //    A ring of sub-blocks keeps three rounds of keys in flight while one is
-//    scored; the loop is fully unrolled and every load is unconditional, so
-//    the compiler's wait counts stay exact instead of draining the ring.
+//    scored (one for bf16 keys); the loop is unrolled and every load is
+//    unconditional, so the compiler's wait counts stay exact instead of
+//    draining the ring.
 //  * The row's query (16 KB) and head weights are staged once in LDS and the
 //    MFMA A operands read from there: the 96 registers this frees let the
 //    compiler keep the loads in flight (registers, not memory, limited it).
@@ -507,8 +508,9 @@ __global__ __launch_bounds__(THREADS, 1) void split_indexer_kernel(
         // A operands: head hb * 32 + lane % 32, dims (lane / 32) * 64 + ks * 8.
         const uint16_t *qa = &sm.q[(lane & 31) * QROW + (lane >> 5) * 64];
         float prev = 0.0f, pscale = 1.0f;
-        // Fully unrolled over the wave's 2 * ROUNDS sub-blocks: with no loop
-        // back-edge the compiler counts the loads in flight exactly.
+        // Unrolled over the wave's 2 * ROUNDS sub-blocks, fully for E4M3 keys
+        // (bf16 keys' larger sub-blocks exceed the unroller's limit): with no
+        // loop back-edge the compiler counts the loads in flight exactly.
 #pragma unroll
         for (int sb0 = 0; sb0 < 2 * ROUNDS; sb0 += NBUF) {
             if (sb0 >= nsub) break;
