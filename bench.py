@@ -399,7 +399,8 @@ def main():
             "query_tok_s": round(4096 / (amed * 1e-6), 1), "flop": aflop,
             "tflops": round(aflop / (amed * 1e-6) / 1e12, 1),
             "mfma_frac": round(aflop / (amed * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4),
-            "gathered_GB_s": round(nsel * at.q.shape[-1] * 2 / (amed * 1e-6) / 1e9, 1)}
+            "gathered_GB_s": round(nsel * at.q.shape[-1] * 2 / (amed * 1e-6) / 1e9, 1),
+            "traffic": measured_traffic("sparse_attention_4096_traffic.txt", "sparse_attention.hip")}
         del aq, akv, aidx, aout
 
     # ---------------------------------------------------------------- key-cache writer

@@ -387,12 +387,18 @@ __global__ __launch_bounds__(THREADS, 1) void mfma_indexer_kernel(
                 for (int n = 0; n < 2; ++n)
                     nb[n] = *reinterpret_cast<const bf16x8 *>(kp + 16 * n * KROW + (ks + 1) * 32);
             }
+            // The wavefront issuing its MFMAs takes priority over the other
+            // wavefront of the SIMD, whose reduction (VALU) then fills the
+            // matrix pipe's gaps instead of delaying the next MFMA (+2.5% on
+            // the 64k step).
+            __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int n = 0; n < 2; ++n)
 #pragma unroll
                 for (int m = 0; m < 4; ++m)
                     acc[h][n][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[m][ks], bk[n],
                                                                           ks ? acc[h][n][m] : f32x4{}, 0, 0, 0);
+            __builtin_amdgcn_s_setprio(0);
             const int n = ks >> 1;  // 8 of the 32 elements of the half being reduced
 #pragma unroll
             for (int mm = 0; mm < 2; ++mm) {
