@@ -58,6 +58,8 @@ def _parse():
     ap.add_argument("--no-others", action="store_true",
                     help="skip the tiny, 8k and 1M prefill workloads")
     ap.add_argument("--attention-iters", type=int, default=10)
+    ap.add_argument("--warm-ms", type=float, default=30.0,
+                    help="device time of the untimed calls queued before each per-call timed loop")
     ap.add_argument("--writer-iters", type=int, default=20)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, copy 256 MiB once (the reference kernel that "
@@ -108,30 +110,37 @@ def _to_device(wl, dev):
     return cv(wl.q, wl.q_dtype), cv(wl.k, wl.k_dtype), ks, torch.from_numpy(wl.w).to(dev)
 
 
-def _hold_calibrate():
-    """Cycles of torch.cuda._sleep per millisecond on this GPU."""
+def _time_calls(call, n: int, stream, warm_ms: float = 30.0):
+    """Device time in microseconds, sorted, of n calls call(i) on `stream`.
+
+    One untimed call gives the duration. Then enough untimed calls to fill about
+    warm_ms of device time are queued right before the n timed ones, with no
+    synchronisation between them. Queuing a call takes the host 10-20 us, less
+    than any of these calls runs, so the device never waits for the host inside
+    a timed event pair, and the timed calls run at the clocks of sustained load.
+    (A spin kernel in place of the warm-up calls leaves the GPU near idle for its
+    length, and the calls after it measured up to 12% slower while the clocks
+    settled; their medians then disagreed with wall-clock time per call.)"""
+    import math
+
     import torch
-    e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    torch.cuda._sleep(1 << 20)
-    e[0].record()
-    torch.cuda._sleep(1 << 22)
-    e[1].record()
+    call(0)
     torch.cuda.synchronize()
-    return (1 << 22) / max(e[0].elapsed_time(e[1]), 1e-3)
-
-
-_HOLD_CYCLES_PER_MS = None
-
-
-def _hold(ms: float = 8.0):
-    """Keep the GPU busy for `ms` on the current stream, so the host can queue
-    a timed loop of short calls before the first of them runs: their HIP
-    events then time the device, not the host's Python and launch latency."""
-    import torch
-    global _HOLD_CYCLES_PER_MS
-    if _HOLD_CYCLES_PER_MS is None:
-        _HOLD_CYCLES_PER_MS = _hold_calibrate()
-    torch.cuda._sleep(int(_HOLD_CYCLES_PER_MS * ms))
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    e[0].record(stream)
+    call(1)
+    e[1].record(stream)
+    torch.cuda.synchronize()
+    nwarm = max(2, min(2000, math.ceil(warm_ms / max(e[0].elapsed_time(e[1]), 1e-3))))
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n)]
+    for i in range(nwarm):
+        call(2 + i)
+    for j, x in enumerate(ev):
+        x[0].record(stream)
+        call(2 + nwarm + j)
+        x[1].record(stream)
+    torch.cuda.synchronize()
+    return sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
 
 
 def _flops_64k(wl):
@@ -268,18 +277,7 @@ def main():
             a = sets[i % 3]
             ds.select(*a, dl.offset, dl.topk, idx=idd, vals=vd, workspace=wsd, stream=stream)
 
-        for i in range(6):
-            dstep(i)
-        torch.cuda.synchronize()
-        dev_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
-                  for _ in range(args.decode_iters)]
-        _hold()
-        for i in range(args.decode_iters):
-            dev_ev[i][0].record(stream)
-            dstep(i)
-            dev_ev[i][1].record(stream)
-        torch.cuda.synchronize()
-        dus = sorted(e[0].elapsed_time(e[1]) * 1e3 for e in dev_ev)
+        dus = _time_calls(dstep, args.decode_iters, stream, args.warm_ms)
         dbytes = dl.k.nbytes + dl.k_scale.nbytes + dl.q.nbytes + dl.w.nbytes + dl.B * dl.topk * 8
         med = dus[len(dus) // 2]
         extra["decode_256k"] = {"us_median": round(med, 2), "us_min": round(dus[0], 2),
@@ -308,18 +306,7 @@ def main():
                 ds.select_varlen(rq, a[1], a[2], rw, cu_q, cu_k, int(lens.max()), dl.topk, idx=ridx,
                                  vals=rvals, workspace=rws, stream=stream)
 
-            for i in range(6):
-                rstep(i)
-            torch.cuda.synchronize()
-            rev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
-                   for _ in range(args.decode_iters)]
-            _hold()
-            for i in range(args.decode_iters):
-                rev[i][0].record(stream)
-                rstep(i)
-                rev[i][1].record(stream)
-            torch.cuda.synchronize()
-            rus = sorted(e[0].elapsed_time(e[1]) * 1e3 for e in rev)
+            rus = _time_calls(rstep, args.decode_iters, stream, args.warm_ms)
             rbytes = int(lens.sum()) * (dl.D + 4) + 64 * (dl.H * dl.D * 2 + dl.H * 4) + 64 * dl.topk * 8
             rmed = rus[len(rus) // 2]
             extra["ragged_decode_64"] = {
@@ -345,21 +332,11 @@ def main():
         pidx = torch.empty((2048, wl.topk), dtype=torch.int32, device=dev)
         pvals = torch.empty((2048, wl.topk), dtype=torch.float32, device=dev)
 
-        def pstep():
+        def pstep(i):
             ds.select_varlen(pq, pk, pks, pw, pcu_q, pcu_k, int(Sk.max()), wl.topk, idx=pidx,
                              vals=pvals, stream=stream)
 
-        for _ in range(3):
-            pstep()
-        torch.cuda.synchronize()
-        pev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(20)]
-        _hold()
-        for e in pev:
-            e[0].record(stream)
-            pstep()
-            e[1].record(stream)
-        torch.cuda.synchronize()
-        pus = sorted(e[0].elapsed_time(e[1]) * 1e3 for e in pev)
+        pus = _time_calls(pstep, 20, stream, args.warm_ms)
         pairs_r = int(sum(t * (s_ - t) + t * (t + 1) // 2 for t, s_ in zip(Tq, Sk)))
         pflop = 2 * wl.H * wl.D * pairs_r
         pmed = pus[len(pus) // 2]
@@ -378,17 +355,10 @@ def main():
         akv = torch.from_numpy(at.kv.view(np.int16)).view(torch.bfloat16).to(dev)
         aidx = torch.from_numpy(at.idx).to(dev)
         aout = torch.empty((1, 4096, 64, at.d_v), dtype=torch.bfloat16, device=dev)
-        for _ in range(2):
+        def astep(i):
             ds.sparse_attention(aq, akv, aidx, at.softmax_scale, at.d_v, out=aout, stream=stream)
-        torch.cuda.synchronize()
-        aev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.attention_iters)]
-        _hold()
-        for e in aev:
-            e[0].record(stream)
-            ds.sparse_attention(aq, akv, aidx, at.softmax_scale, at.d_v, out=aout, stream=stream)
-            e[1].record(stream)
-        torch.cuda.synchronize()
-        aus = sorted(e[0].elapsed_time(e[1]) * 1e3 for e in aev)
+
+        aus = _time_calls(astep, args.attention_iters, stream, args.warm_ms)
         nsel = int((at.idx >= 0).sum())
         aflop = 2 * 64 * nsel * (at.q.shape[-1] + at.d_v)
         amed = aus[len(aus) // 2]
@@ -411,18 +381,10 @@ def main():
         del kn
         cache = torch.empty((n_tok, kdim), dtype=torch.uint8, device=dev)
         cscale = torch.empty((n_tok,), dtype=torch.float32, device=dev)
-        for _ in range(3):
+        def wstep(i):
             ds.k_cache_write(kin, cache, cscale, stream=stream)
-        torch.cuda.synchronize()
-        wev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
-               for _ in range(args.writer_iters)]
-        _hold()
-        for e in wev:
-            e[0].record(stream)
-            ds.k_cache_write(kin, cache, cscale, stream=stream)
-            e[1].record(stream)
-        torch.cuda.synchronize()
-        wus = sorted(e[0].elapsed_time(e[1]) * 1e3 for e in wev)
+
+        wus = _time_calls(wstep, args.writer_iters, stream, args.warm_ms)
         wbytes = n_tok * (2 * kdim + kdim + 4)
         wmed = wus[len(wus) // 2]
         extra["k_cache_write_256k"] = {
@@ -448,20 +410,11 @@ def main():
             ows = ds.new_workspace(ds.make_problem(oq, ok_, ow.offset), ow.topk, dev)
             iters = 3 if name == "prefill_1m" else 20
 
-            def ostep():
+            def ostep(i):
                 ds.select(oq, ok_, oks, ow_, ow.offset, ow.topk, idx=oidx, vals=ovals, workspace=ows,
                           stream=stream)
 
-            ostep()
-            torch.cuda.synchronize()
-            oev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(iters)]
-            _hold()
-            for e in oev:
-                e[0].record(stream)
-                ostep()
-                e[1].record(stream)
-            torch.cuda.synchronize()
-            ous = sorted(e[0].elapsed_time(e[1]) * 1e3 for e in oev)
+            ous = _time_calls(ostep, iters, stream, args.warm_ms)
             omed = ous[len(ous) // 2]
             opairs = ow.B * (ow.T * ow.offset + ow.T * (ow.T + 1) // 2)
             oflop = 2 * ow.H * ow.D * opairs
