@@ -20,7 +20,7 @@ over four streams; and sparse attention (ds4idx_sparse_attention) of one
 4096-query prefill chunk over 512 selected rows of a 65536-row latent cache,
 64 heads, against the bf16 MFMA peak; and the fp8 x fp8 variant of the 64k
 prefill (queries quantised per token and head by the key-cache writer, inside
-the timed step), with its recall of the exact selection on sampled rows; and
+the timed step), with its recall of the bf16-query selection over all rows; and
 the remaining indexer workloads, one ds4idx_select call each: the tiny fp32
 prefill (T = S = 1024, H = 4, D = 64), the 8k bf16 prefill and the 1M chunked
 prefill (2048 queries after 1,046,528 cached E4M3 keys).
@@ -256,6 +256,19 @@ def main():
             "ms_per_step": round(qms, 3), "query_tok_s": round(wl.T / (qms * 1e-3), 1),
             "tflops": round(flops / (qms * 1e-3) / 1e12, 1),
             "fp8_frac": round(flops / (qms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4)}
+        # Cost of the fp8 queries: the share of each row's bf16-query selection (the timed
+        # step's output, parity-checked against the oracle by the tests) that the fp8
+        # selection keeps, over all 65536 rows. Both index lists hold distinct
+        # positions, so after sorting their concatenation every common position is an
+        # adjacent equal pair.
+        both = torch.sort(torch.cat([idx.reshape(wl.T, wl.topk), idx8.reshape(wl.T, wl.topk)], dim=1),
+                          dim=1).values
+        common = ((both[:, 1:] == both[:, :-1]) & (both[:, 1:] >= 0)).sum(dim=1)
+        nvalid = (idx.reshape(wl.T, wl.topk) >= 0).sum(dim=1)
+        recall = (common.double() / nvalid.double()).cpu().numpy()
+        extra["select_qfp8_64k"]["recall_of_bf16_query_top512"] = round(float(recall.mean()), 4)
+        extra["select_qfp8_64k"]["recall_min_row"] = round(float(recall.min()), 4)
+        del both, common, nvalid
 
     # ---------------------------------------------------------------- 256k decode
     if not args.no_decode:
@@ -449,13 +462,6 @@ def main():
         t_cpu = time.perf_counter() - t0
         keys = int(sum(wl.offset + r + 1 for r in rows))
         full_s = t_cpu * pairs / keys
-        if idx8 is not None:  # parity cost of the fp8 queries: overlap with the exact selection
-            prow = np.sort(rng.choice(wl.T, 8, replace=False)).astype(np.int64)
-            oi, _, _, _, _ = oracle.select(wl, rows=prow)
-            g8 = idx8.reshape(wl.T, wl.topk).cpu().numpy()[prow]
-            rec = [len(set(g8[n]) & set(oi[n])) / float(wl.topk) for n in range(len(prow))]
-            extra["select_qfp8_64k"]["recall_of_exact_top512"] = round(float(np.mean(rec)), 4)
-            extra["select_qfp8_64k"]["recall_rows"] = [int(r) for r in prow]
         cpu = {"value": round(wl.T / full_s, 2), "unit": "query-tok/s", "cores": int(used),
                "kind": "oracle",
                "sample": f"{n} uniformly drawn query rows of the 64k prefill ({keys} visible keys, "
