@@ -26,7 +26,8 @@
 //    as B operands.
 //  * Online softmax in the log2 domain: per-head chunk maxima and sums go
 //    through LDS; every wavefront keeps the running max and sum of the heads
-//    its outputs cover.
+//    its outputs cover, and rescales its outputs only when a head's max rises
+//    by more than a factor 2^8.
 //  * Values, O^T = V^T P^T. The S^T accumulator already has the layout of a
 //    B operand (lane = head, 4 consecutive keys per lane group) under a fixed
 //    permutation of the chunk's 32 keys; the V^T fragments are read from the
@@ -46,6 +47,7 @@ constexpr int ATHREADS = 512;
 constexpr int MAIN16 = DV / 8;     // 16-byte pieces of a row's first 512 values (64)
 constexpr int TAIL16 = (DQK - DV) / 8;  // pieces of the rest (8)
 constexpr int NQK = DQK / 32;      // k-steps of the score contraction
+constexpr float RESCALE_LOG2 = 8.0f;  // largest log2 probability before O is rescaled
 
 static_assert(MAIN16 == 64 && TAIL16 == 8, "one wavefront instruction per row head, per 8 row tails");
 
@@ -231,13 +233,22 @@ __global__ __launch_bounds__(ATHREADS, 1) void sparse_attention_kernel(
         if (lane < 16) sm.pmax[kt][ht * 16 + lane] = mx;
         __syncthreads();
 
+        // Lazy rescaling: a head keeps its running max until a chunk's max
+        // exceeds it by more than RESCALE_LOG2, so the probabilities stay
+        // below 2^RESCALE_LOG2 (exact in fp32; bf16 keeps its relative
+        // precision) and O is rescaled only when some head's max jumps,
+        // in practice after the first chunk only.
         float m_new[4], m_use[4], alpha[4];
+        bool moved = false;
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
             const int hh = a * 16 + (lane & 15);
-            m_new[a] = fmaxf(m_run[a], fmaxf(sm.pmax[0][hh], sm.pmax[1][hh]));
+            const float cm = fmaxf(sm.pmax[0][hh], sm.pmax[1][hh]);
+            const bool up = cm > m_run[a] + RESCALE_LOG2;  // always, from -inf, once a key is valid
+            m_new[a] = up ? cm : m_run[a];
             m_use[a] = m_new[a] == -INFINITY ? 0.0f : m_new[a];
-            alpha[a] = exp2f(m_run[a] - m_use[a]);
+            alpha[a] = up ? exp2f(m_run[a] - m_use[a]) : 1.0f;
+            moved = moved || up;
         }
         float pr[4], ps = 0.0f;
 #pragma unroll
@@ -251,13 +262,11 @@ __global__ __launch_bounds__(ATHREADS, 1) void sparse_attention_kernel(
             make_uint2(pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]));
         __syncthreads();
 
-        bool moved = false;
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
             const int hh = a * 16 + (lane & 15);
             l_run[a] = l_run[a] * alpha[a] + (sm.psum[0][hh] + sm.psum[1][hh]);
             m_run[a] = m_new[a];
-            moved = moved || alpha[a] != 1.0f;
         }
         if (wave_ballot(moved)) {  // a head's running max rose: rescale
 #pragma unroll
