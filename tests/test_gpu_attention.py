@@ -73,6 +73,34 @@ def test_peaked_scores():
     check(a, go, glse)
 
 
+@pytest.mark.parametrize("direction", [1.0, -1.0])
+def test_scores_rising_by_chunk(direction):
+    # Scores (log2 units) that move by a per-head step from one 32-row chunk
+    # of the selection to the next. Steps of 7 stay within the running max's
+    # slack of 8, so the probabilities grow to 2^7 without a rescale; steps of
+    # 10.5, 14 and 17.5 force a rescale at every chunk. Falling scores
+    # (direction -1) never rescale after the first chunk. Only the last dim of
+    # q is nonzero, so the score of row j is q[-1] * kv[j, -1] * scale; that
+    # dim lies outside the values, so the tolerance stays set by the N(0,1)
+    # values.
+    B, T, S, H, k = 1, 4, 1024, 64, 512
+    a = W.attention(seed=22, B=B, T=T, S=S, H=H, topk=k, softmax_scale=1.0)
+    g = np.random.Generator(np.random.PCG64(23))
+    ln2 = float(np.log(2.0))
+    sel = np.sort(g.choice(S, k, replace=False))
+    a.idx[:] = sel[None, None, :]
+    kv = W.bf16_bits_to_f32(a.kv)
+    z = direction * 7.0 * (np.arange(k) // 32) + g.uniform(-0.5, 0.5, k)  # log2 units for q0 = 1
+    kv[0, sel, -1] = (z * ln2).astype(np.float32)
+    a.kv[:] = W.to_bf16_bits(kv)
+    q = np.zeros((B, T, H, a.q.shape[-1]), np.float32)
+    q[..., -1] = (1.0 + 0.5 * (np.arange(H) % 4))[None, None, :]  # steps 7, 10.5, 14, 17.5
+    a.q[:] = W.to_bf16_bits(q)
+    _say(f"sparse attention scores moving by chunk, direction {direction}")
+    go, glse = run_attention(a)
+    check(a, go, glse)
+
+
 def test_edge_rows():
     # no valid entry; one valid entry (out is that row's values exactly);
     # out-of-range entries; duplicates of the same position
