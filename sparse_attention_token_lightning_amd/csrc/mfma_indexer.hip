@@ -16,12 +16,14 @@
 //    scale is kept aside and applied once to the head-reduced score (allowed
 //    since the scale is positive, so it commutes with the ReLU).
 //  * Contraction. v_mfma_f32_16x16x32_bf16 with heads on M (four 16-head
-//    tiles) and keys on N: a 64-key pair is 2 x 2 tiles of 16 keys, so each
-//    k-step issues 16 independent MFMAs (4 k-steps over D = 128) on four
-//    B fragments read once from LDS, fp32 accumulation. Many short chains
-//    keep the matrix pipe fed while the other wavefront on the SIMD runs its
-//    epilogue (with two 32x32 tiles per head block the epilogue did not
-//    overlap and cost a fifth of the time).
+//    tiles) and keys on N, fp32 accumulation. A 64-key pair is two 32-key
+//    halves of 2 key tiles x 4 head tiles: each of the 4 k-steps over
+//    D = 128 issues a half's 8 independent MFMAs on two B fragments read
+//    once from LDS, interleaved one MFMA to two VALU instructions with the
+//    reduction of the other half, at raised wavefront priority. The
+//    wavefront keeps its own matrix work going first, and the other
+//    wavefront of the SIMD fills the gaps (with two 32x32 tiles per head
+//    block the epilogue did not overlap and cost a fifth of the time).
 //  * Epilogue in registers. Each lane holds 4 heads of each of 4 head tiles
 //    for 4 keys: ReLU (one v_med3), times w[t,h] (fp32), summed in-lane.
 //    v_permlane32_swap and v_permlane16_swap then add the other three lane
