@@ -1,0 +1,55 @@
+"""Host logic of bench.py (no GPU): the one-GPU guard and the gate that
+reports counter-derived HBM traffic only for the kernel source it was
+measured on."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode != 0
+    assert "--gpus 1" in (r.stdout + r.stderr)
+
+
+def _summary(path, digest, hbm):
+    with open(path, "w") as f:
+        f.write("# comment: a line with a colon is not a field\n")
+        f.write(f"kernel_source_sha256_16: {digest}\n")
+        f.write("launches: 16\n")
+        f.write(f"hbm_bytes_per_launch: {hbm}\n")
+
+
+def test_traffic_reported_only_for_the_measured_source(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    digest = bench.kernel_digest("mfma_indexer.hip")
+    _summary(tmp_path / "same.txt", digest, 123456789)
+    assert bench.measured_traffic("same.txt", "mfma_indexer.hip") == 123456789
+    # the same figure, taken on another source (a changed kernel): no figure
+    _summary(tmp_path / "stale.txt", "0123456789abcdef", 123456789)
+    assert bench.measured_traffic("stale.txt", "mfma_indexer.hip") is None
+    # a summary for one kernel does not vouch for another kernel's source
+    assert bench.measured_traffic("same.txt", "split_indexer.hip") is None
+    assert bench.measured_traffic("missing.txt", "mfma_indexer.hip") is None
+
+
+@pytest.mark.parametrize("summary", ["mfma_select_64k_traffic.txt", "mfma_select_1m_kernel_stats.txt",
+                                     "split_decode_256k_traffic.txt", "k_cache_write_256k_traffic.txt",
+                                     "sparse_attention_4096_traffic.txt"])
+def test_committed_traffic_summaries_parse(summary):
+    path = os.path.join(ROOT, "profiles", summary)
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    assert len(kv["kernel_source_sha256_16"]) == 16
+    fetch, write = int(kv["fetch_bytes_per_launch"]), int(kv["write_bytes_per_launch"])
+    assert int(kv["hbm_bytes_per_launch"]) == fetch + write > 0
