@@ -87,6 +87,33 @@ DECODE_MIX = [(1, 1), (1, 100), (1, 511), (1, 512), (1, 513), (0, 77), (1, 8191)
 PREFILL_MIX = [(700, 700), (1, 20000), (300, 9000), (0, 50), (129, 129), (5, 4099), (17, 60000)]
 
 
+# The two ragged batches bench.py times, at their full shapes (the same
+# recipe; bench.py carves its bytes from the decode and 64k workloads).
+BENCH_DECODE_MIX = [(1, 4096 + 910 * b) for b in range(64)]
+BENCH_PREFILL_MIX = [(1024, 32768), (512, 16384), (256, 8192), (256, 8192)]
+
+
+def test_bench_ragged_decode_mix():
+    # 64 streams x 1 query, 2,096,704 keys in all: the split-key kernel with
+    # more partitions than CUs
+    rg = W.ragged(47, BENCH_DECODE_MIX)
+    assert _route_is_split(rg, rg.topk)
+    _say("ragged decode, the bench mix: 64 streams of 4096 + 910 b keys, seed=47")
+    gi, gv = run_varlen(rg)
+    check_against_single_stream_calls(rg, gi, gv)
+    check_against_oracle(rg, gi, gv, exact=False)
+
+
+def test_bench_ragged_prefill_mix():
+    # a 2048-token budget: 1024/512/256/256 new tokens on caches of
+    # 32768/16384/8192/8192 keys, one prefill-kernel launch
+    rg = W.ragged(48, BENCH_PREFILL_MIX)
+    assert not _route_is_split(rg, rg.topk)
+    _say("ragged prefill, the bench mix: 2048 tokens over 4 streams, seed=48")
+    gi, gv = run_varlen(rg)
+    check_against_oracle(rg, gi, gv, exact=False, n=16)
+
+
 def test_ragged_decode_batch_fp8():
     # few rows: the split-key kernel. Each stream equals its own ds4idx_select
     # call (same kernel) bit for bit, and the oracle within tolerance.
