@@ -162,11 +162,46 @@ def _check_inputs(q, k, k_scale, w):
     for name, t in (("q", q), ("k", k), ("w", w)) + ((("k_scale", k_scale),) if k_scale is not None else ()):
         if not t.is_cuda or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous device tensor")
+        if t.device != q.device:
+            raise ValueError(f"{name} must be on {q.device}")
     B, T, H, _ = q.shape
     if w.dtype != torch.float32 or tuple(w.shape) != (B, T, H):
         raise ValueError("w must be float32 [B,T,H]")
     if k_scale is not None and (k_scale.dtype != torch.float32 or tuple(k_scale.shape) != tuple(k.shape[:2])):
         raise ValueError("k_scale must be float32 [B,S]")
+
+
+def _check_out(t: Optional[torch.Tensor], name: str, shape, dtype, device) -> None:
+    """A caller-supplied output must have exactly the shape and dtype the
+    kernels write, live on the inputs' device and be contiguous: the kernels
+    write shape-many elements through its pointer."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} {tuple(shape)}, got {t.dtype} {tuple(t.shape)}")
+    if not t.is_cuda or t.device != device or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous tensor on {device}")
+
+
+def _check_workspace(ws: Optional[torch.Tensor], device) -> int:
+    """Byte size of a caller-supplied workspace (the library checks it against
+    what the call needs)."""
+    if ws is None:
+        return 0
+    if ws.dtype != torch.uint8 or ws.dim() != 1 or not ws.is_cuda or ws.device != device \
+            or not ws.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous 1-D uint8 tensor on {device}")
+    return ws.numel()
+
+
+def _zeros_on(n: int, device, stream) -> torch.Tensor:
+    """n zero bytes allocated and cleared on `stream` (the stream the kernel
+    that reads them is launched on), so the fill is ordered before it."""
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    if not isinstance(s, torch.cuda.Stream):
+        s = torch.cuda.ExternalStream(int(s), device=device)
+    with torch.cuda.stream(s):
+        return torch.zeros(n, dtype=torch.uint8, device=device)
 
 
 def workspace_bytes(problem: Problem, k: int, op: int = OP_SELECT) -> int:
@@ -176,12 +211,14 @@ def workspace_bytes(problem: Problem, k: int, op: int = OP_SELECT) -> int:
     return n
 
 
-def new_workspace(problem: Problem, k: int, device=None) -> Optional[torch.Tensor]:
-    """A zero-filled device workspace big enough for ds4idx_select (or None)."""
+def new_workspace(problem: Problem, k: int, device=None, stream=None) -> Optional[torch.Tensor]:
+    """A device workspace big enough for ds4idx_select (or None), zero-filled
+    on `stream` (default: the current stream), the stream of the calls that
+    will use it."""
     n = workspace_bytes(problem, k, OP_SELECT)
     if n == 0:
         return None
-    return torch.zeros(n, dtype=torch.uint8, device=device or "cuda")
+    return _zeros_on(n, torch.device(device or "cuda"), stream)
 
 
 def score(q, k, k_scale, w, causal_offset: int, out: Optional[torch.Tensor] = None,
@@ -189,6 +226,7 @@ def score(q, k, k_scale, w, causal_offset: int, out: Optional[torch.Tensor] = No
     """scores [B,T,S] fp32: the indexer score of every visible key, -inf elsewhere."""
     _check_inputs(q, k, k_scale, w)
     p = make_problem(q, k, causal_offset)
+    _check_out(out, "out", (p.B, p.T, p.S), torch.float32, q.device)
     if out is None:
         out = torch.empty((p.B, p.T, p.S), dtype=torch.float32, device=q.device)
     st = lib().ds4idx_score(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(k_scale), _ptr(w), _ptr(out),
@@ -205,7 +243,11 @@ def topk(scores: torch.Tensor, k: int, causal_offset: int, idx: Optional[torch.T
     if scores.dtype != torch.float32 or scores.dim() != 3 or not scores.is_contiguous():
         raise ValueError("scores must be contiguous float32 [B,T,S]")
     B, T, S = scores.shape
+    if not scores.is_cuda:
+        raise ValueError("scores must be a device tensor")
     p = Problem(B, T, S, 1, 1, int(causal_offset), F32, F32)
+    _check_out(idx, "idx", (B, T, k), torch.int32, scores.device)
+    _check_out(vals, "vals", (B, T, k), torch.float32, scores.device)
     if idx is None:
         idx = torch.empty((B, T, k), dtype=torch.int32, device=scores.device)
     if vals is None and with_vals:
@@ -224,13 +266,15 @@ def select(q, k, k_scale, w, causal_offset: int, topk: int = 512,
     """Fused indexer: (idx [B,T,topk] int32 ascending/-1 padded, vals fp32 or None)."""
     _check_inputs(q, k, k_scale, w)
     p = make_problem(q, k, causal_offset)
+    _check_out(idx, "idx", (p.B, p.T, topk), torch.int32, q.device)
+    _check_out(vals, "vals", (p.B, p.T, topk), torch.float32, q.device)
     if idx is None:
         idx = torch.empty((p.B, p.T, topk), dtype=torch.int32, device=q.device)
     if vals is None and with_vals:
         vals = torch.empty((p.B, p.T, topk), dtype=torch.float32, device=q.device)
     if workspace is None:
-        workspace = new_workspace(p, topk, q.device)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        workspace = new_workspace(p, topk, q.device, stream)
+    ws_bytes = _check_workspace(workspace, q.device)
     st = lib().ds4idx_select(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(k_scale), _ptr(w), int(topk),
                              _ptr(idx), _ptr(vals), _ptr(workspace), ws_bytes, _stream(stream))
     if st != OK:
@@ -257,10 +301,11 @@ def varlen_workspace_bytes(problem: VarlenProblem, k: int) -> int:
     return n
 
 
-def new_varlen_workspace(problem: VarlenProblem, k: int, device=None) -> Optional[torch.Tensor]:
-    """A zero-filled device workspace big enough for ds4idx_select_varlen (or None)."""
+def new_varlen_workspace(problem: VarlenProblem, k: int, device=None, stream=None) -> Optional[torch.Tensor]:
+    """A device workspace big enough for ds4idx_select_varlen (or None),
+    zero-filled on `stream` (default: the current stream)."""
     n = varlen_workspace_bytes(problem, k)
-    return None if n == 0 else torch.zeros(n, dtype=torch.uint8, device=device or "cuda")
+    return None if n == 0 else _zeros_on(n, torch.device(device or "cuda"), stream)
 
 
 def select_varlen(q, k, k_scale, w, cu_q, cu_k, max_k: int, topk: int = 512,
@@ -280,13 +325,21 @@ def select_varlen(q, k, k_scale, w, cu_q, cu_k, max_k: int, topk: int = 512,
     p = make_varlen_problem(q, k, cu_q, cu_k, max_k)
     if w.dtype != torch.float32 or tuple(w.shape) != (p.total_q, p.H):
         raise ValueError("w must be float32 [total_q,H]")
+    if k_scale is not None and (k_scale.dtype != torch.float32 or tuple(k_scale.shape) != (p.total_k,)):
+        raise ValueError("k_scale must be float32 [total_k]")
+    for name, t in (("k", k), ("w", w), ("cu_q", cu_q), ("cu_k", cu_k)) + \
+            ((("k_scale", k_scale),) if k_scale is not None else ()):
+        if t.device != q.device:
+            raise ValueError(f"{name} must be on {q.device}")
+    _check_out(idx, "idx", (p.total_q, topk), torch.int32, q.device)
+    _check_out(vals, "vals", (p.total_q, topk), torch.float32, q.device)
     if idx is None:
         idx = torch.empty((p.total_q, topk), dtype=torch.int32, device=q.device)
     if vals is None and with_vals:
         vals = torch.empty((p.total_q, topk), dtype=torch.float32, device=q.device)
     if workspace is None:
-        workspace = new_varlen_workspace(p, topk, q.device)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        workspace = new_varlen_workspace(p, topk, q.device, stream)
+    ws_bytes = _check_workspace(workspace, q.device)
     st = lib().ds4idx_select_varlen(ctypes.byref(p), _ptr(cu_q), _ptr(cu_k), _ptr(q), _ptr(k),
                                     _ptr(k_scale), _ptr(w), int(topk), _ptr(idx), _ptr(vals),
                                     _ptr(workspace), ws_bytes, _stream(stream))
@@ -313,6 +366,13 @@ def select_qfp8(q8, q_scale, k, k_scale, w, causal_offset: int, topk: int = 512,
     if k.dim() != 3 or k.shape[0] != B or k.shape[2] != D or tuple(k_scale.shape) != tuple(k.shape[:2]):
         raise ValueError("k must be [B,S,D] with k_scale [B,S]")
     p = Problem(B, T, k.shape[1], H, D, int(causal_offset), FP8_E4M3, FP8_E4M3)
+    for name, t in (("q_scale", q_scale), ("k", k), ("k_scale", k_scale), ("w", w)):
+        if t.device != q8.device:
+            raise ValueError(f"{name} must be on {q8.device}")
+    if k_scale.dtype != torch.float32:
+        raise ValueError("k_scale must be float32 [B,S]")
+    _check_out(idx, "idx", (B, T, topk), torch.int32, q8.device)
+    _check_out(vals, "vals", (B, T, topk), torch.float32, q8.device)
     if idx is None:
         idx = torch.empty((B, T, topk), dtype=torch.int32, device=q8.device)
     if vals is None and with_vals:
@@ -342,6 +402,9 @@ def sparse_attention(q: torch.Tensor, kv: torch.Tensor, idx: torch.Tensor, softm
     for name, t in (("q", q), ("kv", kv), ("idx", idx)):
         if not t.is_cuda or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous device tensor")
+    if kv.device != q.device or idx.device != q.device:
+        raise ValueError(f"kv and idx must be on {q.device}")
+    _check_out(out, "out", (B, T, H, d_v), torch.bfloat16, q.device)
     if out is None:
         out = torch.empty((B, T, H, d_v), dtype=torch.bfloat16, device=q.device)
     lse = torch.empty((B, T, H), dtype=torch.float32, device=q.device) if with_lse else None
@@ -374,6 +437,8 @@ def k_cache_write(k_new: torch.Tensor, cache: torch.Tensor, cache_scale: torch.T
     for name, t in named:
         if not t.is_cuda or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous device tensor")
+        if t.device != k_new.device:
+            raise ValueError(f"{name} must be on {k_new.device}")
     st = lib().ds4idx_k_cache_write(_ptr(k_new), _dtype_code(k_new, False), int(n), int(D),
                                     _ptr(slots), _ptr(cache), _ptr(cache_scale),
                                     int(cache.shape[0]), _stream(stream))

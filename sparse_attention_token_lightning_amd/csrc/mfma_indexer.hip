@@ -435,10 +435,10 @@ __global__ __launch_bounds__(THREADS, 1) void mfma_indexer_kernel(
 #pragma unroll
         for (int n = 0; n < 2; ++n) part[n] = (s4[n][0] + s4[n][1]) + (s4[n][2] + s4[n][3]);
     };
-    // Scale, mask and insert (or store) the pair at pbase (tile in buffer
-    // cur) from its halves' partial head sums: after the 32- and 16-lane
-    // swaps lane l holds the score of key l of the pair.
-    auto finish_pair = [&](const float (&p0)[2], const float (&p1)[2], long long pbase, int cur) {
+    // Scale, mask and insert (or store) the pair at pbase from its halves'
+    // partial head sums and its keys' scales (lane l: key l of the pair):
+    // after the 32- and 16-lane swaps lane l holds the score of key l.
+    auto finish_pair = [&](const float (&p0)[2], const float (&p1)[2], long long pbase, float kscale) {
         float hsum[2];
 #pragma unroll
         for (int n = 0; n < 2; ++n) {
@@ -449,7 +449,7 @@ __global__ __launch_bounds__(THREADS, 1) void mfma_indexer_kernel(
         const auto w16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(hsum[0]), __float_as_uint(hsum[1]),
                                                           false, false);
         float sc = __uint_as_float(w16[0]) + __uint_as_float(w16[1]);
-        if (KFP8) sc *= sm.scale[cur][(int)(pbase % KT) + lane];
+        if (KFP8) sc *= kscale;
         sc = canon(sc);
         const long long key = pbase + lane;
         const bool vis = key <= lim;
@@ -483,6 +483,11 @@ __global__ __launch_bounds__(THREADS, 1) void mfma_indexer_kernel(
     };
 
     float prev0[2] = {0.0f, 0.0f};  // first half's partial sums of the pair in flight
+    // Scales of the tile's last pair, whose finish runs in the next tile's
+    // first phase. They are read into a register before the end-of-tile
+    // barrier: by that finish, other wavefronts may already be staging the
+    // tile after next into the same scale buffer.
+    float pend_scale = 1.0f;
     for (int tile = 0; tile < ntiles; ++tile) {
         const int cur = tile & 1;
         if (tile + 1 < ntiles) load_tile<KFP8>(tr, tsc, Kb, Ksb, Sb, tile + 1, tid);
@@ -491,12 +496,15 @@ __global__ __launch_bounds__(THREADS, 1) void mfma_indexer_kernel(
         for (int pp = 0; pp < KT / 64; ++pp) {
             float h1[2], h0[2];
             phase(0, cur, pp, h1);  // MFMAs of this pair's first half; previous pair's second half reduced
-            if (tile > 0 || pp > 0)
-                finish_pair(prev0, h1, kbase + pp * 64 - 64, pp > 0 ? cur : cur ^ 1);
+            if (pp > 0)
+                finish_pair(prev0, h1, kbase + pp * 64 - 64, KFP8 ? sm.scale[cur][(pp - 1) * 64 + lane] : 1.0f);
+            else if (tile > 0)
+                finish_pair(prev0, h1, kbase - 64, pend_scale);
             phase(1, cur, pp, h0);  // MFMAs of the second half; this pair's first half reduced
             prev0[0] = h0[0];
             prev0[1] = h0[1];
         }
+        if (KFP8) pend_scale = sm.scale[cur][KT - 64 + lane];
         if (tile + 1 < ntiles) {
             if constexpr (QFP8) store_tile_raw(sm, cur ^ 1, tr, tsc, tid);
             else store_tile<KFP8>(sm, cur ^ 1, tr, tsc, tid);
@@ -515,7 +523,7 @@ __global__ __launch_bounds__(THREADS, 1) void mfma_indexer_kernel(
                 for (int i = 0; i < 4; ++i) s4[i] = fmaf(wv[m][i], relu(r[n][m][i]), s4[i]);
             h1[n] = (s4[0] + s4[1]) + (s4[2] + s4[3]);
         }
-        finish_pair(prev0, h1, (long long)ntiles * KT - 64, (ntiles - 1) & 1);
+        finish_pair(prev0, h1, (long long)ntiles * KT - 64, pend_scale);
     }
 
     if (!SCORE && tok_ok) {

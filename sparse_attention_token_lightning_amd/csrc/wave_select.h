@@ -85,37 +85,4 @@ __device__ uint32_t wave_kth_key(const uint32_t (&u)[C], uint32_t k, uint32_t *h
     return prefix;
 }
 
-// The m-th largest key among the wavefront's keys by m rounds of
-// max-extraction (a DPP max, then the lowest lane holding it drops one
-// copy): cheap for small m, exact with duplicates. Returns 0 when the
-// wavefront holds fewer than m keys. `top`, if given, receives the m largest
-// keys in descending order (wave-uniform values).
-template <int C>
-__device__ uint32_t wave_mth_key(const uint32_t (&u)[C], int m, int lane, uint32_t *top)
-{
-    uint32_t cur[C];
-#pragma unroll
-    for (int j = 0; j < C; ++j) cur[j] = u[j];
-    uint32_t wm = 0u;
-    for (int r = 0; r < m; ++r) {
-        uint32_t lm = 0u;
-#pragma unroll
-        for (int j = 0; j < C; ++j) lm = cur[j] > lm ? cur[j] : lm;
-        wm = wave_max(lm);
-        if (top) top[r] = wm;
-        if (wm == 0u) break;
-        const int first = __builtin_ctzll(wave_ballot(lm == wm));
-        if (lane == first) {
-            bool done = false;
-#pragma unroll
-            for (int j = 0; j < C; ++j) {
-                const bool hit = !done && cur[j] == wm;
-                cur[j] = hit ? 0u : cur[j];
-                done = done || hit;
-            }
-        }
-    }
-    return wm;
-}
-
 }  // namespace ds4idx

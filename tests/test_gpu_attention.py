@@ -1,11 +1,25 @@
 """GPU parity of sparse attention (ds4idx_sparse_attention) through the C ABI
 against the CPU oracle.
 
-Tolerance, from the arithmetic: the probabilities enter the value sum as bf16
-(relative error <= 2^-9 each, so the weighted mean moves by <= 2^-9 of the
-largest selected value), and the output is rounded to bf16 (2^-9 relative);
-scores and sums are fp32. Allowed: |out - ref| <= 2^-8 (max_j |v_j| + |ref|);
-lse within 2e-5 + 1e-5 |lse|."""
+Tolerance, from the arithmetic. Scores, sums and accumulators are fp32; the
+probabilities p_j enter the value sum rounded to bf16, p_j (1 + d_j) with
+|d_j| <= 2^-9, and the output is rounded to bf16 (relative 2^-9 per element).
+
+* Element bound (worst case): the weighted mean moves by at most 2^-9 of the
+  largest selected value, so |out - ref| <= 2^-8 (max_j |v_j| + |ref|).
+* Norm bound per (token, head), over the d_v outputs: with softmax weights
+  w_j, the probability rounding adds e = sum_j w_j (d_j - dbar) v_j, where
+  dbar = sum_j w_j d_j (the denominator may or may not see the rounding).
+  The dbar part is at most 2^-9 |ref| in norm; the rest is a sum of
+  independent rounding errors with standard deviation at most
+  2^-9 / sqrt(3) * sqrt(sum_j w_j^2 |v_j|^2). Allowed:
+      |out - ref|_2 <= 2^-8 |ref|_2 + 6 * 2^-9 / sqrt(3) * sqrt(sum_j w_j^2 |v_j|_2^2) + 1e-6
+  (output rounding and dbar, plus six standard deviations; when at most 12
+  keys carry the weight, the second term also covers the worst case
+  2^-9 sum_j w_j |v_j|). On N(0,1) rows of 512 keys this is about 1% of
+  |ref|_2, where dropping one selected key from the value sum alone moves the
+  output by about 4%.
+* lse within 2e-5 + 1e-5 |lse|."""
 import numpy as np
 import pytest
 import torch
@@ -39,6 +53,7 @@ def check(a: W.AttnInputs, go, glse, rows=None):
     rows = np.arange(B * T) if rows is None else np.asarray(rows)
     ro, rl = oracle.sparse_attention(a.q, a.kv, a.idx, a.softmax_scale, a.d_v, rows=rows)
     kvf = W.bf16_bits_to_f32(a.kv).astype(np.float64)
+    qf = W.bf16_bits_to_f32(a.q).astype(np.float64).reshape(B * T, H, -1)
     S = a.kv.shape[1]
     for n, r in enumerate(rows):
         b = r // T
@@ -48,6 +63,19 @@ def check(a: W.AttnInputs, go, glse, rows=None):
         tol = 2.0 ** -8 * (vmax + np.abs(ro[n]))
         err = np.abs(go[r] - ro[n])
         assert np.all(err <= tol), f"row {r}: max error {err.max()} (worst head {np.unravel_index(np.argmax(err - tol), err.shape)})"
+        if len(sel):
+            # softmax weights of the selection (tolerance scale only)
+            z = a.softmax_scale * (qf[r] @ kvf[b, sel].T)             # [H, n_sel]
+            wgt = np.exp(z - z.max(axis=1, keepdims=True))
+            wgt /= wgt.sum(axis=1, keepdims=True)
+            vn2 = (kvf[b, sel, :a.d_v] ** 2).sum(axis=1)               # |v_j|^2
+            spread = np.sqrt((wgt ** 2 * vn2[None, :]).sum(axis=1))    # [H]
+            refn = np.linalg.norm(ro[n], axis=1)
+            errn = np.linalg.norm(go[r] - ro[n], axis=1)
+            ntol = 2.0 ** -8 * refn + 6.0 * 2.0 ** -9 / np.sqrt(3.0) * spread + 1e-6
+            worst = int(np.argmax(errn / ntol))
+            assert np.all(errn <= ntol), \
+                f"row {r} head {worst}: |out-ref|_2 = {errn[worst]:.3e} > {ntol[worst]:.3e} (|ref|_2 = {refn[worst]:.3e})"
         if len(sel) == 0:
             assert np.all(np.isneginf(glse[r])) and np.all(go[r] == 0)
         else:

@@ -89,4 +89,7 @@ def test_prefill_chunk_matches_dequantised_oracle():
     oi, _, _, _, _ = oracle.select(last, rows=rows)
     recall = np.mean([len(set(gi[r]) & set(oi[n])) / 512.0 for n, r in enumerate(rows)])
     _say(f"qfp8 recall of the bf16-query top-512 over {len(rows)} rows: {recall:.4f}")
-    assert recall > 0.5
+    # 0.968 measured on these rows (0.971 over all 65536 rows): the guard
+    # sits just under it, so a scorer that loses a further 1-2% of the exact
+    # selection fails
+    assert recall > 0.955

@@ -240,6 +240,26 @@ def sample_rows(wl: Workload, n: int, seed: int = 7) -> np.ndarray:
     return np.array(sorted(rows), dtype=np.int64)
 
 
+def sample_rows_per_chunk(wl: Workload, per_chunk: int = 4, seed: int = 7) -> np.ndarray:
+    """Flat row ids with `per_chunk` rows from every chunk of every stream: the
+    chunk's first and last query plus uniform draws inside it, and, when the
+    first chunk starts at offset 0, the rows around t = k-1 (where rows reach
+    k visible keys)."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    rows = set()
+    for b in range(wl.B):
+        for (t0, tc, _s, _o) in wl.chunks:
+            mine = {b * wl.T + t0, b * wl.T + t0 + tc - 1}
+            while len(mine) < min(per_chunk, tc):
+                mine.add(b * wl.T + t0 + int(g.integers(0, tc)))
+            rows |= mine
+        if wl.offset == 0:
+            for t in (wl.topk - 2, wl.topk - 1, wl.topk):
+                if 0 <= t < wl.T:
+                    rows.add(b * wl.T + t)
+    return np.array(sorted(rows), dtype=np.int64)
+
+
 # --------------------------------------------------------------------------- key-cache writer
 
 def new_keys(seed: int = 6, n: int = 8 * 262144, D: int = 128, log_spread: float = 0.0,
