@@ -62,7 +62,8 @@ typedef enum {
     DS4IDX_ERR_INVALID_ARG = 1, /* null pointer, bad size, misalignment, bad k */
     DS4IDX_ERR_UNSUPPORTED = 2, /* shape/dtype with no kernel under the forced implementation */
     DS4IDX_ERR_WORKSPACE = 3,   /* workspace NULL or smaller than ds4idx_workspace_bytes */
-    DS4IDX_ERR_HIP = 4          /* a HIP launch or query failed */
+    DS4IDX_ERR_HIP = 4,         /* a HIP launch or query failed */
+    DS4IDX_ERR_SCRATCH = 5      /* ds4idx_select_noalloc: needs more than DS4IDX_NOALLOC_SCRATCH_BYTES */
 } ds4idx_status;
 
 typedef enum {
@@ -128,6 +129,28 @@ int ds4idx_topk(const ds4idx_problem *p, const float *scores, int32_t k, int32_t
 int ds4idx_select(const ds4idx_problem *p, const void *Q, const void *K, const float *K_scale,
                   const float *W, int32_t k, int32_t *idx, float *vals, void *workspace,
                   size_t ws_bytes, void *stream);
+
+/* Allocation-free fused select, for callers that cannot allocate device
+ * memory around the call: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc. Same arguments, outputs and kernels as
+ * ds4idx_select, without the workspace: the workspace the call would need
+ * (the split-key kernel's per-row counters and candidate lists, or the plain
+ * kernels' score matrix) lives in a fixed array of
+ * DS4IDX_NOALLOC_SCRATCH_BYTES in device memory that the library holds on
+ * each GPU it runs on until the process ends. The call allocates nothing and
+ * frees nothing; it clears the words that must start at zero with a fill
+ * kernel on `stream` before the selection kernel.
+ *
+ * Problems whose workspace (ds4idx_workspace_bytes) exceeds the array return
+ * DS4IDX_ERR_SCRATCH before any HIP call; the prefill kernel's problems need
+ * none. The array belongs to the device current on the calling thread, which
+ * must be the device of `stream`. Every call on a GPU shares that GPU's
+ * array: calls whose executions overlap on one GPU (other streams, other
+ * threads) race and give undefined results; calls in one stream are
+ * ordered. */
+#define DS4IDX_NOALLOC_SCRATCH_BYTES (32u << 20)
+int ds4idx_select_noalloc(const ds4idx_problem *p, const void *Q, const void *K, const float *K_scale,
+                          const float *W, int32_t k, int32_t *idx, float *vals, void *stream);
 
 /* Ragged batch: B independent streams (requests) packed along the rows, in
  * one launch, as a serving step mixes requests with different cache lengths

@@ -25,7 +25,8 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libds4idx.so")
 
-OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP, ERR_SCRATCH = 0, 1, 2, 3, 4, 5
+NOALLOC_SCRATCH_BYTES = 32 << 20
 F32, BF16, FP8_E4M3 = 0, 1, 2
 OP_SCORE, OP_TOPK, OP_SELECT = 0, 1, 2
 IMPL_AUTO, IMPL_REF, IMPL_OPT = 0, 1, 2
@@ -37,7 +38,7 @@ ABI_VERSION = 1
 EXPORTS = ("ds4idx_abi_version", "ds4idx_status_string", "ds4idx_set_impl", "ds4idx_get_impl",
            "ds4idx_workspace_bytes", "ds4idx_score", "ds4idx_topk", "ds4idx_select",
            "ds4idx_k_cache_write", "ds4idx_varlen_workspace_bytes", "ds4idx_select_varlen",
-           "ds4idx_sparse_attention", "ds4idx_select_qfp8")
+           "ds4idx_sparse_attention", "ds4idx_select_qfp8", "ds4idx_select_noalloc")
 
 
 class Problem(ctypes.Structure):
@@ -92,6 +93,8 @@ def lib() -> ctypes.CDLL:
         L.ds4idx_topk.restype = ctypes.c_int
         L.ds4idx_select.argtypes = [P, vp, vp, vp, vp, i32, vp, vp, vp, sz, vp]
         L.ds4idx_select.restype = ctypes.c_int
+        L.ds4idx_select_noalloc.argtypes = [P, vp, vp, vp, vp, i32, vp, vp, vp]
+        L.ds4idx_select_noalloc.restype = ctypes.c_int
         L.ds4idx_k_cache_write.argtypes = [vp, i32, ctypes.c_int64, i32, vp, vp, vp,
                                            ctypes.c_int64, vp]
         L.ds4idx_k_cache_write.restype = ctypes.c_int
@@ -280,6 +283,25 @@ def select(q, k, k_scale, w, causal_offset: int, topk: int = 512,
     if st != OK:
         raise Ds4idxError(st, "ds4idx_select")
     return idx, vals
+
+
+def select_noalloc(q, k, k_scale, w, causal_offset: int, idx: torch.Tensor,
+                   vals: Optional[torch.Tensor] = None, stream=None) -> None:
+    """ds4idx_select without a workspace and without allocating: writes the
+    caller's idx [B,T,topk] int32 (topk = idx.shape[-1]) and optional vals.
+    The library's fixed per-GPU scratch array stands in for the workspace, so
+    calls whose executions overlap on one GPU must not be made."""
+    _check_inputs(q, k, k_scale, w)
+    p = make_problem(q, k, causal_offset)
+    if idx is None or idx.dim() != 3:
+        raise ValueError("idx must be a preallocated [B,T,topk] int32 tensor")
+    topk = idx.shape[-1]
+    _check_out(idx, "idx", (p.B, p.T, topk), torch.int32, q.device)
+    _check_out(vals, "vals", (p.B, p.T, topk), torch.float32, q.device)
+    st = lib().ds4idx_select_noalloc(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(k_scale), _ptr(w), int(topk),
+                                     _ptr(idx), _ptr(vals), _stream(stream))
+    if st != OK:
+        raise Ds4idxError(st, "ds4idx_select_noalloc")
 
 
 def make_varlen_problem(q, k, cu_q, cu_k, max_k: int) -> VarlenProblem:

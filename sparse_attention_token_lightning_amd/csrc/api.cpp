@@ -12,6 +12,9 @@
 
 using ds4idx::Problem;
 
+static_assert(DS4IDX_NOALLOC_SCRATCH_BYTES == ds4idx::kNoallocScratchBytes,
+              "the header states the scratch array's size");
+
 namespace {
 
 std::atomic<int> g_impl{-1};
@@ -158,6 +161,8 @@ const char *ds4idx_status_string(int status)
     case DS4IDX_ERR_UNSUPPORTED: return "unsupported shape or dtype for the selected kernels";
     case DS4IDX_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case DS4IDX_ERR_HIP: return "HIP launch or runtime error";
+    case DS4IDX_ERR_SCRATCH:
+        return "problem needs more scratch memory than the allocation-free entry point holds";
     default: return "unknown status";
     }
 }
@@ -234,6 +239,40 @@ int ds4idx_select(const ds4idx_problem *p, const void *Q, const void *K, const f
     if (r == R_SPLIT)
         return launch_status(ds4idx::launch_split_select(q, Q, K, K_scale, W, k, idx, vals, workspace, s));
     float *sc = static_cast<float *>(workspace);
+    st = launch_status(ds4idx::launch_score_ref(q, Q, K, K_scale, W, sc, s));
+    if (st != DS4IDX_OK) return st;
+    return launch_status(ds4idx::launch_topk_ref(q, sc, k, idx, vals, s));
+}
+
+int ds4idx_select_noalloc(const ds4idx_problem *p, const void *Q, const void *K, const float *K_scale,
+                          const float *W, int32_t k, int32_t *idx, float *vals, void *stream)
+{
+    int st = check_problem(p);
+    if (st != DS4IDX_OK) return st;
+    if ((st = check_inputs(p, Q, K, K_scale, W)) != DS4IDX_OK) return st;
+    if (k < 1 || k > DS4IDX_MAX_TOPK) return DS4IDX_ERR_INVALID_ARG;
+    if (!idx || !aligned(idx, 4) || (vals && !aligned(vals, 4))) return DS4IDX_ERR_INVALID_ARG;
+    const int r = route_select(p, k);
+    if (r == R_NONE) return DS4IDX_ERR_UNSUPPORTED;
+    const Problem q = to_internal(p);
+    const size_t need = r == R_REF ? ref_select_bytes(p)
+                        : r == R_SPLIT ? ds4idx::split_workspace_bytes(ds4idx::split_shape(q), k) : 0;
+    if (need > ds4idx::kNoallocScratchBytes) return DS4IDX_ERR_SCRATCH;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (r == R_PREFILL)
+        return launch_status(ds4idx::launch_mfma_select(q, Q, K, K_scale, W, k, idx, vals, s));
+    void *ws = ds4idx::noalloc_scratch();
+    if (!ws) return DS4IDX_ERR_HIP;
+    if (r == R_SPLIT) {
+        // Only the arrival counters must start at zero; every other word of
+        // the split-key workspace is written before it is read.
+        const ds4idx::SplitShape sh = ds4idx::split_shape(q);
+        st = launch_status(
+            ds4idx::launch_zero_words(ds4idx::split_workspace(ws, sh, k).ctr, sh.rows, s));
+        if (st != DS4IDX_OK) return st;
+        return launch_status(ds4idx::launch_split_select(q, Q, K, K_scale, W, k, idx, vals, ws, s));
+    }
+    float *sc = static_cast<float *>(ws);
     st = launch_status(ds4idx::launch_score_ref(q, Q, K, K_scale, W, sc, s));
     if (st != DS4IDX_OK) return st;
     return launch_status(ds4idx::launch_topk_ref(q, sc, k, idx, vals, s));

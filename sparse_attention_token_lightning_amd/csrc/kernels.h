@@ -76,6 +76,12 @@ hipError_t launch_split_select_varlen(const VarlenProblem &p, const int *cu_q, c
                                       const void *Q, const void *K, const float *Ks, const float *W, int k,
                                       int *idx, float *vals, void *ws, hipStream_t st);
 
+// Allocation-free select: a fixed scratch array per GPU holds what the
+// caller's workspace would (the split-key lists, or the plain path's scores).
+constexpr size_t kNoallocScratchBytes = (size_t)32 << 20;
+void *noalloc_scratch();  // this device's scratch address (nullptr on failure)
+hipError_t launch_zero_words(uint32_t *p, long long n, hipStream_t st);
+
 // Sparse attention over selected positions of a shared latent cache: the key
 // is the whole row (576 values), the value its first 512; heads in tiles of 64.
 constexpr int kAttnHeadTile = 64, kAttnDqk = 576, kAttnDv = 512, kAttnMaxK = 2048;

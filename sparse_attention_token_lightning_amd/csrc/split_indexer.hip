@@ -39,6 +39,9 @@
 #include "device_common.h"
 #include "kernels.h"
 
+#include <atomic>
+#include <mutex>
+
 namespace ds4idx {
 namespace {
 
@@ -1033,6 +1036,54 @@ hipError_t launch_split_select(const Problem &p, const void *Q, const void *K, c
     const SplitShape sh = split_shape(p);
     if (p.k_dtype == FP8) return launch_t<true, false>(p, sh, Ragged{}, Q, K, Ks, W, k, idx, vals, ws, st);
     return launch_t<false, false>(p, sh, Ragged{}, Q, K, Ks, W, k, idx, vals, ws, st);
+}
+
+// ---- the allocation-free entry point's scratch memory
+//
+// One fixed array per GPU, in the code object's device memory, so that the
+// allocation-free select needs no workspace from its caller. Host code never
+// uses the array's name as an address (on the host it is only a stand-in):
+// the device address comes from hipGetSymbolAddress, once per device with
+// that device current, and is kept per device.
+namespace {
+
+__device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+__global__ __launch_bounds__(256) void zero_words_kernel(uint32_t *__restrict__ p, long long n)
+{
+    const long long stride = (long long)gridDim.x * blockDim.x;
+    for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = 0u;
+}
+
+}  // namespace
+
+void *noalloc_scratch()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    void *p = g_scratch[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (!p) {
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+        g_scratch[dev].store(p, std::memory_order_release);
+    }
+    return p;
+}
+
+// Zero n words on the stream with a fill kernel (no memset node, so the call
+// can be captured into a graph and replayed).
+hipError_t launch_zero_words(uint32_t *p, long long n, hipStream_t st)
+{
+    if (n <= 0) return hipSuccess;
+    const long long blocks = (n + 255) / 256;
+    hipLaunchKernelGGL(zero_words_kernel, dim3((unsigned)(blocks < 1024 ? blocks : 1024)), dim3(256), 0, st, p, n);
+    return hipGetLastError();
 }
 
 hipError_t launch_split_select_varlen(const VarlenProblem &p, const int *cu_q, const long long *cu_k,

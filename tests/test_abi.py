@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for s in range(5):
+    for s in range(6):
         assert ds.status_string(s)
     assert ds.status_string(99) == "unknown status"
 
@@ -292,3 +292,29 @@ def test_qfp8_unsupported_shapes():
     p = _prob(q_dtype=ds.FP8_E4M3)
     assert ds.lib().ds4idx_select_qfp8(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, 1024, FAKE, None,
                                        None) == ds.ERR_UNSUPPORTED
+
+
+def test_noalloc_validates_before_any_hip_call():
+    L = ds.lib()
+    p = _prob(B=8, T=1, S=262144, causal_offset=262143)
+    assert L.ds4idx_select_noalloc(ctypes.byref(p), None, FAKE, FAKE, FAKE, 512, FAKE, None,
+                                   None) == ds.ERR_INVALID_ARG
+    assert L.ds4idx_select_noalloc(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, 512, None, None,
+                                   None) == ds.ERR_INVALID_ARG
+    assert L.ds4idx_select_noalloc(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, 0, FAKE, None,
+                                   None) == ds.ERR_INVALID_ARG
+    assert L.ds4idx_select_noalloc(ctypes.byref(p), FAKE_MIS, FAKE, FAKE, FAKE, 512, FAKE, None,
+                                   None) == ds.ERR_INVALID_ARG
+    assert L.ds4idx_select_noalloc(None, FAKE, FAKE, FAKE, FAKE, 512, FAKE, None, None) == ds.ERR_INVALID_ARG
+    # workspace beyond the scratch array: refused with its own status, no HIP call made
+    big = _prob(B=64, T=1, S=1 << 20, causal_offset=(1 << 20) - 1)
+    assert ds.workspace_bytes(big, 512) > ds.NOALLOC_SCRATCH_BYTES
+    assert L.ds4idx_select_noalloc(ctypes.byref(big), FAKE, FAKE, FAKE, FAKE, 512, FAKE, None,
+                                   None) == ds.ERR_SCRATCH
+    assert ds.workspace_bytes(p, 512) <= ds.NOALLOC_SCRATCH_BYTES
+
+
+def test_noalloc_scratch_size_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define DS4IDX_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == ds.NOALLOC_SCRATCH_BYTES
