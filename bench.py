@@ -25,6 +25,12 @@ the remaining indexer workloads, one ds4idx_select call each: the tiny fp32
 prefill (T = S = 1024, H = 4, D = 64), the 8k bf16 prefill and the 1M chunked
 prefill (2048 queries after 1,046,528 cached E4M3 keys).
 
+Before each timed 64k step a 512 MB buffer is written so the step starts
+with a cold last-level cache (--no-flush to skip). Also reported: measured
+ceilings in plain torch (an HBM read of 277 MB rotated over three copies, an
+8192^3 bf16 matmul), and the CPU oracle timed per workload with the host's
+core count, CPU model and a one-thread rate.
+
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
 """
 from __future__ import annotations
@@ -61,6 +67,13 @@ def _parse():
     ap.add_argument("--warm-ms", type=float, default=30.0,
                     help="device time of the untimed calls queued before each per-call timed loop")
     ap.add_argument("--writer-iters", type=int, default=20)
+    ap.add_argument("--no-cpu-configs", action="store_true",
+                    help="skip the per-workload oracle timings (every row of the tiny, 8k, 8k-int and "
+                         "decode workloads; sampled rows of the 64k and 1M prefills)")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the measured ceilings (torch read of 3 x 277 MB rotated; bf16 matmul)")
+    ap.add_argument("--no-flush", action="store_true",
+                    help="do not write a 512 MB buffer before each timed 64k step")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, copy 256 MiB once (the reference kernel that "
                          "scales the FETCH_SIZE / WRITE_SIZE counters to bytes)")
@@ -196,11 +209,21 @@ def main():
     torch.cuda.synchronize()
     events = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in wl.chunks]
               for _ in range(args.steps)]
-    t_start = time.perf_counter()
+    # "Cold": before each timed step, 512 MB are written (twice the 256 MB
+    # last-level cache), so no key, query or weight byte of the step is
+    # cached when it starts. The write is outside the timed region: each step
+    # is bracketed by synchronisations and timed on the host clock.
+    flush = None if args.no_flush else torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    elapsed = 0.0
     for s in range(args.steps):
+        if flush is not None:
+            flush.fill_(s & 0xff)
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
         step(events[s])
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t_start
+        torch.cuda.synchronize()
+        elapsed += time.perf_counter() - t_start
+    del flush
     launch_ms = [ev[0].elapsed_time(ev[1]) for st in events for ev in st]
     ms_per_step = elapsed * 1e3 / args.steps
     value = wl.T * args.steps / elapsed
@@ -214,7 +237,10 @@ def main():
                 "traffic": measured_traffic(),
                 "kernel": "mfma_indexer_kernel<fp8 keys, select>",
                 "avg_launch_us": round(avg_launch_s * 1e6, 2),
-                "flop_per_launch": flops // n_launch}
+                "flop_per_launch": flops // n_launch,
+                "fp8_peak": FP8_PEAK_TFLOPS,
+                "fp8_frac": round(achieved_tflops / FP8_PEAK_TFLOPS, 4),
+                "cold": not args.no_flush}
 
     if args.copy_calibration:
         src = torch.ones(256 << 18, dtype=torch.float32, device=dev)  # 256 MiB
@@ -270,9 +296,11 @@ def main():
         extra["select_qfp8_64k"]["recall_min_row"] = round(float(recall.min()), 4)
         del both, common, nvalid
 
+    hostwl = {"prefill_64k": wl}
     # ---------------------------------------------------------------- 256k decode
     if not args.no_decode:
         dl = W.decode()
+        hostwl["decode_256k"] = dl
         sets = []
         qd = torch.from_numpy(dl.q.view(np.int16)).view(torch.bfloat16).to(dev)
         kd = torch.from_numpy(dl.k).to(dev)
@@ -441,7 +469,43 @@ def main():
                 "input_bytes": int(host_bytes)}
             if name == "prefill_1m":
                 extra[name]["traffic"] = measured_traffic("mfma_select_1m_kernel_stats.txt", "mfma_indexer.hip")
+            hostwl[name] = ow  # host arrays, for the oracle timings below
             del oq, ok_, oks, ow_, oidx, ovals, ows, ow
+
+    # ---------------------------------------------------------------- measured ceilings
+    # What this GPU sustains in plain torch operations, beside the kernels'
+    # fractions of the datasheet peaks: a read of the decode's 277 MB
+    # (rotated over three copies, so the last-level cache holds none of it)
+    # and a large bf16 matmul.
+    if not args.no_ceilings:
+        nbytes = 276989952
+        bufs = [torch.ones(nbytes // 4, dtype=torch.float32, device=dev) for _ in range(3)]
+
+        def rstep(i):
+            bufs[i % 3].sum()
+
+        rus = _time_calls(rstep, 30, stream, args.warm_ms)
+        rmed = rus[len(rus) // 2]
+        del bufs
+        n = 8192
+        ma = torch.randn((n, n), dtype=torch.bfloat16, device=dev)
+        mb = torch.randn((n, n), dtype=torch.bfloat16, device=dev)
+        mc = torch.empty((n, n), dtype=torch.bfloat16, device=dev)
+
+        def mstep(i):
+            torch.matmul(ma, mb, out=mc)
+
+        mus = _time_calls(mstep, 20, stream, args.warm_ms)
+        mmed = mus[len(mus) // 2]
+        del ma, mb, mc
+        extra["ceilings"] = {
+            "hbm_read": {"what": "torch.sum over 276,989,952 B, rotated over 3 copies",
+                         "us_median": round(rmed, 2), "GB_s": round(nbytes / (rmed * 1e-6) / 1e9, 1),
+                         "frac_of_peak": round(nbytes / (rmed * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
+            "bf16_matmul": {"what": "torch.matmul 8192 x 8192 x 8192 bf16",
+                            "us_median": round(mmed, 2),
+                            "tflops": round(2 * n ** 3 / (mmed * 1e-6) / 1e12, 1),
+                            "frac_of_peak": round(2 * n ** 3 / (mmed * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4)}}
 
     # ---------------------------------------------------------------- CPU oracle
     cpu = None
@@ -467,6 +531,56 @@ def main():
                "sample": f"{n} uniformly drawn query rows of the 64k prefill ({keys} visible keys, "
                          f"{t_cpu:.1f} s measured), extrapolated by visible-key count to all "
                          f"{wl.T} rows ({pairs} keys)"}
+
+    # Every workload's oracle time on the host: every row of the tiny, 8k,
+    # 8k-int and decode workloads; the 64k prefill's 4 rows per chunk (each
+    # chunk's first and last, 2 drawn) plus rows 510-512; 64 rows of the 1M
+    # prefill (0 and 2047 included). Full-workload seconds are extrapolated
+    # by visible keys. A 1-thread run of 4 rows of the 64k prefill (16k to 64k
+    # visible keys) gives the per-core rate.
+    if not args.no_cpu_baseline and not args.no_cpu_configs:
+        import oracle
+        per = {}
+        plan = [("tiny_1024", lambda: hostwl.get("tiny_1024") or W.tiny(), None),
+                ("prefill_8k", lambda: hostwl.get("prefill_8k") or W.prefill_bf16(), None),
+                ("prefill_8k_int", W.prefill_bf16_int, None),
+                ("prefill_64k", lambda: wl, lambda x: W.sample_rows_per_chunk(x, 4)),
+                ("decode_256k", lambda: hostwl.get("decode_256k") or W.decode(), None),
+                ("prefill_1m", lambda: hostwl.get("prefill_1m") or W.long_prefill(),
+                 lambda x: W.sample_rows(x, 64))]
+        for name, make, pick in plan:
+            cw = make()
+            rows = np.arange(cw.B * cw.T, dtype=np.int64) if pick is None else pick(cw)
+            vis = lambda r: cw.offset + (np.asarray(r) % cw.T) + 1
+            t0 = time.perf_counter()
+            _, _, _, _, used = oracle.select(cw, rows=rows)
+            t_meas = time.perf_counter() - t0
+            keys = int(vis(rows).sum())
+            all_keys = int(vis(np.arange(cw.B * cw.T)).sum())
+            full_s = t_meas * all_keys / keys
+            per[name] = {"rows": "all" if pick is None else f"{len(rows)} sampled",
+                         "rows_measured": int(len(rows)), "s_measured": round(t_meas, 3),
+                         "s_full_extrapolated": round(full_s, 2),
+                         "query_tok_s": round(cw.B * cw.T / full_s, 2), "threads": int(used)}
+            del cw
+        one = np.array([16383, 32767, 49151, 65535], dtype=np.int64)  # chunk-end rows, 16k to 64k keys
+        t0 = time.perf_counter()
+        _, _, _, _, used1 = oracle.select(wl, rows=one, nthreads=1)
+        t1 = time.perf_counter() - t0
+        keys1 = int(sum(wl.offset + (r % wl.T) + 1 for r in one))
+        cpu_model = None
+        try:
+            for line in open("/proc/cpuinfo"):
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+        except OSError:
+            pass
+        extra["cpu_baseline_per_config"] = {
+            "kind": "oracle", "nproc": os.cpu_count(), "cpu_model": cpu_model, "configs": per,
+            "one_thread": {"threads": int(used1), "rows": len(one), "keys": keys1, "s": round(t1, 3),
+                           "keys_per_s": round(keys1 / t1, 1),
+                           "query_tok_s_64k_equivalent": round(keys1 / t1 / (pairs / wl.T), 3)}}
 
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "query-tok/s", "n_gpus": 1,
