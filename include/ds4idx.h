@@ -104,6 +104,22 @@ const char *ds4idx_status_string(int status);
 int ds4idx_set_impl(int impl);
 int ds4idx_get_impl(void);
 
+/* Partition length of the split-key kernel, the kernel for problems with few
+ * query rows over long caches (decode): each workgroup scores one partition
+ * of a row's keys and the last one to finish merges the row. Lengths 8192,
+ * 12288 and 16384 keys are built; 0 (the default) lets the library pick per
+ * call the shortest length whose partitions all start in one round on the
+ * GPU's compute units (one partition per unit), using for ragged batches with
+ * one query per stream the bound total_k / length + B. A fixed length is for
+ * measurement and comparison: results are identical for every length. The
+ * workspace size depends on the length, so query ds4idx_workspace_bytes (or
+ * ds4idx_varlen_workspace_bytes) after changing it. The initial value comes
+ * from the environment variable DS4IDX_SPLIT (a length in keys; anything
+ * else means automatic). ds4idx_set_split returns the previous value, or -1
+ * for an unsupported length (then nothing changes). */
+int ds4idx_set_split(int keys);
+int ds4idx_get_split(void);
+
 /* Bytes of device workspace that `op` (DS4IDX_OP_*) needs for this problem
  * and k under the current kernel family, or 0 if it needs none. Returns
  * (size_t)-1 for an invalid problem. The workspace for DS4IDX_OP_SELECT must

@@ -38,7 +38,9 @@ ABI_VERSION = 1
 EXPORTS = ("ds4idx_abi_version", "ds4idx_status_string", "ds4idx_set_impl", "ds4idx_get_impl",
            "ds4idx_workspace_bytes", "ds4idx_score", "ds4idx_topk", "ds4idx_select",
            "ds4idx_k_cache_write", "ds4idx_varlen_workspace_bytes", "ds4idx_select_varlen",
-           "ds4idx_sparse_attention", "ds4idx_select_qfp8", "ds4idx_select_noalloc")
+           "ds4idx_sparse_attention", "ds4idx_select_qfp8", "ds4idx_select_noalloc", "ds4idx_set_split",
+           "ds4idx_get_split")
+SPLIT_LENS = (8192, 12288, 16384)
 
 
 class Problem(ctypes.Structure):
@@ -85,6 +87,10 @@ def lib() -> ctypes.CDLL:
         L.ds4idx_set_impl.restype = ctypes.c_int
         L.ds4idx_get_impl.argtypes = []
         L.ds4idx_get_impl.restype = ctypes.c_int
+        L.ds4idx_set_split.argtypes = [ctypes.c_int]
+        L.ds4idx_set_split.restype = ctypes.c_int
+        L.ds4idx_get_split.argtypes = []
+        L.ds4idx_get_split.restype = ctypes.c_int
         L.ds4idx_workspace_bytes.argtypes = [P, i32, i32]
         L.ds4idx_workspace_bytes.restype = sz
         L.ds4idx_score.argtypes = [P, vp, vp, vp, vp, vp, vp]
@@ -129,6 +135,20 @@ def set_impl(impl) -> int:
 
 def get_impl() -> int:
     return lib().ds4idx_get_impl()
+
+
+def set_split(keys: int) -> int:
+    """Fix the split-key kernel's partition length (8192, 12288 or 16384 keys;
+    0 = automatic) for later calls; returns the previous value. Workspaces are
+    sized for the length in force when they are created."""
+    prev = lib().ds4idx_set_split(int(keys))
+    if prev < 0:
+        raise ValueError(f"unsupported partition length {keys}; use 0 or one of {SPLIT_LENS}")
+    return prev
+
+
+def get_split() -> int:
+    return lib().ds4idx_get_split()
 
 
 def _ptr(t: Optional[torch.Tensor]):

@@ -177,6 +177,10 @@ int ds4idx_set_impl(int impl)
 
 int ds4idx_get_impl(void) { return impl_now(); }
 
+int ds4idx_set_split(int keys) { return ds4idx::set_split_len(keys); }
+
+int ds4idx_get_split(void) { return ds4idx::get_split_len(); }
+
 size_t ds4idx_workspace_bytes(const ds4idx_problem *p, int32_t k, int32_t op)
 {
     if (check_problem(p) != DS4IDX_OK) return (size_t)-1;

@@ -47,10 +47,14 @@ hipError_t launch_mfma_select_varlen(const VarlenProblem &p, const int *cu_q, co
                                      const void *Q, const void *K, const float *Ks, const float *W,
                                      int k, int *idx, float *vals, hipStream_t st);
 
-// Split-key kernel for few rows over long caches (decode): partitions of 8192
-// keys, each emitting a superset of its top k plus its m-th largest key; the
-// last-arriving workgroup of a row merges.
+// Split-key kernel for few rows over long caches (decode): partitions of
+// 8192, 12288 or 16384 keys, each emitting a superset of its top k plus its
+// m-th largest key; the last-arriving workgroup of a row merges.
 constexpr int kSplitMaxParts = 256;
+constexpr int kSplitPartLens[3] = {8192, 12288, 16384};
+constexpr int kSplitCUs = 256;  // compute units of an MI355X: one split workgroup each
+int set_split_len(int len);     // 0 = automatic; returns the previous value, -1 if unsupported
+int get_split_len();
 struct SplitWorkspace {
     uint32_t *ctr;         // [rows] arrival counters, zero between calls
     uint64_t *meta;        // [rows, P, 2] short-list edge << 32 | m-th largest key (~0: none); largest key
@@ -62,6 +66,7 @@ struct SplitWorkspace {
 // to the full lists, which for short rows are few).
 struct SplitShape {
     long long rows, max_len, short_len;
+    int part;  // partition length (keys), one of kSplitPartLens
 };
 SplitShape split_shape(const Problem &p);
 SplitShape split_shape(const VarlenProblem &p);

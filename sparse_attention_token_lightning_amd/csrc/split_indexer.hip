@@ -43,6 +43,7 @@
 #include "kernels.h"
 
 #include <atomic>
+#include <cstdlib>
 #include <mutex>
 
 namespace ds4idx {
@@ -52,8 +53,7 @@ constexpr int H = kMfmaH;
 constexpr int D = kMfmaD;
 constexpr int NW = 8;
 constexpr int THREADS = NW * 64;
-constexpr int NSUB = 32;                 // 32-key sub-blocks per wavefront
-constexpr int PART = NW * NSUB * 32;     // 8192 keys per partition
+constexpr int PL_MAX = 16384;            // longest partition (keys); see kSplitPartLens
 constexpr int HBITS = 12;                // histogram digit width
 constexpr int HBINS = 1 << HBITS;        // 4096 = 8 bins per thread
 constexpr int HSHIFT = 32 - HBITS;       // partition histogram: top 12 key bits
@@ -64,7 +64,6 @@ constexpr int GB = 16;                   // 64-slot groups per wavefront per mer
 constexpr int MAX_SLOTS = 4096;          // full-list slots for k = 2048, the largest k
 constexpr int HWORDS = HBINS + HBINS / 8;  // one pad word after every 8 bins
 static_assert(HBINS == 8 * THREADS, "each thread owns eight histogram bins");
-static_assert(PART == 1 << 13, "partition size is used as a shift");
 static_assert(HWORDS >= 2 * 2048, "the histogram words stage k <= 2048 output pairs");
 
 // LDS word of histogram bin b. The scan gives each thread 8 consecutive bins;
@@ -84,7 +83,7 @@ constexpr int QROW = D + 8;  // bf16 per LDS query row: 272 B keeps 16-byte read
 struct SplitSmem {
     union {
         struct {
-            uint32_t sc[PART + PART / 16];  // partition score keys (0 = no key) at scx(i)
+            uint32_t sc[PL_MAX + PL_MAX / 16];  // partition score keys (0 = no key) at scx(i)
             uint16_t q[H * QROW];           // the row's query, head-major (scoring only)
             float wl[H];                    // the row's head weights (scoring only)
         };
@@ -426,7 +425,7 @@ __device__ __forceinline__ float score_sub(const Raw<KFP8> &r, const uint16_t *q
 // rows hold it (see StreamGeo); rows of no stream see no keys. Every
 // partition of every row still takes part in the arrival, so the counters
 // return to zero.
-template <bool KFP8, bool VARLEN>
+template <bool KFP8, bool VARLEN, int PART>
 __global__ __launch_bounds__(THREADS, 1) void split_indexer_kernel(
     const uint16_t *__restrict__ Q, const uint8_t *__restrict__ K, const float *__restrict__ Ks,
     const float *__restrict__ W, int T, int S, long long offset, int topk, int P, int slots, int s1,
@@ -467,6 +466,8 @@ __global__ __launch_bounds__(THREADS, 1) void split_indexer_kernel(
         L = offset + t + 1;
         k0 = (long long)b * S;
     }
+    static_assert(PART % (NW * 32 * 4) == 0 && PART <= PL_MAX, "whole rounds, whole ring cycles");
+    constexpr int NSUB = PART / (NW * 32);  // 32-key sub-blocks per wavefront
     const long long pbase = (long long)p * PART;
 
     // This wavefront's keys: the partition is read in 32 rounds of 256
@@ -490,8 +491,11 @@ __global__ __launch_bounds__(THREADS, 1) void split_indexer_kernel(
     const long long wrem = L - wbase;
     const int nsub = full_part ? NROUND
                      : wrem <= 0 ? 0 : (int)(((wrem + RKEYS - 1) / RKEYS + 1) & ~1LL);  // even: whole pairs
-    const int rot0 = full_part ? p : 0;
-    auto sbase = [&](int sb) { return wbase + (long long)((sb + rot0) & (NROUND - 1)) * RKEYS; };
+    const int rot0 = full_part ? p % NROUND : 0;
+    auto sbase = [&](int sb) {
+        const int rr = sb + rot0;
+        return wbase + (long long)(rr >= NROUND ? rr - NROUND : rr) * RKEYS;
+    };
     const uint8_t *Kr = K + (size_t)k0 * (KFP8 ? D : 2 * D);
     const float *Ksr = KFP8 ? Ks + (size_t)k0 : nullptr;
     constexpr int NBUF = KFP8 ? 4 : 2;
@@ -556,18 +560,18 @@ __global__ __launch_bounds__(THREADS, 1) void split_indexer_kernel(
     // rounds in order, so they are the last ones) hold no key.
     for (int i = nsub + (lane >> 5); i < NROUND; i += 2) sm.sc[scx(i * RKEYS + wid * 32 + (lane & 31))] = 0u;
     __syncthreads();
-    // From here on thread t holds the keys of indices pbase + 16t .. +15.
-    constexpr int KPT = PART / THREADS;  // 16
+    // From here on thread t holds the keys of indices pbase + KPT t .. +KPT-1.
+    constexpr int KPT = PART / THREADS;  // 16, 24 or 32
     uint32_t u[KPT];
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) u[j] = sm.sc[KPT * tid + tid + j];
+    for (int j = 0; j < KPT; ++j) u[j] = sm.sc[scx(KPT * tid + j)];
     const long long ibase = pbase + (long long)KPT * tid;
 
     // ---- bins of the partition's k-th, m-th and c1-th largest keys. The
     // full partitions of the row (PART keys each) alone hold fullp*m >= k
     // keys. Only nonzero keys are counted: the all-ones NaN pattern maps to
     // key 0, which reads as "no key" everywhere.
-    const uint32_t fullp = (uint32_t)(L >> 13);  // L / PART
+    const uint32_t fullp = (uint32_t)(L / PART);
     const uint32_t mth = fullp > 0 ? ((uint32_t)topk + fullp - 1) / fullp : 0u;  // 0: no bound
     const uint32_t c1 = (uint32_t)(s1 / 4);
     uint32_t mykmax = 0, kmax;
@@ -798,7 +802,7 @@ __global__ __launch_bounds__(THREADS, 1) void split_indexer_kernel(
             }
         }
         __syncthreads();
-        constexpr int KPT = PART / THREADS;  // 16 slots per thread
+        constexpr int KPT = MSURV / THREADS;  // 16 slots per thread
         uint32_t kk[KPT];
 #pragma unroll
         for (int j = 0; j < KPT; ++j) kk[j] = KPT * tid + j < nslot ? sm.sv.key[KPT * tid + tid + j] : 0u;
@@ -981,26 +985,89 @@ hipError_t launch_t(const Problem &p, const SplitShape &sh, const Ragged &rg, co
 {
     const int P = split_parts(sh);
     SplitWorkspace w = split_workspace(ws, sh, k);
-    hipLaunchKernelGGL((split_indexer_kernel<KFP8, VARLEN>), dim3(P, (unsigned)sh.rows), dim3(THREADS), 0, st,
-                       static_cast<const uint16_t *>(Q), static_cast<const uint8_t *>(K), Ks, W,
-                       p.T, p.S, p.offset, k, P, split_slots(k), split_short_slots(sh, k), w.ctr, w.meta,
-                       w.full_list, w.short_list, idx, vals, rg);
+    auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, dim3(P, (unsigned)sh.rows), dim3(THREADS), 0, st,
+                           static_cast<const uint16_t *>(Q), static_cast<const uint8_t *>(K), Ks, W, p.T, p.S,
+                           p.offset, k, P, split_slots(k), split_short_slots(sh, k), w.ctr, w.meta, w.full_list,
+                           w.short_list, idx, vals, rg);
+    };
+    if (sh.part == kSplitPartLens[2]) go(split_indexer_kernel<KFP8, VARLEN, kSplitPartLens[2]>);
+    else if (sh.part == kSplitPartLens[1]) go(split_indexer_kernel<KFP8, VARLEN, kSplitPartLens[1]>);
+    else go(split_indexer_kernel<KFP8, VARLEN, kSplitPartLens[0]>);
     return hipGetLastError();
+}
+
+std::atomic<int> g_split_len{-1};  // -1: not read from the environment yet; 0: automatic
+
+bool supported_len(int len)
+{
+    for (int l : kSplitPartLens)
+        if (len == l) return true;
+    return false;
+}
+
+int split_len_now()
+{
+    int v = g_split_len.load(std::memory_order_relaxed);
+    if (v >= 0) return v;
+    int init = 0;
+    if (const char *e = std::getenv("DS4IDX_SPLIT")) {
+        const int x = std::atoi(e);
+        if (supported_len(x)) init = x;
+    }
+    int expected = -1;
+    g_split_len.compare_exchange_strong(expected, init);
+    return g_split_len.load(std::memory_order_relaxed);
+}
+
+// Partition length: the override if set, else the shortest length whose
+// partitions (`blocks(len)`, at most) all start in one round on the GPU's
+// compute units, else the shortest. One workgroup runs per CU, so a batch
+// that needs a second round of partitions pays for a whole second round.
+template <class Blocks>
+int pick_part(Blocks blocks)
+{
+    const int o = split_len_now();
+    if (o) return o;
+    for (int l : kSplitPartLens)
+        if (blocks((long long)l) <= kSplitCUs) return l;
+    return kSplitPartLens[0];
 }
 
 }  // namespace
 
+int set_split_len(int len)
+{
+    if (len != 0 && !supported_len(len)) return -1;
+    const int prev = split_len_now();
+    g_split_len.store(len, std::memory_order_relaxed);
+    return prev;
+}
+
+int get_split_len() { return split_len_now(); }
+
 SplitShape split_shape(const Problem &p)
 {
-    return SplitShape{(long long)p.B * p.T, p.offset + p.T, p.offset + 1};
+    const long long rows = (long long)p.B * p.T, max_len = p.offset + p.T;
+    const int part = pick_part([&](long long l) { return rows * ((max_len + l - 1) / l); });
+    return SplitShape{rows, max_len, p.offset + 1, part};
 }
 
 SplitShape split_shape(const VarlenProblem &p)
 {
-    return SplitShape{p.total_q, p.max_k, p.max_k};
+    // The stream lengths are on the device. With one query per stream the
+    // nonempty partitions number at most total_k / len + B, exactly
+    // B ceil(max_k / len) when every stream holds max_k keys; with several
+    // queries per stream there is no such bound here.
+    const int part = pick_part([&](long long l) {
+        if (p.total_q != p.B) return (long long)p.total_q * ((p.max_k + l - 1) / l);
+        if (p.total_k == (long long)p.B * p.max_k) return (long long)p.B * ((p.max_k + l - 1) / l);
+        return (p.total_k + l - 1) / l + p.B;
+    });
+    return SplitShape{p.total_q, p.max_k, p.max_k, part};
 }
 
-int split_parts(const SplitShape &sh) { return (int)((sh.max_len + PART - 1) / PART); }
+int split_parts(const SplitShape &sh) { return (int)((sh.max_len + sh.part - 1) / sh.part); }
 
 int split_slots(int k) { return (2 * k + 63) / 64 * 64; }
 
@@ -1009,7 +1076,7 @@ int split_short_slots(const SplitShape &sh, int k)
     // Room for the keys from the bin of the c1-th largest up, c1 = 4m (m =
     // ceil(k / full partitions) of the row with the fewest): the kernel takes
     // c1 = slots / 4, so the bin may hold up to 3 c1 further keys.
-    const long long fullp = sh.short_len / PART;
+    const long long fullp = sh.short_len / sh.part;
     if (fullp < 1) return 64;
     const long long m = (k + fullp - 1) / fullp;
     const long long s = (16 * m + 63) / 64 * 64;

@@ -229,11 +229,52 @@ def test_varlen_empty_batch_is_a_no_op():
 
 def test_varlen_workspace_matches_uniform_decode():
     # 8 streams of one query over 262144 keys: the same split-key workspace as
-    # the uniform decode problem
+    # the uniform decode problem, under the automatic and every fixed
+    # partition length
     v = _vprob(B=8, total_q=8, total_k=8 * 262144, max_k=262144)
     u = ds.Problem(8, 1, 262144, 64, 128, 262143, ds.BF16, ds.FP8_E4M3)
-    assert ds.lib().ds4idx_varlen_workspace_bytes(ctypes.byref(v), 512) == \
-        ds.lib().ds4idx_workspace_bytes(ctypes.byref(u), 512, ds.OP_SELECT)
+    prev = ds.set_split(0)
+    try:
+        for keys in (0,) + ds.SPLIT_LENS:
+            ds.set_split(keys)
+            assert ds.lib().ds4idx_varlen_workspace_bytes(ctypes.byref(v), 512) == \
+                ds.lib().ds4idx_workspace_bytes(ctypes.byref(u), 512, ds.OP_SELECT)
+    finally:
+        ds.set_split(prev)
+
+
+def test_split_length_switch_and_automatic_choice():
+    prev = ds.set_split(0)
+    try:
+        assert ds.get_split() == 0
+        with pytest.raises(ValueError):
+            ds.set_split(10000)
+        assert ds.get_split() == 0 and ds.lib().ds4idx_set_split(4096) == -1
+        dec = ds.Problem(8, 1, 262144, 64, 128, 262143, ds.BF16, ds.FP8_E4M3)
+        auto = ds.workspace_bytes(dec, 512)
+        ds.set_split(8192)
+        assert ds.workspace_bytes(dec, 512) == auto  # 8 x 32 partitions fill the 256 CUs
+        ds.set_split(16384)
+        assert ds.workspace_bytes(dec, 512) < auto   # half the partitions
+        assert ds.set_split(0) == 16384
+        # 10 streams: 320 partitions of 8192 keys would need two rounds; 12288
+        # keys gives 220, one round
+        ten = ds.Problem(10, 1, 262144, 64, 128, 262143, ds.BF16, ds.FP8_E4M3)
+        auto10 = ds.workspace_bytes(ten, 512)
+        ds.set_split(12288)
+        assert ds.workspace_bytes(ten, 512) == auto10
+        ds.set_split(0)
+        # the ragged decode mix: 64 streams of 4096 + 910 b keys (2,096,704 in
+        # all, at most 61426): 2096704 / 8192 + 64 > 256 partitions, so 12288
+        lens = [4096 + 910 * b for b in range(64)]
+        v = _vprob(B=64, total_q=64, total_k=sum(lens), max_k=max(lens))
+        autov = ds.varlen_workspace_bytes(v, 512)
+        ds.set_split(12288)
+        assert ds.varlen_workspace_bytes(v, 512) == autov
+        ds.set_split(8192)
+        assert ds.varlen_workspace_bytes(v, 512) > autov
+    finally:
+        ds.set_split(prev)
 
 
 def _aprob(**kw):

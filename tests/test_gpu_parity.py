@@ -338,3 +338,45 @@ def test_split_long_cache_decode(S, topk, B):
     gi, gv = run_select(wl, poison=True)
     check_invariants(wl, gi)
     compare_rows(wl, np.arange(wl.B * wl.T), gi, gv, exact=False)
+
+
+# ------------------------------------------------------------------ partition lengths
+
+def _split_cases():
+    c = {}
+    c["decode B=3 S=100000"] = W.decode(seed=91, B=3, S=100000, topk=512)
+    w = W.prefill_fp8(seed=92, T=5, S=40000, offset=39995, topk=512, chunk=5)
+    w.chunks = [(0, 5, 40000, 39995)]
+    c["fp8 T=5 S=40000"] = w
+    w = W.prefill_bf16(seed=93, T=3, S=30001, offset=29998, topk=300, B=2)
+    w.chunks = [(0, 3, 30001, 29998)]
+    c["bf16 B=2 T=3 S=30001 k=300"] = w
+    c["decode B=2 S=262144 k=2048"] = W.decode(seed=94, B=2, S=262144, topk=2048)
+    w = W.decode(seed=95, B=2, S=50000, topk=512)
+    w.k[:] = 0  # every score 0: exact partition selection, tie-break by index
+    c["all-equal B=2 S=50000"] = w
+    return c
+
+
+@pytest.mark.parametrize("keys", [8192, 12288, 16384])
+def test_split_partition_lengths_identical(keys):
+    # Scores and the exact selection do not depend on how the keys are split,
+    # so every partition length returns the same indices and values, bit for
+    # bit, as the automatic choice (the first case is also checked against
+    # the oracle).
+    prev = ds.set_split(0)
+    try:
+        for n, (name, wl) in enumerate(_split_cases().items()):
+            _say(f"split length {keys}: {name}")
+            dev = to_device(wl)
+            ds.set_split(0)
+            ai, av = run_select(wl, dev=dev, poison=True)
+            ds.set_split(keys)
+            gi, gv = run_select(wl, dev=dev, poison=True)
+            check_invariants(wl, gi)
+            assert np.array_equal(gi, ai), f"{name}: indices differ between lengths"
+            assert np.array_equal(gv.view(np.uint32), av.view(np.uint32)), f"{name}: values differ"
+            if n == 0:
+                compare_rows(wl, np.arange(wl.B * wl.T), gi, gv, exact=False)
+    finally:
+        ds.set_split(prev)

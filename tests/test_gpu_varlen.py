@@ -199,3 +199,23 @@ def test_workspace_reuse_across_ragged_batches():
     np.testing.assert_array_equal(first[0], again[0])
     np.testing.assert_array_equal(first[1], again[1])
     check_against_oracle(b, other[0], other[1], exact=False)
+
+
+@pytest.mark.parametrize("keys", [8192, 12288, 16384])
+def test_ragged_partition_lengths_identical(keys):
+    # The ragged decode mixes under every partition length return what the
+    # automatic choice returns (12288 for the bench mix), bit for bit.
+    prev = ds.set_split(0)
+    try:
+        for name, mix, seed in (("bench decode mix", BENCH_DECODE_MIX, 47), ("decode mix", DECODE_MIX, 41)):
+            rg = W.ragged(seed, mix)
+            dev = _dev(rg)
+            _say(f"ragged {name}, partition length {keys}")
+            ds.set_split(0)
+            ai, av = run_varlen(rg, dev=dev)
+            ds.set_split(keys)
+            gi, gv = run_varlen(rg, dev=dev)
+            assert np.array_equal(gi, ai), f"{name}: indices differ between lengths"
+            assert np.array_equal(gv.view(np.uint32), av.view(np.uint32)), f"{name}: values differ"
+    finally:
+        ds.set_split(prev)
