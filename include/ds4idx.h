@@ -120,6 +120,21 @@ int ds4idx_get_impl(void);
 int ds4idx_set_split(int keys);
 int ds4idx_get_split(void);
 
+/* Key parts for ragged prefill batches (ds4idx_select_varlen on the prefill
+ * kernel): in a small batch the 8-token blocks of the longest caches set the
+ * pace while other compute units idle, so each block's visible keys can be
+ * split into up to 4 parts, each scored by its own workgroup; the part that
+ * finishes last merges the parts' exact selections per token (the result is
+ * identical to the unsplit one). 0 (default): parts of 8192 keys when the
+ * longest cache exceeds 8192 keys and the batch has at most two rounds of
+ * blocks for the GPU's compute units; -1: never; a positive value: parts of
+ * that many keys (rounded up to a multiple of 128, and at least a quarter of
+ * max_k). Parts need workspace, so query ds4idx_varlen_workspace_bytes after
+ * changing this. Initial value from the environment variable
+ * DS4IDX_PREFILL_SPLIT. ds4idx_set_prefill_split returns the previous value. */
+int ds4idx_set_prefill_split(int keys);
+int ds4idx_get_prefill_split(void);
+
 /* Bytes of device workspace that `op` (DS4IDX_OP_*) needs for this problem
  * and k under the current kernel family, or 0 if it needs none. Returns
  * (size_t)-1 for an invalid problem. The workspace for DS4IDX_OP_SELECT must
@@ -198,7 +213,9 @@ typedef struct {
 } ds4idx_varlen_problem;
 
 /* Workspace bytes for ds4idx_select_varlen (0 if none), or (size_t)-1 for an
- * invalid problem. Same zero-fill and alignment rules as ds4idx_select's. */
+ * invalid problem: the split-key kernel's lists, or the prefill kernel's key
+ * parts (see ds4idx_set_prefill_split). Same zero-fill and alignment rules as
+ * ds4idx_select's. */
 size_t ds4idx_varlen_workspace_bytes(const ds4idx_varlen_problem *p, int32_t k);
 
 /* Fused scorer + top-k over a ragged batch (see above). 1 <= k <= DS4IDX_MAX_TOPK;

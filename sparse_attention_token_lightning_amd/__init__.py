@@ -39,7 +39,7 @@ EXPORTS = ("ds4idx_abi_version", "ds4idx_status_string", "ds4idx_set_impl", "ds4
            "ds4idx_workspace_bytes", "ds4idx_score", "ds4idx_topk", "ds4idx_select",
            "ds4idx_k_cache_write", "ds4idx_varlen_workspace_bytes", "ds4idx_select_varlen",
            "ds4idx_sparse_attention", "ds4idx_select_qfp8", "ds4idx_select_noalloc", "ds4idx_set_split",
-           "ds4idx_get_split")
+           "ds4idx_get_split", "ds4idx_set_prefill_split", "ds4idx_get_prefill_split")
 SPLIT_LENS = (8192, 12288, 16384)
 
 
@@ -91,6 +91,10 @@ def lib() -> ctypes.CDLL:
         L.ds4idx_set_split.restype = ctypes.c_int
         L.ds4idx_get_split.argtypes = []
         L.ds4idx_get_split.restype = ctypes.c_int
+        L.ds4idx_set_prefill_split.argtypes = [ctypes.c_int]
+        L.ds4idx_set_prefill_split.restype = ctypes.c_int
+        L.ds4idx_get_prefill_split.argtypes = []
+        L.ds4idx_get_prefill_split.restype = ctypes.c_int
         L.ds4idx_workspace_bytes.argtypes = [P, i32, i32]
         L.ds4idx_workspace_bytes.restype = sz
         L.ds4idx_score.argtypes = [P, vp, vp, vp, vp, vp, vp]
@@ -149,6 +153,17 @@ def set_split(keys: int) -> int:
 
 def get_split() -> int:
     return lib().ds4idx_get_split()
+
+
+def set_prefill_split(keys: int) -> int:
+    """Key parts for ragged prefill batches: 0 automatic, -1 never, or a part
+    length in keys; returns the previous value. Workspaces are sized for the
+    setting in force when they are created."""
+    return lib().ds4idx_set_prefill_split(int(keys))
+
+
+def get_prefill_split() -> int:
+    return lib().ds4idx_get_prefill_split()
 
 
 def _ptr(t: Optional[torch.Tensor]):

@@ -140,7 +140,7 @@ int route_varlen(const ds4idx_varlen_problem *p, int32_t k)
                        (v.k_dtype == DS4IDX_BF16 || v.k_dtype == DS4IDX_FP8_E4M3);
     if (!shape) return R_NONE;
     const long long blocks = ds4idx::mfma_varlen_blocks(v.B, v.total_q);
-    const bool prefill_ok = k <= ds4idx::kMfmaMaxK && blocks <= (long long)INT32_MAX;
+    const bool prefill_ok = k <= ds4idx::kMfmaMaxK && blocks * ds4idx::kPrefillMaxParts <= (long long)INT32_MAX;
     const bool split_ok = v.total_q <= 65535 &&
                           ds4idx::split_parts(ds4idx::split_shape(v)) <= ds4idx::kSplitMaxParts;
     if (split_ok && (blocks < 128 || !prefill_ok)) return R_SPLIT;
@@ -180,6 +180,10 @@ int ds4idx_get_impl(void) { return impl_now(); }
 int ds4idx_set_split(int keys) { return ds4idx::set_split_len(keys); }
 
 int ds4idx_get_split(void) { return ds4idx::get_split_len(); }
+
+int ds4idx_set_prefill_split(int keys) { return ds4idx::set_prefill_split(keys); }
+
+int ds4idx_get_prefill_split(void) { return ds4idx::get_prefill_split(); }
 
 size_t ds4idx_workspace_bytes(const ds4idx_problem *p, int32_t k, int32_t op)
 {
@@ -306,7 +310,10 @@ int ds4idx_k_cache_write(const void *K_new, int32_t k_dtype, int64_t n, int32_t 
 size_t ds4idx_varlen_workspace_bytes(const ds4idx_varlen_problem *p, int32_t k)
 {
     if (check_varlen(p) != DS4IDX_OK || k < 1 || k > DS4IDX_MAX_TOPK) return (size_t)-1;
-    if (route_varlen(p, k) != R_SPLIT || p->total_q == 0) return 0;
+    if (p->total_q == 0) return 0;
+    const int r = route_varlen(p, k);
+    if (r == R_PREFILL) return ds4idx::prefill_parts_workspace_bytes(to_internal(p), k);
+    if (r != R_SPLIT) return 0;
     return ds4idx::split_workspace_bytes(ds4idx::split_shape(to_internal(p)), k);
 }
 
@@ -329,8 +336,12 @@ int ds4idx_select_varlen(const ds4idx_varlen_problem *p, const int32_t *cu_q, co
     hipStream_t s = static_cast<hipStream_t>(stream);
     static_assert(sizeof(long long) == sizeof(int64_t), "int64 prefix sums");
     const long long *ck = reinterpret_cast<const long long *>(cu_k);
-    if (r == R_PREFILL)
-        return launch_status(ds4idx::launch_mfma_select_varlen(v, cu_q, ck, Q, K, K_scale, W, k, idx, vals, s));
+    if (r == R_PREFILL) {
+        const size_t pneed = ds4idx::prefill_parts_workspace_bytes(v, k);
+        if (pneed > 0 && (!workspace || !aligned(workspace, 256) || ws_bytes < pneed)) return DS4IDX_ERR_WORKSPACE;
+        return launch_status(
+            ds4idx::launch_mfma_select_varlen(v, cu_q, ck, Q, K, K_scale, W, k, idx, vals, workspace, s));
+    }
     const size_t need = ds4idx::split_workspace_bytes(ds4idx::split_shape(v), k);
     if (!workspace || !aligned(workspace, 256) || ws_bytes < need) return DS4IDX_ERR_WORKSPACE;
     return launch_status(

@@ -27,6 +27,21 @@ __device__ __forceinline__ float key_float(uint32_t o)
 
 __device__ __forceinline__ uint64_t wave_ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
 
+// Device-scope (agent) relaxed stores and loads: the candidate lists that one
+// workgroup publishes and another, on any XCD, merges after an arrival
+// counter (global_store / global_load with sc1 on gfx950).
+template <class V>
+__device__ __forceinline__ void store_agent(V *p, V v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <class V>
+__device__ __forceinline__ V load_agent(const V *p)
+{
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Number of set bits of m in lanes below the calling lane.
 __device__ __forceinline__ uint32_t lanes_below(uint64_t m)
 {
@@ -140,12 +155,22 @@ __device__ __forceinline__ int wave_row_stream(const int *cu_q, const long long 
     return -1;
 }
 
-// Block x of a grid giving each stream ceil(min(T, S) / tq) blocks, streams in
-// order: returns the stream (-1 past the last block) and sets j, the block's
-// index within the stream. Wave-uniform result.
+// Parts a stream's key range is split into when blocks take at most kpart
+// keys each (kpart = 0: one part). At most `maxp`.
+__device__ __forceinline__ int stream_parts(long long S, int kpart, int maxp)
+{
+    if (kpart <= 0 || S <= kpart) return 1;
+    const long long n = (S + kpart - 1) / kpart;
+    return (int)(n < maxp ? n : maxp);
+}
+
+// Block x of a grid giving each stream ceil(min(T, S) / tq) * parts blocks
+// (parts from stream_parts(S, kpart, maxp)), streams in order: returns the
+// stream (-1 past the last block) and sets j, the block's index within the
+// stream. Wave-uniform result.
 __device__ __forceinline__ int wave_block_stream(const int *cu_q, const long long *cu_k, int B,
                                                  int total_q, long long total_k, int tq, long long x,
-                                                 int lane, int &j)
+                                                 int lane, int &j, int kpart = 0, int maxp = 1)
 {
     long long base = 0;
     for (int c = 0; c < B; c += 64) {
@@ -154,7 +179,7 @@ __device__ __forceinline__ int wave_block_stream(const int *cu_q, const long lon
         if (s < B) {
             const StreamGeo g = stream_geo(cu_q, cu_k, s, total_q, total_k);
             const long long t = (long long)g.T < g.S ? (long long)g.T : g.S;
-            nb = (uint32_t)((t + tq - 1) / tq);
+            nb = (uint32_t)((t + tq - 1) / tq) * (uint32_t)stream_parts(g.S, kpart, maxp);
         }
         const uint32_t incl = wave_scan_incl(nb, 0u, OpAdd{});
         const long long lo = base + (long long)(incl - nb), hi = base + (long long)incl;

@@ -43,9 +43,26 @@ hipError_t launch_mfma_select(const Problem &p, const void *Q, const void *K, co
 hipError_t launch_mfma_select_qfp8(const Problem &p, const void *Q8, const float *QS, const void *K, const float *Ks,
                                    const float *W, int k, int *idx, float *vals, hipStream_t st);
 long long mfma_varlen_blocks(int B, int total_q);
+// Ragged prefill with key parts: an 8-token block's visible keys are split
+// into up to kPrefillMaxParts parts of kpart keys (a multiple of 128), each
+// scored by its own workgroup, which publishes its exact top k per token; the
+// last part to arrive merges. Workspace: [total_q] arrival counters (zero
+// between calls), [total_q, kPrefillMaxParts] counts, [total_q,
+// kPrefillMaxParts, k] (index << 32 | order key) entries.
+constexpr int kPrefillMaxParts = 4;
+struct PrefillParts {
+    int kpart;  // keys per part; 0 = no parts
+    uint64_t *list;
+    uint32_t *cnt;
+    uint32_t *ctr;
+};
+int set_prefill_split(int keys);  // -1 never, 0 automatic, > 0 part length; returns the previous value
+int get_prefill_split();
+int prefill_kpart(const VarlenProblem &p);  // 0: no parts for this problem
+size_t prefill_parts_workspace_bytes(const VarlenProblem &p, int k);
 hipError_t launch_mfma_select_varlen(const VarlenProblem &p, const int *cu_q, const long long *cu_k,
                                      const void *Q, const void *K, const float *Ks, const float *W,
-                                     int k, int *idx, float *vals, hipStream_t st);
+                                     int k, int *idx, float *vals, void *ws, hipStream_t st);
 
 // Split-key kernel for few rows over long caches (decode): partitions of
 // 8192, 12288 or 16384 keys, each emitting a superset of its top k plus its

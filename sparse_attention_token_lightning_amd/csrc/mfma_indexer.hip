@@ -45,6 +45,9 @@
 #include "kernels.h"
 #include "wave_select.h"
 
+#include <atomic>
+#include <cstdlib>
+
 namespace ds4idx {
 namespace {
 
@@ -69,6 +72,7 @@ struct alignas(16) Smem {
     float cs[TQ][CAP];
     int ci[TQ][CAP];
     uint32_t hist[NWAVE][256];
+    int last;  // split parts: this block arrived last for its 8 tokens
 };
 
 // v_mfma_f32_16x16x32_bf16 operand layout: lane l supplies row (A) or column
@@ -240,6 +244,97 @@ __device__ __forceinline__ void store_tile(Smem &sm, int buf, const TileRegs<KFP
     }
 }
 
+// Key parts (SPLITK): each wavefront holds its token's exact selection among
+// this part's keys (cs/ci, cnt entries in index order). It is published with
+// device-scope stores; after every wavefront's stores have completed and the
+// workgroup has passed a barrier, one lane counts the part in; the workgroup
+// that sees the last count merges, each wavefront its token: the parts'
+// lists, concatenated in part order (= index order), go into registers, the
+// exact k-th key comes from register radix passes, and an ordered ballot
+// compaction writes the row. The same instruction-level handoff as the
+// split-key kernel's (see there).
+__device__ __forceinline__ void parts_finish(Smem &sm, float *cs, int *ci, int cnt, int topk, bool tok_ok,
+                                             long long q0, int tok, int t0, int part, int nparts,
+                                             const PrefillParts &pw, int *__restrict__ idx,
+                                             float *__restrict__ vals)
+{
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const long long row = q0 + tok;
+    if (tok_ok) {
+        wave_lds_sync();
+        if (cnt > topk) {
+            wave_keep_topk(cs, ci, cnt, topk, sm.hist[wid], lane);
+            cnt = topk;
+        }
+        uint64_t *lst = pw.list + ((size_t)row * kPrefillMaxParts + part) * topk;
+        for (int i = lane; i < cnt; i += 64) store_agent(&lst[i], ((uint64_t)(uint32_t)ci[i] << 32) | ord_key(cs[i]));
+        if (lane == 0) store_agent(&pw.cnt[row * kPrefillMaxParts + part], (uint32_t)cnt);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    uint32_t *ctr = pw.ctr + (q0 + t0);  // one counter per 8-token block: its first row
+    if (tid == 0)
+        sm.last = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(nparts - 1);
+    __syncthreads();
+    if (!sm.last) return;
+    if (tok_ok) {
+        constexpr int MC = kPrefillMaxParts * kMfmaMaxK / 64;  // entries per lane
+        uint32_t pc[kPrefillMaxParts], tot = 0;
+#pragma unroll
+        for (int q = 0; q < kPrefillMaxParts; ++q) {
+            pc[q] = q < nparts ? load_agent(&pw.cnt[row * kPrefillMaxParts + q]) : 0u;
+            tot += pc[q];
+        }
+        const uint64_t *rl = pw.list + (size_t)row * kPrefillMaxParts * topk;
+        uint32_t u[MC];
+        int iv[MC];
+#pragma unroll
+        for (int j = 0; j < MC; ++j) {
+            const uint32_t e = (uint32_t)(j * 64 + lane);
+            uint32_t base = 0;
+            int q = 0;
+#pragma unroll
+            for (int qq = 0; qq < kPrefillMaxParts - 1; ++qq)
+                if (q == qq && e >= base + pc[qq]) {
+                    base += pc[qq];
+                    q = qq + 1;
+                }
+            u[j] = 0u;
+            iv[j] = 0;
+            if (e < tot) {
+                const uint64_t v = load_agent(&rl[(size_t)q * topk + (e - base)]);
+                u[j] = (uint32_t)v;
+                iv[j] = (int)(v >> 32);
+            }
+        }
+        uint32_t tau = 0, ties = 0;  // at most k entries: every one is kept
+        if (tot > (uint32_t)topk) tau = wave_kth_key<MC>(u, (uint32_t)topk, sm.hist[wid], lane, ties);
+        int *io = idx + row * topk;
+        float *vo = vals ? vals + row * topk : nullptr;
+        uint32_t out = 0, eqseen = 0;
+#pragma unroll
+        for (int j = 0; j < MC; ++j) {
+            const uint32_t key = u[j];
+            const bool eq = key != 0u && key == tau;
+            const uint64_t meq = wave_ballot(eq);
+            const bool keep = key != 0u && (key > tau || (eq && eqseen + lanes_below(meq) < ties));
+            const uint64_t mk = wave_ballot(keep);
+            if (keep) {
+                const uint32_t pos = out + lanes_below(mk);
+                io[pos] = iv[j];
+                if (vo) vo[pos] = key_float(key);
+            }
+            out += (uint32_t)__builtin_popcountll(mk);
+            eqseen += (uint32_t)__builtin_popcountll(meq);
+        }
+        for (int j = (int)out + lane; j < topk; j += 64) {
+            io[j] = -1;
+            if (vo) vo[j] = -INFINITY;
+        }
+    }
+    if (tid == 0) *ctr = 0u;
+}
+
 // Ragged batches (VARLEN): the streams of rg (see StreamGeo); the grid's x
 // dimension covers every stream's 8-token blocks, and blocks past the last
 // one exit at once.
@@ -249,22 +344,26 @@ __device__ __forceinline__ void store_tile(Smem &sm, int buf, const TileRegs<KFP
 // one v_mfma_scale_f32_16x16x128_f8f6f4 over all 128 dims (unit block
 // scales): the same lane mapping for both operands (lane l: row or column
 // l % 16, bytes 32 (l / 16) .. +31) pairs their contraction elements.
-template <bool KFP8, bool SCORE, bool VARLEN, bool QFP8>
+template <bool KFP8, bool SCORE, bool VARLEN, bool QFP8, bool SPLITK = false>
 __global__ __launch_bounds__(THREADS, 1) void mfma_indexer_kernel(
     const uint16_t *__restrict__ Q, const uint8_t *__restrict__ K, const float *__restrict__ Ks,
     const float *__restrict__ W, int T, int S, long long offset, int topk, int *__restrict__ idx,
-    float *__restrict__ vals, float *__restrict__ scores, const float *__restrict__ QS, Ragged rg)
+    float *__restrict__ vals, float *__restrict__ scores, const float *__restrict__ QS, Ragged rg,
+    PrefillParts pp_ws = PrefillParts{})
 {
     static_assert(!QFP8 || (KFP8 && !SCORE && !VARLEN), "the fp8 x fp8 scorer is the E4M3-key select");
+    static_assert(!SPLITK || (VARLEN && !SCORE && !QFP8), "key parts are a ragged-select feature");
     __shared__ Smem sm;
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     // This block's stream: first query row q0, first key row k0, Tb queries
     // over Sb cached keys, query t seeing keys <= offb + t.
     long long q0, k0, offb;
     int Tb, Sb, t0;
+    int part = 0, nparts = 1;  // key part of this block (SPLITK), of nparts
     if constexpr (VARLEN) {
         int j = 0;
-        const int bs = wave_block_stream(rg.cu_q, rg.cu_k, rg.B, rg.total_q, rg.total_k, TQ, blockIdx.x, lane, j);
+        const int bs = wave_block_stream(rg.cu_q, rg.cu_k, rg.B, rg.total_q, rg.total_k, TQ, blockIdx.x, lane, j,
+                                         SPLITK ? pp_ws.kpart : 0, kPrefillMaxParts);
         if (bs < 0) return;  // the same for every wavefront of the block
         const StreamGeo g = stream_geo(rg.cu_q, rg.cu_k, bs, rg.total_q, rg.total_k);
         q0 = g.q0;
@@ -272,6 +371,11 @@ __global__ __launch_bounds__(THREADS, 1) void mfma_indexer_kernel(
         Sb = (int)(g.S < 0x7fffffffLL ? g.S : 0x7fffffffLL);
         Tb = g.T < Sb ? g.T : Sb;  // rows past the cache (malformed input) are dropped
         offb = (long long)g.S - g.T;
+        if constexpr (SPLITK) {
+            nparts = stream_parts(g.S, pp_ws.kpart, kPrefillMaxParts);
+            part = j % nparts;
+            j /= nparts;
+        }
         t0 = ((Tb + TQ - 1) / TQ - 1 - j) * TQ;  // longest rows of the stream first
     } else {
         const int nblk = (T + TQ - 1) / TQ;
@@ -319,7 +423,19 @@ __global__ __launch_bounds__(THREADS, 1) void mfma_indexer_kernel(
 
     const long long blk_last = offb + (t0 + TQ < Tb ? t0 + TQ : Tb) - 1;  // last key any token sees
     const long long nkeys = SCORE ? (long long)Sb : blk_last + 1;
-    const int ntiles = (int)((nkeys + KT - 1) / KT);
+    // Tiles tlo .. thi-1: every tile of the visible keys, or with key parts
+    // (SPLITK) those of part `part`: keys part*kpart .. (part+1)*kpart - 1,
+    // the last part taking the rest (kpart is a multiple of KT).
+    int tlo = 0, thi = (int)((nkeys + KT - 1) / KT);
+    if constexpr (SPLITK) {
+        if (nparts > 1) {
+            const int per = pp_ws.kpart / KT;
+            tlo = part * per;
+            if (part < nparts - 1) thi = thi < tlo + per ? thi : tlo + per;
+            if (thi < tlo) thi = tlo;
+        }
+    }
+    const int ntiles = thi - tlo;
     const uint8_t *Kb = K + (size_t)k0 * (KFP8 ? D : 2 * D);
     const float *Ksb = KFP8 ? Ks + (size_t)k0 : nullptr;
     float *cs = sm.cs[wid];
@@ -329,7 +445,7 @@ __global__ __launch_bounds__(THREADS, 1) void mfma_indexer_kernel(
 
     TileRegs<KFP8> tr;
     float tsc;
-    load_tile<KFP8>(tr, tsc, Kb, Ksb, Sb, 0, tid);
+    load_tile<KFP8>(tr, tsc, Kb, Ksb, Sb, tlo, tid);
     if constexpr (QFP8) store_tile_raw(sm, 0, tr, tsc, tid);
     else store_tile<KFP8>(sm, 0, tr, tsc, tid);
     __syncthreads();
@@ -488,9 +604,10 @@ __global__ __launch_bounds__(THREADS, 1) void mfma_indexer_kernel(
     // barrier: by that finish, other wavefronts may already be staging the
     // tile after next into the same scale buffer.
     float pend_scale = 1.0f;
-    for (int tile = 0; tile < ntiles; ++tile) {
-        const int cur = tile & 1;
-        if (tile + 1 < ntiles) load_tile<KFP8>(tr, tsc, Kb, Ksb, Sb, tile + 1, tid);
+    for (int it = 0; it < ntiles; ++it) {
+        const int tile = tlo + it;
+        const int cur = it & 1;
+        if (it + 1 < ntiles) load_tile<KFP8>(tr, tsc, Kb, Ksb, Sb, tile + 1, tid);
         const long long kbase = (long long)tile * KT;
 #pragma unroll
         for (int pp = 0; pp < KT / 64; ++pp) {
@@ -498,20 +615,20 @@ __global__ __launch_bounds__(THREADS, 1) void mfma_indexer_kernel(
             phase(0, cur, pp, h1);  // MFMAs of this pair's first half; previous pair's second half reduced
             if (pp > 0)
                 finish_pair(prev0, h1, kbase + pp * 64 - 64, KFP8 ? sm.scale[cur][(pp - 1) * 64 + lane] : 1.0f);
-            else if (tile > 0)
+            else if (it > 0)
                 finish_pair(prev0, h1, kbase - 64, pend_scale);
             phase(1, cur, pp, h0);  // MFMAs of the second half; this pair's first half reduced
             prev0[0] = h0[0];
             prev0[1] = h0[1];
         }
         if (KFP8) pend_scale = sm.scale[cur][KT - 64 + lane];
-        if (tile + 1 < ntiles) {
+        if (it + 1 < ntiles) {
             if constexpr (QFP8) store_tile_raw(sm, cur ^ 1, tr, tsc, tid);
             else store_tile<KFP8>(sm, cur ^ 1, tr, tsc, tid);
         }
         __syncthreads();
     }
-    {  // the last pair's second half
+    if (ntiles > 0) {  // the last pair's second half
         float h1[2];
         const f32x4 (&r)[2][4] = acc[1];
 #pragma unroll
@@ -523,7 +640,14 @@ __global__ __launch_bounds__(THREADS, 1) void mfma_indexer_kernel(
                 for (int i = 0; i < 4; ++i) s4[i] = fmaf(wv[m][i], relu(r[n][m][i]), s4[i]);
             h1[n] = (s4[0] + s4[1]) + (s4[2] + s4[3]);
         }
-        finish_pair(prev0, h1, (long long)ntiles * KT - 64, pend_scale);
+        finish_pair(prev0, h1, (long long)thi * KT - 64, pend_scale);
+    }
+
+    if constexpr (SPLITK) {
+        if (nparts > 1) {
+            parts_finish(sm, cs, ci, cnt, topk, tok_ok, q0, tok, t0, part, nparts, pp_ws, idx, vals);
+            return;
+        }
     }
 
     if (!SCORE && tok_ok) {
@@ -585,21 +709,103 @@ hipError_t launch_mfma_select_qfp8(const Problem &p, const void *Q8, const float
 
 long long mfma_varlen_blocks(int B, int total_q) { return ((long long)total_q + TQ - 1) / TQ + B; }
 
+namespace {
+
+std::atomic<int> g_prefill_split{-2};  // -2: not read from the environment yet
+
+int prefill_split_now()
+{
+    int v = g_prefill_split.load(std::memory_order_relaxed);
+    if (v != -2) return v;
+    int init = 0;
+    if (const char *e = std::getenv("DS4IDX_PREFILL_SPLIT")) {
+        const int x = std::atoi(e);
+        init = x < 0 ? -1 : x;
+    }
+    int expected = -2;
+    g_prefill_split.compare_exchange_strong(expected, init);
+    return g_prefill_split.load(std::memory_order_relaxed);
+}
+
+constexpr int kPrefillPartKeys = 8192;  // automatic part length
+
+size_t align256(size_t n) { return (n + 255) / 256 * 256; }
+
+}  // namespace
+
+int set_prefill_split(int keys)
+{
+    const int prev = prefill_split_now();
+    g_prefill_split.store(keys < 0 ? -1 : keys, std::memory_order_relaxed);
+    return prev;
+}
+
+int get_prefill_split() { return prefill_split_now(); }
+
+// A small ragged prefill batch whose longest rows set the pace: 8-token
+// blocks over long caches are split into key parts of 8192 (at most
+// kPrefillMaxParts, so longer caches get longer parts). Batches with more
+// blocks than two rounds of the 256 CUs balance well without parts.
+int prefill_kpart(const VarlenProblem &p)
+{
+    const int o = prefill_split_now();
+    if (o < 0 || p.total_q == 0) return 0;
+    const long long per4 = ((long long)p.max_k + kPrefillMaxParts - 1) / kPrefillMaxParts;
+    long long kp;
+    if (o > 0) {
+        kp = o > per4 ? o : per4;
+    } else {
+        if (p.max_k <= kPrefillPartKeys || mfma_varlen_blocks(p.B, p.total_q) > 2 * kSplitCUs) return 0;
+        kp = kPrefillPartKeys > per4 ? kPrefillPartKeys : per4;
+    }
+    kp = (kp + KT - 1) / KT * KT;
+    if (kp >= p.max_k) return 0;  // one part
+    return kp > 0x7fffffffLL ? 0 : (int)kp;
+}
+
+size_t prefill_parts_workspace_bytes(const VarlenProblem &p, int k)
+{
+    if (prefill_kpart(p) == 0) return 0;
+    const size_t rows = (size_t)p.total_q;
+    return align256(rows * 4) + align256(rows * kPrefillMaxParts * 4) + align256(rows * kPrefillMaxParts * (size_t)k * 8);
+}
+
 hipError_t launch_mfma_select_varlen(const VarlenProblem &p, const int *cu_q, const long long *cu_k,
                                      const void *Q, const void *K, const float *Ks, const float *W,
-                                     int k, int *idx, float *vals, hipStream_t st)
+                                     int k, int *idx, float *vals, void *ws, hipStream_t st)
 {
-    // Every stream's blocks fit in ceil(total_q / 8) + B.
-    const dim3 grid((unsigned)mfma_varlen_blocks(p.B, p.total_q));
     const Ragged rg{cu_q, cu_k, p.B, p.total_q, p.total_k};
     const uint16_t *q = static_cast<const uint16_t *>(Q);
     const uint8_t *kk = static_cast<const uint8_t *>(K);
+    const int kpart = prefill_kpart(p);
+    if (kpart > 0) {
+        // Every stream's blocks fit in (ceil(total_q / 8) + B) x parts.
+        const dim3 grid((unsigned)(mfma_varlen_blocks(p.B, p.total_q) * kPrefillMaxParts));
+        const size_t rows = (size_t)p.total_q;
+        char *c = static_cast<char *>(ws);
+        PrefillParts pw;
+        pw.kpart = kpart;
+        pw.ctr = reinterpret_cast<uint32_t *>(c);
+        c += align256(rows * 4);
+        pw.cnt = reinterpret_cast<uint32_t *>(c);
+        c += align256(rows * kPrefillMaxParts * 4);
+        pw.list = reinterpret_cast<uint64_t *>(c);
+        if (p.k_dtype == FP8)
+            hipLaunchKernelGGL((mfma_indexer_kernel<true, false, true, false, true>), grid, dim3(THREADS), 0, st, q, kk,
+                               Ks, W, 0, 0, 0LL, k, idx, vals, nullptr, nullptr, rg, pw);
+        else
+            hipLaunchKernelGGL((mfma_indexer_kernel<false, false, true, false, true>), grid, dim3(THREADS), 0, st, q,
+                               kk, Ks, W, 0, 0, 0LL, k, idx, vals, nullptr, nullptr, rg, pw);
+        return hipGetLastError();
+    }
+    // Every stream's blocks fit in ceil(total_q / 8) + B.
+    const dim3 grid((unsigned)mfma_varlen_blocks(p.B, p.total_q));
     if (p.k_dtype == FP8)
         hipLaunchKernelGGL((mfma_indexer_kernel<true, false, true, false>), grid, dim3(THREADS), 0, st, q, kk, Ks, W, 0,
-                           0, 0LL, k, idx, vals, nullptr, nullptr, rg);
+                           0, 0LL, k, idx, vals, nullptr, nullptr, rg, PrefillParts{});
     else
         hipLaunchKernelGGL((mfma_indexer_kernel<false, false, true, false>), grid, dim3(THREADS), 0, st, q, kk, Ks, W,
-                           0, 0, 0LL, k, idx, vals, nullptr, nullptr, rg);
+                           0, 0, 0LL, k, idx, vals, nullptr, nullptr, rg, PrefillParts{});
     return hipGetLastError();
 }
 

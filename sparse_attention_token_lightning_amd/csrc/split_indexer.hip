@@ -110,18 +110,6 @@ struct SplitSmem {
     int last;
 };
 
-template <class V>
-__device__ __forceinline__ void store_agent(V *p, V v)
-{
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-template <class V>
-__device__ __forceinline__ V load_agent(const V *p)
-{
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 // A candidate slot: order key in the low word (0 = empty), key index in the high word.
 __device__ __forceinline__ uint64_t slot(uint32_t key, long long index)
 {

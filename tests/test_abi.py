@@ -359,3 +359,32 @@ def test_noalloc_scratch_size_matches_header():
     text = open(HEADER).read()
     m = re.search(r"#define DS4IDX_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
     assert m and int(m.group(1)) << int(m.group(2)) == ds.NOALLOC_SCRATCH_BYTES
+
+
+def test_prefill_split_switch_and_workspace():
+    # The 2048-token ragged prefill budget (1024/512/256/256 new tokens on
+    # caches of 32768/16384/8192/8192 keys): the prefill kernel with key parts
+    # of 8192 by default, which need workspace; none with parts off.
+    tq, sk = [1024, 512, 256, 256], [32768, 16384, 8192, 8192]
+    v = _vprob(B=4, total_q=sum(tq), total_k=sum(sk), max_k=max(sk))
+    prev = ds.set_prefill_split(0)
+    try:
+        assert ds.get_prefill_split() == 0
+        auto = ds.varlen_workspace_bytes(v, 512)
+        assert auto >= 2048 * 4 * 512 * 8  # counters, counts and 4 lists of k entries per row
+        assert _vselect(v) == ds.ERR_WORKSPACE  # parts need a workspace; refused before any HIP call
+        ds.set_prefill_split(-1)
+        assert ds.get_prefill_split() == -1 and ds.varlen_workspace_bytes(v, 512) == 0
+        ds.set_prefill_split(5000)
+        assert ds.varlen_workspace_bytes(v, 512) == auto  # same layout: always 4 part slots per row
+        # short caches: a single part, no workspace
+        short = _vprob(B=4, total_q=2048, total_k=4 * 4096, max_k=4096)
+        ds.set_prefill_split(0)
+        assert ds.varlen_workspace_bytes(short, 512) == 0
+        # a large batch balances without parts
+        big = _vprob(B=2, total_q=8192, total_k=2 * 65536, max_k=65536)
+        assert ds.varlen_workspace_bytes(big, 512) == 0
+        ds.set_prefill_split(4096)
+        assert ds.varlen_workspace_bytes(big, 512) > 0
+    finally:
+        ds.set_prefill_split(prev)

@@ -46,9 +46,15 @@ def run_varlen(rg: W.Ragged, topk=None, dev=None, workspace=None, poison=True):
 
 
 def _route_is_split(rg, topk):
+    # with the prefill kernel's key parts off, only the split-key kernel needs
+    # a workspace
     q, k, _, _, cq, ck = _dev(rg)
     p = ds.make_varlen_problem(q, k, cq, ck, _max_k(rg))
-    return ds.varlen_workspace_bytes(p, topk) > 0
+    prev = ds.set_prefill_split(-1)
+    try:
+        return ds.varlen_workspace_bytes(p, topk) > 0
+    finally:
+        ds.set_prefill_split(prev)
 
 
 def _rows_for_oracle(T, n=16):
@@ -219,3 +225,33 @@ def test_ragged_partition_lengths_identical(keys):
             assert np.array_equal(gv.view(np.uint32), av.view(np.uint32)), f"{name}: values differ"
     finally:
         ds.set_split(prev)
+
+
+PARTS_MIX = [(300, 8000), (40, 3000), (1, 7999), (64, 64), (9, 6001)]
+
+
+@pytest.mark.parametrize("keys", [0, 2048, 5000])
+def test_ragged_prefill_key_parts_identical(keys):
+    # Splitting an 8-token block's keys into parts changes neither the
+    # scores nor the exact selection: the parted launch returns the unsplit
+    # launch's indices and values bit for bit, and matches the oracle
+    # (exactly on integer inputs). With 2048-key parts the 8000-key stream
+    # takes 4 parts, the 3000-key one 2, the 64-key one 1.
+    prev = ds.get_prefill_split()
+    try:
+        cases = [("bench prefill mix", BENCH_PREFILL_MIX, 48, "fp8"), ("parts mix", PARTS_MIX, 49, "fp8"),
+                 ("parts mix int", PARTS_MIX, 50, "int"), ("parts mix bf16", PARTS_MIX, 51, "bf16")]
+        for name, mix, seed, kind in cases:
+            rg = W.ragged(seed, mix, kind=kind)
+            dev = _dev(rg)
+            _say(f"ragged prefill key parts {keys}: {name} ({kind})")
+            ds.set_prefill_split(-1)
+            ri, rv = run_varlen(rg, dev=dev)
+            ds.set_prefill_split(keys)
+            gi, gv = run_varlen(rg, dev=dev)
+            assert np.array_equal(gi, ri), f"{name}: indices differ with key parts"
+            assert np.array_equal(gv.view(np.uint32), rv.view(np.uint32)), f"{name}: values differ with key parts"
+            if name != "bench prefill mix" or keys == 0:
+                check_against_oracle(rg, gi, gv, exact=(kind == "int"), n=8)
+    finally:
+        ds.set_prefill_split(prev)
