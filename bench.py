@@ -84,15 +84,45 @@ PROFILES = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles")
 CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "sparse_attention_token_lightning_amd", "csrc")
 
 
+def _code_only(text: str) -> str:
+    """C++ source with comments removed and whitespace runs collapsed, so an
+    edit to comments or layout alone leaves the digest unchanged."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":                                   # string or char literal, kept whole
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i) or text.startswith("/*", i) or c.isspace():
+            if text.startswith("//", i):
+                j = text.find("\n", i)
+                i = n if j < 0 else j
+            elif text.startswith("/*", i):
+                j = text.find("*/", i + 2)
+                i = n if j < 0 else j + 2
+            else:
+                i += 1
+            if out and out[-1] != " ":                   # one space per gap outside literals
+                out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return "".join(out).strip()
+
+
 def kernel_digest(src: str) -> str:
     import hashlib
-    with open(os.path.join(CSRC, src), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    with open(os.path.join(CSRC, src), encoding="utf-8") as f:
+        return hashlib.sha256(_code_only(f.read()).encode()).hexdigest()[:16]
 
 
 def measured_traffic(summary: str = "mfma_select_64k_traffic.txt", src: str = "mfma_indexer.hip"):
     """HBM bytes per launch from a committed counter summary, or None when the
-    kernel source changed since the counters were taken."""
+    kernel's code (comments and layout aside) changed since the counters were
+    taken."""
     path = os.path.join(PROFILES, summary)
     if not os.path.exists(path):
         return None
@@ -101,7 +131,7 @@ def measured_traffic(summary: str = "mfma_select_64k_traffic.txt", src: str = "m
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("kernel_source_sha256_16") != kernel_digest(src):
+    if kv.get("kernel_code_sha256_16") != kernel_digest(src):
         return None
     try:
         return int(float(kv["hbm_bytes_per_launch"]))

@@ -458,11 +458,12 @@ __global__ __launch_bounds__(THREADS, 1) void split_indexer_kernel(
     constexpr int NSUB = PART / (NW * 32);  // 32-key sub-blocks per wavefront
     const long long pbase = (long long)p * PART;
 
-    // This wavefront's keys: the partition is read in 32 rounds of 256
-    // consecutive keys, the eight wavefronts taking 32 keys each, and a full
-    // partition starts its rounds at round p (mod 32). At any moment the
-    // blocks of a row then read different offsets of their 1 MB, instead of
-    // all reading at multiples of 1 MB apart: a read-only probe of this
+    // This wavefront's keys: the partition is read in PART / 256 rounds of
+    // 256 consecutive keys, the eight wavefronts taking 32 keys each, and a
+    // full partition starts its rounds at round p (mod PART / 256). At any
+    // moment the blocks of a row then read different offsets of their
+    // partitions, instead of all reading at multiples of the partition's
+    // bytes apart: a read-only probe of this
     // geometry measured 48.4 against 53.2 us for the 8 x 262144-key decode
     // (and a wavefront owning 128 KB of its partition was as slow as the
     // latter). Sub-block sb of the wavefront covers keys

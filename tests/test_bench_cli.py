@@ -22,7 +22,7 @@ def test_more_than_one_gpu_is_refused():
 def _summary(path, digest, hbm):
     with open(path, "w") as f:
         f.write("# comment: a line with a colon is not a field\n")
-        f.write(f"kernel_source_sha256_16: {digest}\n")
+        f.write(f"kernel_code_sha256_16: {digest}\n")
         f.write("launches: 16\n")
         f.write(f"hbm_bytes_per_launch: {hbm}\n")
 
@@ -50,6 +50,16 @@ def test_committed_traffic_summaries_parse(summary):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    assert len(kv["kernel_source_sha256_16"]) == 16
+    assert len(kv["kernel_code_sha256_16"]) == 16
     fetch, write = int(kv["fetch_bytes_per_launch"]), int(kv["write_bytes_per_launch"])
     assert int(kv["hbm_bytes_per_launch"]) == fetch + write > 0
+
+
+def test_digest_ignores_comments_and_layout_only():
+    src = 'int f(int x) {  // doubles\n  return 2 * x; /* no\noverflow */ }\nconst char *s = "a // b";\n'
+    same = 'int f(int x) { return 2 * x; }\n// a new comment\nconst char *s = "a // b";'
+    changed = 'int f(int x) { return 3 * x; }\nconst char *s = "a // b";'
+    literal = 'int f(int x) { return 2 * x; }\nconst char *s = "a  // b";'
+    assert bench._code_only(src) == bench._code_only(same)
+    assert bench._code_only(src) != bench._code_only(changed)
+    assert bench._code_only(src) != bench._code_only(literal)   # inside a literal, text counts
