@@ -64,13 +64,14 @@ struct AttnSmem {
     int sel[kAttnMaxK];             // the token's rows, -1 where the entry is not valid
     uint16_t p[4][64][8];           // P^T B fragments per head tile and lane
     float pmax[2][AH];              // chunk maxima per key tile and head
-    float psum[2][AH];
+    float psum[2][AH];              // final sums per key tile and head
+    alignas(8) uint8_t jump[8];     // per wavefront: a head's max rose by more than 2^RESCALE_LOG2
 };
 
-// Key s of a chunk, in the order shared by the score tiles and the value
-// fragments: lane group g of a score tile holds keys 4g..4g+3 of each 16-key
-// tile, and a value fragment of group g takes those 8 keys.
-__device__ __forceinline__ int perm_key(int g, int e) { return e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4); }
+// The chunk's keys in the order shared by the score tiles and the value
+// fragments: lane group g (lanes 16g..16g+15) of a score tile holds keys
+// 4g..4g+3 of each 16-key tile, so element e of its value-fragment operand is
+// key 4g + e for e < 4 and key 16 + 4g + (e - 4) otherwise.
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
@@ -189,12 +190,10 @@ __global__ __launch_bounds__(ATHREADS, 1) void sparse_attention_kernel(
     for (int a = 0; a < 4; ++a)
 #pragma unroll
         for (int j = 0; j < 4; ++j) o[a][j] = f32x4{};
-    float m_run[4], l_run[4];  // heads 16 a + lane % 16 of the tile, log2 domain
+    float m_run[4];  // running max of heads 16 a + lane % 16, log2 domain
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-        m_run[a] = -INFINITY;
-        l_run[a] = 0.0f;
-    }
+    for (int a = 0; a < 4; ++a) m_run[a] = -INFINITY;
+    float l_part = 0.0f;  // sum of P over this wavefront's keys (tile kt), head 16 ht + lane % 16
 
     for (int c = 0; c < NBUF - 1 && c < nchunk; ++c) issue(c);
     for (int c = 0; c < nchunk; ++c) {
@@ -239,58 +238,81 @@ __global__ __launch_bounds__(ATHREADS, 1) void sparse_attention_kernel(
         }
         mx = quad_max(mx);
         if (lane < 16) sm.pmax[kt][ht * 16 + lane] = mx;
-        __syncthreads();
 
         // Lazy rescaling: a head keeps its running max until a chunk's max
         // exceeds it by more than RESCALE_LOG2, so the probabilities stay
         // below 2^RESCALE_LOG2 (exact in fp32; bf16 keeps its relative
-        // precision) and O is rescaled only when some head's max jumps,
-        // in practice after the first chunk only.
-        float m_new[4], m_use[4], alpha[4];
-        bool moved = false;
+        // precision) and O is rescaled only when some head's max jumps, in
+        // practice after the first chunk only. So P is first formed against
+        // the running max, which every wavefront holds alike, with no
+        // exchange; a wavefront that sees one of its heads jump raises a
+        // flag, and only then do all wavefronts exchange the chunk maxima,
+        // form P again and rescale.
+        float m_ht = m_run[0];
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
-            const int hh = a * 16 + (lane & 15);
-            const float cm = fmaxf(sm.pmax[0][hh], sm.pmax[1][hh]);
-            const bool up = cm > m_run[a] + RESCALE_LOG2;  // always, from -inf, once a key is valid
-            m_new[a] = up ? cm : m_run[a];
-            m_use[a] = m_new[a] == -INFINITY ? 0.0f : m_new[a];
-            alpha[a] = up ? exp2_fast(m_run[a] - m_use[a]) : 1.0f;
-            moved = moved || up;
-        }
+        for (int a = 1; a < 4; ++a) m_ht = ht == a ? m_run[a] : m_ht;
+        if (lane == 0) sm.jump[wid] = wave_ballot(mx > m_ht + RESCALE_LOG2) != 0 ? 1 : 0;
         float pr[4], ps = 0.0f;
+        {
+            const float mu = m_ht == -INFINITY ? 0.0f : m_ht;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            pr[i] = exp2_fast(z[i] - m_use[ht]);
-            ps += pr[i];
+            for (int i = 0; i < 4; ++i) {
+                pr[i] = exp2_fast(z[i] - mu);
+                ps += pr[i];
+            }
         }
-        ps = quad_sum(ps);
-        if (lane < 16) sm.psum[kt][ht * 16 + lane] = ps;
         *reinterpret_cast<uint2 *>(&sm.p[ht][lane][kt * 4]) =
             make_uint2(pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]));
         __syncthreads();
 
+        if (*reinterpret_cast<const uint64_t *>(sm.jump) != 0) {  // the same answer in every wavefront
+            float m_new[4], m_use[4], alpha[4];
+            bool moved = false;
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
-            const int hh = a * 16 + (lane & 15);
-            l_run[a] = l_run[a] * alpha[a] + (sm.psum[0][hh] + sm.psum[1][hh]);
-            m_run[a] = m_new[a];
+            for (int a = 0; a < 4; ++a) {
+                const int hh = a * 16 + (lane & 15);
+                const float cm = fmaxf(sm.pmax[0][hh], sm.pmax[1][hh]);
+                const bool up = cm > m_run[a] + RESCALE_LOG2;  // always, from -inf, once a key is valid
+                m_new[a] = up ? cm : m_run[a];
+                m_use[a] = m_new[a] == -INFINITY ? 0.0f : m_new[a];
+                alpha[a] = up ? exp2_fast(m_run[a] - m_use[a]) : 1.0f;
+                moved = moved || up;
+            }
+            float mu = m_use[0], al = alpha[0];
+#pragma unroll
+            for (int a = 1; a < 4; ++a) {
+                mu = ht == a ? m_use[a] : mu;
+                al = ht == a ? alpha[a] : al;
+            }
+            ps = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                pr[i] = exp2_fast(z[i] - mu);
+                ps += pr[i];
+            }
+            l_part *= al;
+            *reinterpret_cast<uint2 *>(&sm.p[ht][lane][kt * 4]) =
+                make_uint2(pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]));
+#pragma unroll
+            for (int a = 0; a < 4; ++a) m_run[a] = m_new[a];
+            if (wave_ballot(moved)) {  // a head's running max rose: rescale
+#pragma unroll
+                for (int a = 0; a < 4; ++a)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) o[a][j][i] *= alpha[a];
+            }
+            __syncthreads();  // P formed again; maxima and flags read
         }
-        if (wave_ballot(moved)) {  // a head's running max rose: rescale
-#pragma unroll
-            for (int a = 0; a < 4; ++a)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) o[a][j][i] *= alpha[a];
-        }
+        l_part += quad_sum(ps);
         // One value fragment at a time (its 8 keys read from the raw rows);
         // the four P fragments are read once per chunk and kept in registers
         // (reading them for each value tile was 96 KB of LDS reads per chunk
         // more: 605 -> 585 us). Nothing spills, so no vector-memory
         // instruction but the gathers runs in this loop.
         const int ln = lane, g = lane >> 4, i16 = lane & 15;
-        const int kr0 = 4 * g + (i16 >> 2), kr1 = kr0 + 16;  // the two key runs of perm_key(g, .)
+        const int kr0 = 4 * g + (i16 >> 2), kr1 = kr0 + 16;  // the two key runs of lane group g
         bf16x8 pf[4];  // the chunk's P fragments, read once for the four value tiles
 #pragma unroll
         for (int a = 0; a < 4; ++a) pf[a] = *reinterpret_cast<const bf16x8 *>(&sm.p[a][ln][0]);
@@ -315,6 +337,13 @@ __global__ __launch_bounds__(ATHREADS, 1) void sparse_attention_kernel(
             __builtin_amdgcn_sched_barrier(0);
         }
     }
+
+    // The two key tiles' sums of each head, added once.
+    if (lane < 16) sm.psum[kt][ht * 16 + lane] = l_part;
+    __syncthreads();
+    float l_run[4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) l_run[a] = sm.psum[0][a * 16 + (lane & 15)] + sm.psum[1][a * 16 + (lane & 15)];
 
     // O^T tile (value tile 4 wid + j, head tile a): lane holds head 16 a +
     // lane % 16 and value dims 16 (4 wid + j) + 4 (lane / 16) .. +3.
