@@ -53,6 +53,7 @@ constexpr int NQK = DQK / 32;      // k-steps of the score contraction
 constexpr float RESCALE_LOG2 = 8.0f;  // largest log2 probability before O is rescaled
 
 static_assert(MAIN16 == 64 && TAIL16 == 8, "one wavefront instruction per row head, per 8 row tails");
+static_assert(kAttnMaxK / CK <= 64, "one chunk per lane in the row-index registers");
 
 typedef __attribute__((__vector_size__(8 * sizeof(short)))) short bf16x8;
 typedef short v4s __attribute__((ext_vector_type(4)));
@@ -61,11 +62,10 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 struct AttnSmem {
     uint4 head[NBUF][CK * MAIN16];  // row r, piece p at [r * 64 + (p ^ (r & 15))]
     uint4 tail[NBUF][CK * TAIL16];  // row r, piece q at [r * 8 + (q ^ (r & 7))]
-    int sel[kAttnMaxK];             // the token's rows, -1 where the entry is not valid
-    uint16_t p[4][64][8];           // P^T B fragments per head tile and lane
-    float pmax[2][AH];              // chunk maxima per key tile and head
-    float psum[2][AH];              // final sums per key tile and head
-    alignas(8) uint8_t jump[8];     // per wavefront: a head's max rose by more than 2^RESCALE_LOG2
+    uint16_t p[2][4][64][8];        // P^T B fragments per head tile and lane, chunk parity
+    float pmax[2][AH];              // chunk maxima per key tile and head; at the end, the sums
+    uint8_t validb[kAttnMaxK / CK][8];  // chunk c, byte w, bit j: row 4w + j is valid
+    alignas(8) uint8_t jump[2][8];  // per chunk parity and wavefront: a head's max rose by more than 2^RESCALE_LOG2
 };
 
 // The chunk's keys in the order shared by the score tiles and the value
@@ -144,11 +144,16 @@ __global__ __launch_bounds__(ATHREADS, 1) void sparse_attention_kernel(
     const int kt = wid & 1, ht = wid >> 1;
     const int nchunk = (topk + CK - 1) / CK;
 
-    // The selected rows, validated once.
-    for (int j = tid; j < nchunk * CK; j += ATHREADS) {
-        const int e = j < topk ? ir[j] : -1;
-        sm.sel[j] = (e >= 0 && e < S) ? e : -1;
-    }
+    // The rows this wavefront gathers, in registers: lane l holds those of
+    // chunk l, the heads of rows 4w + j in hsel[j] and (wavefronts 0..3) the
+    // tails of rows 8w + j in tsel[j]. Every load is issued, at a clamped
+    // entry, so that they fly together with the Q loads below.
+    int hsel[4], tsel[8];
+    const int last = topk - 1;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) hsel[j] = ir[min(lane * CK + 4 * wid + j, last)];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) tsel[j] = ir[min(lane * CK + 8 * (wid & 3) + j, last)];
     // Q^T fragments of head tile ht: head h0 + 16 ht + lane % 16, dims 32 ks + 8 (lane / 16) ..
     bf16x8 qf[NQK];
     {
@@ -157,30 +162,56 @@ __global__ __launch_bounds__(ATHREADS, 1) void sparse_attention_kernel(
 #pragma unroll
         for (int ks = 0; ks < NQK; ++ks) qf[ks] = qp[ks * 4];
     }
-    // Finish the Q loads here, so that no wait for them is left to the main
+    // Finish these loads here, so that no wait for them is left to the main
     // loop (where vmcnt counts only the gathers).
     wait_vm<0>();
 #pragma unroll
     for (int ks = 0; ks < NQK; ++ks) asm volatile("" : "+v"(qf[ks]));
-    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 4; ++j) asm volatile("" : "+v"(hsel[j]));
+#pragma unroll
+    for (int j = 0; j < 8; ++j) asm volatile("" : "+v"(tsel[j]));
+    // An entry is valid if it lies within topk and 0 <= idx < S. Validity
+    // bits for the score mask: byte w of chunk c, bit j = row 4w + j. A row
+    // that is not valid is gathered from row 0 (its score is masked), so
+    // every gathered value is finite.
+    {
+        uint32_t vbits = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const bool ok = lane * CK + 4 * wid + j <= last && hsel[j] >= 0 && hsel[j] < S;
+            vbits |= (ok ? 1u : 0u) << j;
+            hsel[j] = ok ? hsel[j] : 0;
+        }
+        if (lane < nchunk) sm.validb[lane][wid] = (uint8_t)vbits;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const bool ok = lane * CK + 8 * (wid & 3) + j <= last && tsel[j] >= 0 && tsel[j] < S;
+            tsel[j] = ok ? tsel[j] : 0;
+        }
+    }
 
     // Gather of chunk c into buffer c % NBUF: wavefront w loads the heads of
     // rows 4w..4w+3 (lane i takes piece i ^ (r & 15) of row r into slot i),
-    // wavefronts 0..3 also the tails of rows 8w..8w+7. Invalid entries load
-    // row 0, so every value read is finite; their scores are masked.
+    // wavefronts 0..3 also the tails of rows 8w..8w+7.
     auto issue = [&](int c) {
         const int b = c % NBUF;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int r = 4 * wid + j;
-            const int e = sm.sel[c * CK + r];
-            const char *src = Cb + (long long)(e < 0 ? 0 : e) * (DQK * 2) + ((lane ^ (r & 15)) * 16);
+            const int e = __builtin_amdgcn_readlane(hsel[j], c);
+            const char *src = Cb + (long long)e * (DQK * 2) + ((lane ^ (r & 15)) * 16);
             gather16(src, __builtin_amdgcn_readfirstlane(lds_addr(&sm.head[b][r * MAIN16])));
         }
         if (wid < 4) {
             const int r = 8 * wid + (lane >> 3);
-            const int e = sm.sel[c * CK + r];
-            const char *src = Cb + (long long)(e < 0 ? 0 : e) * (DQK * 2) + DV * 2 + (((lane & 7) ^ (r & 7)) * 16);
+            int e = __builtin_amdgcn_readlane(tsel[0], c);
+#pragma unroll
+            for (int j = 1; j < 8; ++j) {
+                const int ej = __builtin_amdgcn_readlane(tsel[j], c);
+                e = (lane >> 3) == j ? ej : e;
+            }
+            const char *src = Cb + (long long)e * (DQK * 2) + DV * 2 + (((lane & 7) ^ (r & 7)) * 16);
             gather16(src, __builtin_amdgcn_readfirstlane(lds_addr(&sm.tail[b][wid * 64])));
         }
     };
@@ -195,22 +226,25 @@ __global__ __launch_bounds__(ATHREADS, 1) void sparse_attention_kernel(
     for (int a = 0; a < 4; ++a) m_run[a] = -INFINITY;
     float l_part = 0.0f;  // sum of P over this wavefront's keys (tile kt), head 16 ht + lane % 16
 
+    // One barrier per chunk. Before the barrier of chunk c each wavefront
+    // has written its share of P(c) and waited for its own gathers of chunk
+    // c + 1; after it, chunk c + 1 is visible to all, every wavefront is past
+    // the values of chunk c - 1, so chunk c + 3 is gathered into that
+    // chunk's buffer. P and the flags alternate between two buffers, so a
+    // wavefront writing those of chunk c + 1 cannot overwrite what a slower
+    // one still reads of chunk c. Waits count gathers: 5 per chunk in
+    // wavefronts 0..3, 4 in the others.
     for (int c = 0; c < NBUF - 1 && c < nchunk; ++c) issue(c);
+    if (nchunk >= 3) {
+        if (wid < 4) wait_vm<10>(); else wait_vm<8>();
+    } else if (nchunk == 2) {
+        if (wid < 4) wait_vm<5>(); else wait_vm<4>();
+    } else {
+        wait_vm<0>();
+    }
+    __syncthreads();  // chunk 0 and the validity bits visible
     for (int c = 0; c < nchunk; ++c) {
-        const int b = c % NBUF;
-        // this wavefront's gathers of chunk c are done once at most those of
-        // the chunks issued after it remain (4 or 5 per chunk)
-        const int ahead = (c + NBUF - 2 < nchunk - 1 ? c + NBUF - 2 : nchunk - 1) - c;
-        if (ahead >= 2) {
-            if (wid < 4) wait_vm<10>(); else wait_vm<8>();
-        } else if (ahead == 1) {
-            if (wid < 4) wait_vm<5>(); else wait_vm<4>();
-        } else {
-            wait_vm<0>();
-        }
-        __syncthreads();  // chunk c visible; every wavefront is past chunk c - 1
-        if (c + NBUF - 1 < nchunk) issue(c + NBUF - 1);
-
+        const int b = c % NBUF, pb = c & 1;
         // scores of key tile kt x head tile ht
         f32x4 s = f32x4{};
         {
@@ -229,11 +263,11 @@ __global__ __launch_bounds__(ATHREADS, 1) void sparse_attention_kernel(
             }
         }
         __builtin_amdgcn_s_setprio(0);
+        const uint32_t vb = sm.validb[c][4 * kt + (lane >> 4)];  // keys kt * 16 + 4 (lane / 16) + i
         float z[4], mx = -INFINITY;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int key = kt * 16 + 4 * (lane >> 4) + i;
-            z[i] = sm.sel[c * CK + key] >= 0 ? s[i] * scale_log2 : -INFINITY;
+            z[i] = (vb >> i) & 1u ? s[i] * scale_log2 : -INFINITY;
             mx = fmaxf(mx, z[i]);
         }
         mx = quad_max(mx);
@@ -251,7 +285,7 @@ __global__ __launch_bounds__(ATHREADS, 1) void sparse_attention_kernel(
         float m_ht = m_run[0];
 #pragma unroll
         for (int a = 1; a < 4; ++a) m_ht = ht == a ? m_run[a] : m_ht;
-        if (lane == 0) sm.jump[wid] = wave_ballot(mx > m_ht + RESCALE_LOG2) != 0 ? 1 : 0;
+        if (lane == 0) sm.jump[pb][wid] = wave_ballot(mx > m_ht + RESCALE_LOG2) != 0 ? 1 : 0;
         float pr[4], ps = 0.0f;
         {
             const float mu = m_ht == -INFINITY ? 0.0f : m_ht;
@@ -261,11 +295,17 @@ __global__ __launch_bounds__(ATHREADS, 1) void sparse_attention_kernel(
                 ps += pr[i];
             }
         }
-        *reinterpret_cast<uint2 *>(&sm.p[ht][lane][kt * 4]) =
+        *reinterpret_cast<uint2 *>(&sm.p[pb][ht][lane][kt * 4]) =
             make_uint2(pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]));
+        if (c + 2 < nchunk) {
+            if (wid < 4) wait_vm<5>(); else wait_vm<4>();
+        } else {
+            wait_vm<0>();
+        }
         __syncthreads();
+        if (c + NBUF - 1 < nchunk) issue(c + NBUF - 1);
 
-        if (*reinterpret_cast<const uint64_t *>(sm.jump) != 0) {  // the same answer in every wavefront
+        if (*reinterpret_cast<const uint64_t *>(sm.jump[pb]) != 0) {  // the same answer in every wavefront
             float m_new[4], m_use[4], alpha[4];
             bool moved = false;
 #pragma unroll
@@ -291,7 +331,7 @@ __global__ __launch_bounds__(ATHREADS, 1) void sparse_attention_kernel(
                 ps += pr[i];
             }
             l_part *= al;
-            *reinterpret_cast<uint2 *>(&sm.p[ht][lane][kt * 4]) =
+            *reinterpret_cast<uint2 *>(&sm.p[pb][ht][lane][kt * 4]) =
                 make_uint2(pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]));
 #pragma unroll
             for (int a = 0; a < 4; ++a) m_run[a] = m_new[a];
@@ -315,7 +355,7 @@ __global__ __launch_bounds__(ATHREADS, 1) void sparse_attention_kernel(
         const int kr0 = 4 * g + (i16 >> 2), kr1 = kr0 + 16;  // the two key runs of lane group g
         bf16x8 pf[4];  // the chunk's P fragments, read once for the four value tiles
 #pragma unroll
-        for (int a = 0; a < 4; ++a) pf[a] = *reinterpret_cast<const bf16x8 *>(&sm.p[a][ln][0]);
+        for (int a = 0; a < 4; ++a) pf[a] = *reinterpret_cast<const bf16x8 *>(&sm.p[pb][a][ln][0]);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             // Transposed LDS reads: lane 4q + c of a 16-lane group points at
@@ -338,12 +378,14 @@ __global__ __launch_bounds__(ATHREADS, 1) void sparse_attention_kernel(
         }
     }
 
-    // The two key tiles' sums of each head, added once.
-    if (lane < 16) sm.psum[kt][ht * 16 + lane] = l_part;
+    // The two key tiles' sums of each head, added once. (The maxima are read
+    // only between a chunk's barrier and the barrier that ends its rescale,
+    // so their array is free here.)
+    if (lane < 16) sm.pmax[kt][ht * 16 + lane] = l_part;
     __syncthreads();
     float l_run[4];
 #pragma unroll
-    for (int a = 0; a < 4; ++a) l_run[a] = sm.psum[0][a * 16 + (lane & 15)] + sm.psum[1][a * 16 + (lane & 15)];
+    for (int a = 0; a < 4; ++a) l_run[a] = sm.pmax[0][a * 16 + (lane & 15)] + sm.pmax[1][a * 16 + (lane & 15)];
 
     // O^T tile (value tile 4 wid + j, head tile a): lane holds head 16 a +
     // lane % 16 and value dims 16 (4 wid + j) + 4 (lane / 16) .. +3.
