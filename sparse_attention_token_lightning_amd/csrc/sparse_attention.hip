@@ -11,31 +11,37 @@
 //
 // over the valid entries of idx[t] (0 <= idx < S), plus lse[t,h].
 //
-// Layout on CDNA4. A 512-thread workgroup owns one query token and one tile of
-// 64 heads; the selected rows stream through LDS in chunks of 32:
+// Layout on CDNA4. The work items are (query token, tile of 64 heads); one
+// 512-thread workgroup per CU takes a contiguous run of them, and each item's
+// selected rows stream through LDS in chunks of 32:
 //  * Gather. The rows of a chunk go straight from global memory into LDS
-//    (global_load_lds_dwordx4: each wavefront instruction moves 64 x 16 bytes,
-//    one 1 KB row head or the 128-byte tails of 8 rows), into a ring of four
-//    chunk buffers, three chunks ahead of the one being computed, so a CU
-//    keeps ~110 KB of gathers in flight without holding them in registers.
-//    The 16-byte pieces of a row are XOR-swizzled by the row number so the
-//    MFMA fragment reads below are bank-conflict free.
+//    (global_load_lds_dwordx4: each wavefront instruction moves 64 x 16 bytes
+//    of one 1 KB row head, or in 32 lanes the 128-byte tails of 4 rows), into
+//    a ring of four chunk buffers, two to three chunks ahead of the one being
+//    computed, so a CU keeps ~75-110 KB of gathers in flight without holding
+//    them in registers. The ring runs on from one item into the next: the
+//    next item's first chunks, its Q and its successor's row indices are
+//    loaded while the current item finishes. The 16-byte pieces of a row are
+//    XOR-swizzled by the row number so the MFMA fragment reads below are
+//    bank-conflict free.
 //  * Scores transposed, S^T = C Q^T (v_mfma_f32_16x16x32_bf16, keys on M,
 //    heads on N): wavefront w computes the 16-key x 16-head tile (w & 1,
 //    w >> 1) over 18 k-steps of the 576 dims, with its 16 heads of Q resident
-//    as B operands.
-//  * Online softmax in the log2 domain: per-head chunk maxima and sums go
-//    through LDS; every wavefront keeps the running max and sum of the heads
-//    its outputs cover, and rescales its outputs only when a head's max rises
-//    by more than a factor 2^8.
+//    as B operands and the fragment reads three k-steps ahead.
+//  * Online softmax in the log2 domain against a running max per head that
+//    every wavefront holds alike; the chunk maxima are exchanged, and the
+//    outputs rescaled, only when some head's max rises by more than a factor
+//    2^8. Each wavefront sums its own keys' probabilities; the two key tiles'
+//    sums are added once per item.
 //  * Values, O^T = V^T P^T. The S^T accumulator already has the layout of a
 //    B operand (lane = head, 4 consecutive keys per lane group) under a fixed
 //    permutation of the chunk's 32 keys, two runs of 4 consecutive keys per
 //    lane group; the V^T fragments come from the raw rows in that key order
 //    with two transposed LDS reads (ds_read_b64_tr_b16) each, instead of
 //    eight 2-byte reads (707 -> 648 us on the 4096-query bench, identical
-//    output). Wavefront w owns value tiles 4w .. 4w+3 of all four head
-//    tiles: 16 accumulators.
+//    output), one value tile ahead. Wavefront w owns value tiles 4w .. 4w+3
+//    of all four head tiles: 16 accumulators.
+//  * One barrier per chunk (see the main loop).
 #include "device_common.h"
 #include "kernels.h"
 
@@ -63,8 +69,9 @@ struct AttnSmem {
     uint4 head[NBUF][CK * MAIN16];  // row r, piece p at [r * 64 + (p ^ (r & 15))]
     uint4 tail[NBUF][CK * TAIL16];  // row r, piece q at [r * 8 + (q ^ (r & 7))]
     uint16_t p[2][4][64][8];        // P^T B fragments per head tile and lane, chunk parity
-    float pmax[2][AH];              // chunk maxima per key tile and head; at the end, the sums
-    uint8_t validb[kAttnMaxK / CK][8];  // chunk c, byte w, bit j: row 4w + j is valid
+    float pmax[2][AH];              // chunk maxima per key tile and head
+    float psum[2][AH];              // an item's sums per key tile and head
+    uint8_t validb[2][kAttnMaxK / CK][8];  // item parity, chunk c, byte w, bit j: row 4w + j is valid
     alignas(8) uint8_t jump[2][8];  // per chunk parity and wavefront: a head's max rose by more than 2^RESCALE_LOG2
 };
 
@@ -131,277 +138,396 @@ __device__ __forceinline__ void wait_vm()
     __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 
+// Where an item (query row, head tile) is: uniform values that step from
+// one item to the next without a division.
+struct ItemPos {
+    long long row;      // b * T + t
+    int tile;           // head tile
+    int t;              // the row's position in its stream
+    const char *cache;  // the stream's latent cache
+};
+
 __global__ __launch_bounds__(ATHREADS, 1) void sparse_attention_kernel(
     const uint16_t *__restrict__ Q, const uint16_t *__restrict__ C, const int *__restrict__ idx, int T, int S,
-    int H, int topk, float scale_log2, uint16_t *__restrict__ O, float *__restrict__ lse)
+    int H, int topk, long long items, float scale_log2, uint16_t *__restrict__ O, float *__restrict__ lse)
 {
     __shared__ AttnSmem sm;
     const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const long long row = blockIdx.x;  // b * T + t
-    const int h0 = blockIdx.y * AH;
-    const char *Cb = reinterpret_cast<const char *>(C + (row / T) * (long long)S * DQK);
-    const int *ir = idx + row * topk;
     const int kt = wid & 1, ht = wid >> 1;
+    const int ntile = H / AH;
     const int nchunk = (topk + CK - 1) / CK;
-
-    // The rows this wavefront gathers, in registers: lane l holds those of
-    // chunk l, the heads of rows 4w + j in hsel[j] and (wavefronts 0..3) the
-    // tails of rows 8w + j in tsel[j]. Every load is issued, at a clamped
-    // entry, so that they fly together with the Q loads below.
-    int hsel[4], tsel[8];
     const int last = topk - 1;
+
+    // Items (query row i / ntile, head tile i % ntile) are dealt out in
+    // contiguous runs, one per workgroup, and taken in order.
+    const long long first = blockIdx.x * items / gridDim.x, end = (blockIdx.x + 1) * items / gridDim.x;
+    if (first >= end) return;
+    ItemPos cp;
+    cp.row = first / ntile;
+    cp.tile = (int)(first % ntile);
+    cp.t = (int)(cp.row % T);
+    cp.cache = reinterpret_cast<const char *>(C + (cp.row / T) * (long long)S * DQK);
+    auto advance = [&](ItemPos q) {
+        if (++q.tile == ntile) {
+            q.tile = 0;
+            ++q.row;
+            if (++q.t == T) {
+                q.t = 0;
+                q.cache += (long long)S * DQK * 2;
+            }
+        }
+        return q;
+    };
+    ItemPos np = advance(cp);
+
+    // The rows this wavefront gathers for an item, in registers: lane l
+    // holds entries 32 l + 4 w + j (j < 4) of chunk l. Every load is issued,
+    // at a clamped entry, so that they fly together.
+    // (The lane number is made opaque at each call, so that the offsets are
+    // computed there instead of being hoisted and held across the loop.)
+    auto load_sel = [&](long long row, int (&s)[4]) {
+        const int *ir = idx + row * topk;
+        int l = lane;
+        asm volatile("" : "+v"(l));
 #pragma unroll
-    for (int j = 0; j < 4; ++j) hsel[j] = ir[min(lane * CK + 4 * wid + j, last)];
+        for (int j = 0; j < 4; ++j) s[j] = ir[min(l * CK + 4 * wid + j, last)];
+    };
+    // An entry is valid if it lies within topk and 0 <= idx < S. Its bit
+    // goes to the score mask of item parity `par` (chunk c, byte w, bit j =
+    // row 4w + j); a row that is not valid is gathered from row 0, so every
+    // gathered value is finite, and its score is masked.
+    auto validate = [&](int (&s)[4], int par) {
+        uint32_t vbits = 0;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) tsel[j] = ir[min(lane * CK + 8 * (wid & 3) + j, last)];
+        for (int j = 0; j < 4; ++j) {
+            const bool ok = lane * CK + 4 * wid + j <= last && s[j] >= 0 && s[j] < S;
+            vbits |= (ok ? 1u : 0u) << j;
+            s[j] = ok ? s[j] : 0;
+        }
+        if (lane < nchunk) sm.validb[par][lane][wid] = (uint8_t)vbits;
+    };
     // Q^T fragments of head tile ht: head h0 + 16 ht + lane % 16, dims 32 ks + 8 (lane / 16) ..
     bf16x8 qf[NQK];
-    {
-        const bf16x8 *qp = reinterpret_cast<const bf16x8 *>(
-            Q + ((row * H + h0 + ht * 16 + (lane & 15)) * DQK + (lane >> 4) * 8));
+    auto load_q = [&](const ItemPos &q) {
+        const uint16_t *qb = Q + (q.row * H + q.tile * AH + ht * 16) * DQK;
+        int l = lane;
+        asm volatile("" : "+v"(l));
+        const bf16x8 *qp = reinterpret_cast<const bf16x8 *>(qb + ((l & 15) * DQK + (l >> 4) * 8));
 #pragma unroll
         for (int ks = 0; ks < NQK; ++ks) qf[ks] = qp[ks * 4];
-    }
+    };
+    // Gather of chunk c of an item into buffer b: wavefront w loads the
+    // heads of rows 4w..4w+3 (lane i takes piece i ^ (r & 15) of row r into
+    // slot i) and, in lanes 0..31, their tails: five instructions per
+    // wavefront and chunk.
+    // e[j]: the row of entry 4w + j (uniform).
+    auto issue = [&](const char *Cb, const int (&e)[4], int b) {
+        int l = lane;
+        asm volatile("" : "+v"(l));
+        int e4 = e[0];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = 4 * wid + j;
+            e4 = ((l >> 3) & 3) == j ? e[j] : e4;
+            const char *src = Cb + (long long)e[j] * (DQK * 2) + ((l ^ (r & 15)) * 16);
+            gather16(src, __builtin_amdgcn_readfirstlane(lds_addr(&sm.head[b][r * MAIN16])));
+        }
+        const int r = 4 * wid + ((l >> 3) & 3);
+        const char *src = Cb + (long long)e4 * (DQK * 2) + DV * 2 + (((l & 7) ^ (r & 7)) * 16);
+        const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(&sm.tail[b][4 * wid * TAIL16]));
+        if (l < 32) gather16(src, dst);
+    };
+    auto rows_of = [&](const int (&s)[4], int c, int (&e)[4]) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) e[j] = __builtin_amdgcn_readlane(s[j], c);
+    };
+
+    int cur[4], nxt[4];
+    load_sel(cp.row, cur);
+    load_sel(first + 1 < end ? np.row : cp.row, nxt);
+    load_q(cp);
     // Finish these loads here, so that no wait for them is left to the main
-    // loop (where vmcnt counts only the gathers).
+    // loop (where vmcnt counts only the gathers and, after an item, its
+    // output stores).
     wait_vm<0>();
 #pragma unroll
     for (int ks = 0; ks < NQK; ++ks) asm volatile("" : "+v"(qf[ks]));
 #pragma unroll
-    for (int j = 0; j < 4; ++j) asm volatile("" : "+v"(hsel[j]));
-#pragma unroll
-    for (int j = 0; j < 8; ++j) asm volatile("" : "+v"(tsel[j]));
-    // An entry is valid if it lies within topk and 0 <= idx < S. Validity
-    // bits for the score mask: byte w of chunk c, bit j = row 4w + j. A row
-    // that is not valid is gathered from row 0 (its score is masked), so
-    // every gathered value is finite.
-    {
-        uint32_t vbits = 0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const bool ok = lane * CK + 4 * wid + j <= last && hsel[j] >= 0 && hsel[j] < S;
-            vbits |= (ok ? 1u : 0u) << j;
-            hsel[j] = ok ? hsel[j] : 0;
-        }
-        if (lane < nchunk) sm.validb[lane][wid] = (uint8_t)vbits;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const bool ok = lane * CK + 8 * (wid & 3) + j <= last && tsel[j] >= 0 && tsel[j] < S;
-            tsel[j] = ok ? tsel[j] : 0;
-        }
+    for (int j = 0; j < 4; ++j) asm volatile("" : "+v"(cur[j]), "+v"(nxt[j]));
+    validate(cur, 0);
+    validate(nxt, 1);
+
+    // The chunks of this workgroup's items form one sequence, g = 0, 1, ...:
+    // chunk g goes to buffer g % NBUF, and its P and flags to parity g & 1.
+    // One barrier per chunk. Before the barrier of chunk g each wavefront has
+    // written its share of P(g) and waited for its own gathers of chunk g + 1;
+    // after it, chunk g + 1 is visible to all and every wavefront is past the
+    // values of chunk g - 1, so chunk g + 3 (of this item or the next) is
+    // gathered into that chunk's buffer. P and the flags alternate between two
+    // buffers, so a wavefront writing those of chunk g + 1 cannot overwrite
+    // what a slower one still reads of chunk g. At the end of an item the
+    // next item's Q, taken after the last score phase, and its successor's
+    // row indices are waited for, once: the next item's first three chunks
+    // have landed by then, so its first two waits are skipped (they would
+    // wait for the output stores issued after). Waits count gathers, five
+    // per chunk.
+    for (int c = 0; c < NBUF - 1 && c < nchunk; ++c) {
+        int e[4];
+        rows_of(cur, c, e);
+        issue(cp.cache, e, c);
     }
-
-    // Gather of chunk c into buffer c % NBUF: wavefront w loads the heads of
-    // rows 4w..4w+3 (lane i takes piece i ^ (r & 15) of row r into slot i),
-    // wavefronts 0..3 also the tails of rows 8w..8w+7.
-    auto issue = [&](int c) {
-        const int b = c % NBUF;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int r = 4 * wid + j;
-            const int e = __builtin_amdgcn_readlane(hsel[j], c);
-            const char *src = Cb + (long long)e * (DQK * 2) + ((lane ^ (r & 15)) * 16);
-            gather16(src, __builtin_amdgcn_readfirstlane(lds_addr(&sm.head[b][r * MAIN16])));
-        }
-        if (wid < 4) {
-            const int r = 8 * wid + (lane >> 3);
-            int e = __builtin_amdgcn_readlane(tsel[0], c);
-#pragma unroll
-            for (int j = 1; j < 8; ++j) {
-                const int ej = __builtin_amdgcn_readlane(tsel[j], c);
-                e = (lane >> 3) == j ? ej : e;
-            }
-            const char *src = Cb + (long long)e * (DQK * 2) + DV * 2 + (((lane & 7) ^ (r & 7)) * 16);
-            gather16(src, __builtin_amdgcn_readfirstlane(lds_addr(&sm.tail[b][wid * 64])));
-        }
-    };
-
-    f32x4 o[4][4];  // [head tile][value tile 4 wid + j]
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) o[a][j] = f32x4{};
-    float m_run[4];  // running max of heads 16 a + lane % 16, log2 domain
-#pragma unroll
-    for (int a = 0; a < 4; ++a) m_run[a] = -INFINITY;
-    float l_part = 0.0f;  // sum of P over this wavefront's keys (tile kt), head 16 ht + lane % 16
-
-    // One barrier per chunk. Before the barrier of chunk c each wavefront
-    // has written its share of P(c) and waited for its own gathers of chunk
-    // c + 1; after it, chunk c + 1 is visible to all, every wavefront is past
-    // the values of chunk c - 1, so chunk c + 3 is gathered into that
-    // chunk's buffer. P and the flags alternate between two buffers, so a
-    // wavefront writing those of chunk c + 1 cannot overwrite what a slower
-    // one still reads of chunk c. Waits count gathers: 5 per chunk in
-    // wavefronts 0..3, 4 in the others.
-    for (int c = 0; c < NBUF - 1 && c < nchunk; ++c) issue(c);
-    if (nchunk >= 3) {
-        if (wid < 4) wait_vm<10>(); else wait_vm<8>();
-    } else if (nchunk == 2) {
-        if (wid < 4) wait_vm<5>(); else wait_vm<4>();
-    } else {
-        wait_vm<0>();
-    }
+    if (nchunk >= 3) wait_vm<10>();
+    else if (nchunk == 2) wait_vm<5>();
+    else wait_vm<0>();
     __syncthreads();  // chunk 0 and the validity bits visible
-    for (int c = 0; c < nchunk; ++c) {
-        const int b = c % NBUF, pb = c & 1;
-        // scores of key tile kt x head tile ht
-        f32x4 s = f32x4{};
-        {
-            const int r = kt * 16 + (lane & 15);
-            const uint4 *hr = &sm.head[b][r * MAIN16];
-            const uint4 *tr = &sm.tail[b][r * TAIL16];
-            // Each MFMA group runs at raised wavefront priority, so the other
-            // wavefront of the SIMD fills the matrix pipe's gaps with its
-            // VALU work instead of delaying the next MFMA (2% on the bench).
-            __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-            for (int ks = 0; ks < NQK; ++ks) {
-                const int pc = ks * 4 + (lane >> 4);
-                const uint4 v = pc < MAIN16 ? hr[pc ^ (r & 15)] : tr[(pc - MAIN16) ^ (r & 7)];
-                s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v), qf[ks], s, 0, 0, 0);
-            }
-        }
-        __builtin_amdgcn_s_setprio(0);
-        const uint32_t vb = sm.validb[c][4 * kt + (lane >> 4)];  // keys kt * 16 + 4 (lane / 16) + i
-        float z[4], mx = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            z[i] = (vb >> i) & 1u ? s[i] * scale_log2 : -INFINITY;
-            mx = fmaxf(mx, z[i]);
-        }
-        mx = quad_max(mx);
-        if (lane < 16) sm.pmax[kt][ht * 16 + lane] = mx;
 
-        // Lazy rescaling: a head keeps its running max until a chunk's max
-        // exceeds it by more than RESCALE_LOG2, so the probabilities stay
-        // below 2^RESCALE_LOG2 (exact in fp32; bf16 keeps its relative
-        // precision) and O is rescaled only when some head's max jumps, in
-        // practice after the first chunk only. So P is first formed against
-        // the running max, which every wavefront holds alike, with no
-        // exchange; a wavefront that sees one of its heads jump raises a
-        // flag, and only then do all wavefronts exchange the chunk maxima,
-        // form P again and rescale.
-        float m_ht = m_run[0];
+    int g = 0;
+    int par = 0;  // item parity of the validity bits
+    bool fresh = false;
+    for (long long n = first;;) {
+        const bool more = n + 1 < end;
+        const bool carry = more && nchunk >= NBUF - 1;  // the ring runs on into the next item
+        f32x4 o[4][4];  // [head tile][value tile 4 wid + j]
 #pragma unroll
-        for (int a = 1; a < 4; ++a) m_ht = ht == a ? m_run[a] : m_ht;
-        if (lane == 0) sm.jump[pb][wid] = wave_ballot(mx > m_ht + RESCALE_LOG2) != 0 ? 1 : 0;
-        float pr[4], ps = 0.0f;
-        {
-            const float mu = m_ht == -INFINITY ? 0.0f : m_ht;
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) o[a][j] = f32x4{};
+        float m_run[4];  // running max of heads 16 a + lane % 16, log2 domain
+#pragma unroll
+        for (int a = 0; a < 4; ++a) m_run[a] = -INFINITY;
+        float l_part = 0.0f;  // sum of P over this wavefront's keys (tile kt), head 16 ht + lane % 16
+
+        for (int c = 0; c < nchunk; ++c, ++g) {
+            const int b = g & (NBUF - 1), pb = g & 1;
+
+            // scores of key tile kt x head tile ht
+            f32x4 s = f32x4{};
+            {
+                const int r = kt * 16 + (lane & 15);
+                const uint4 *hr = &sm.head[b][r * MAIN16];
+                const uint4 *tr = &sm.tail[b][r * TAIL16];
+                // Each MFMA group runs at raised wavefront priority, so the other
+                // wavefront of the SIMD fills the matrix pipe's gaps with its
+                // VALU work instead of delaying the next MFMA (2% on the bench).
+                __builtin_amdgcn_s_setprio(1);
+                // The fragment reads run three ahead of the MFMAs, so their
+                // LDS latency stays hidden behind the chain; scheduling
+                // barriers keep that order under register pressure.
+                auto frag = [&](int ks) {
+                    const int pc = ks * 4 + (lane >> 4);
+                    return pc < MAIN16 ? hr[pc ^ (r & 15)] : tr[(pc - MAIN16) ^ (r & 7)];
+                };
+                uint4 v0 = frag(0), v1 = frag(1), v2 = frag(2);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int ks = 0; ks < NQK; ++ks) {
+                    s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v0), qf[ks], s, 0, 0, 0);
+                    v0 = v1;
+                    v1 = v2;
+                    if (ks + 3 < NQK) v2 = frag(ks + 3);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            __builtin_amdgcn_s_setprio(0);
+            const uint32_t vb = sm.validb[par][c][4 * kt + (lane >> 4)];  // keys kt * 16 + 4 (lane / 16) + i
+            float z[4], mx = -INFINITY;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                pr[i] = exp2_fast(z[i] - mu);
-                ps += pr[i];
+                z[i] = (vb >> i) & 1u ? s[i] * scale_log2 : -INFINITY;
+                mx = fmaxf(mx, z[i]);
             }
-        }
-        *reinterpret_cast<uint2 *>(&sm.p[pb][ht][lane][kt * 4]) =
-            make_uint2(pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]));
-        if (c + 2 < nchunk) {
-            if (wid < 4) wait_vm<5>(); else wait_vm<4>();
-        } else {
-            wait_vm<0>();
-        }
-        __syncthreads();
-        if (c + NBUF - 1 < nchunk) issue(c + NBUF - 1);
+            mx = quad_max(mx);
+            if (lane < 16) sm.pmax[kt][ht * 16 + lane] = mx;
 
-        if (*reinterpret_cast<const uint64_t *>(sm.jump[pb]) != 0) {  // the same answer in every wavefront
-            float m_new[4], m_use[4], alpha[4];
-            bool moved = false;
+            // Lazy rescaling: a head keeps its running max until a chunk's max
+            // exceeds it by more than RESCALE_LOG2, so the probabilities stay
+            // below 2^RESCALE_LOG2 (exact in fp32; bf16 keeps its relative
+            // precision) and O is rescaled only when some head's max jumps, in
+            // practice after the first chunk only. So P is first formed against
+            // the running max, which every wavefront holds alike, with no
+            // exchange; a wavefront that sees one of its heads jump raises a
+            // flag, and only then do all wavefronts exchange the chunk maxima,
+            // form P again and rescale.
+            float m_ht = m_run[0];
 #pragma unroll
-            for (int a = 0; a < 4; ++a) {
-                const int hh = a * 16 + (lane & 15);
-                const float cm = fmaxf(sm.pmax[0][hh], sm.pmax[1][hh]);
-                const bool up = cm > m_run[a] + RESCALE_LOG2;  // always, from -inf, once a key is valid
-                m_new[a] = up ? cm : m_run[a];
-                m_use[a] = m_new[a] == -INFINITY ? 0.0f : m_new[a];
-                alpha[a] = up ? exp2_fast(m_run[a] - m_use[a]) : 1.0f;
-                moved = moved || up;
-            }
-            float mu = m_use[0], al = alpha[0];
+            for (int a = 1; a < 4; ++a) m_ht = ht == a ? m_run[a] : m_ht;
+            if (lane == 0) sm.jump[pb][wid] = wave_ballot(mx > m_ht + RESCALE_LOG2) != 0 ? 1 : 0;
+            float pr[4], ps = 0.0f;
+            {
+                const float mu = m_ht == -INFINITY ? 0.0f : m_ht;
 #pragma unroll
-            for (int a = 1; a < 4; ++a) {
-                mu = ht == a ? m_use[a] : mu;
-                al = ht == a ? alpha[a] : al;
+                for (int i = 0; i < 4; ++i) {
+                    pr[i] = exp2_fast(z[i] - mu);
+                    ps += pr[i];
+                }
             }
-            ps = 0.0f;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                pr[i] = exp2_fast(z[i] - mu);
-                ps += pr[i];
-            }
-            l_part *= al;
             *reinterpret_cast<uint2 *>(&sm.p[pb][ht][lane][kt * 4]) =
                 make_uint2(pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]));
+            if (!fresh || c >= 2) {
+                if (c + 2 < nchunk || carry) wait_vm<5>();
+                else wait_vm<0>();
+            }
+            __syncthreads();
+            {
+                const bool own = c + NBUF - 1 < nchunk;
+                if (own || carry) {
+                    int e[4], en[4];
+                    rows_of(cur, c + NBUF - 1, e);
+                    rows_of(nxt, c + NBUF - 1 - nchunk, en);
 #pragma unroll
-            for (int a = 0; a < 4; ++a) m_run[a] = m_new[a];
-            if (wave_ballot(moved)) {  // a head's running max rose: rescale
+                    for (int j = 0; j < 4; ++j) e[j] = own ? e[j] : en[j];
+                    issue(own ? cp.cache : np.cache, e, (g + NBUF - 1) & (NBUF - 1));
+                }
+            }
+            if (c == nchunk - 1 && carry) {
+                // The scores of this item are done: the next item's Q and the
+                // row indices of the one after it are loaded now, waited for
+                // at the end of the item.
+                load_q(np);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) cur[j] = nxt[j];
+                load_sel(n + 2 < end ? advance(np).row : np.row, nxt);
+            }
+
+            if (*reinterpret_cast<const uint64_t *>(sm.jump[pb]) != 0) {  // the same answer in every wavefront
+                float m_new[4], m_use[4], alpha[4];
+                bool moved = false;
+#pragma unroll
+                for (int a = 0; a < 4; ++a) {
+                    const int hh = a * 16 + (lane & 15);
+                    const float cm = fmaxf(sm.pmax[0][hh], sm.pmax[1][hh]);
+                    const bool up = cm > m_run[a] + RESCALE_LOG2;  // always, from -inf, once a key is valid
+                    m_new[a] = up ? cm : m_run[a];
+                    m_use[a] = m_new[a] == -INFINITY ? 0.0f : m_new[a];
+                    alpha[a] = up ? exp2_fast(m_run[a] - m_use[a]) : 1.0f;
+                    moved = moved || up;
+                }
+                float mu = m_use[0], al = alpha[0];
+#pragma unroll
+                for (int a = 1; a < 4; ++a) {
+                    mu = ht == a ? m_use[a] : mu;
+                    al = ht == a ? alpha[a] : al;
+                }
+                ps = 0.0f;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    pr[i] = exp2_fast(z[i] - mu);
+                    ps += pr[i];
+                }
+                l_part *= al;
+                *reinterpret_cast<uint2 *>(&sm.p[pb][ht][lane][kt * 4]) =
+                    make_uint2(pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]));
+#pragma unroll
+                for (int a = 0; a < 4; ++a) m_run[a] = m_new[a];
+                if (wave_ballot(moved)) {  // a head's running max rose: rescale
+#pragma unroll
+                    for (int a = 0; a < 4; ++a)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) o[a][j][i] *= alpha[a];
+                }
+                __syncthreads();  // P formed again; maxima and flags read
+            }
+            l_part += quad_sum(ps);
+            // Value fragments (each 8 keys of one dim column, read from the raw
+            // rows) one tile ahead of the MFMAs that use them; the four P
+            // fragments are read once per chunk and kept in registers (reading
+            // them for each value tile was 96 KB of LDS reads per chunk more:
+            // 605 -> 585 us). Nothing spills, so no vector-memory instruction
+            // but the gathers runs in this loop.
+            const int ln = lane, g = lane >> 4, i16 = lane & 15;
+            const int kr0 = 4 * g + (i16 >> 2), kr1 = kr0 + 16;  // the two key runs of lane group g
+            // Transposed LDS reads: lane 4q + c of a 16-lane group points at 4
+            // values (dims dv0 + 4c ..) of key 4g + q (then 16 + 4g + q), and
+            // lane i of the group receives dim dv0 + i of those 4 keys.
+            auto vfrag = [&](int j) {
+                const int col = (4 * wid + j) * 16 + 4 * (i16 & 3);
+                auto trv = [&](int key) {
+                    const char *p = reinterpret_cast<const char *>(&sm.head[b][key * MAIN16 + ((col >> 3) ^ (key & 15))]) +
+                                    (col & 7) * 2;
+                    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s *)p);
+                };
+                const v4s lo = trv(kr0), hi = trv(kr1);
+                return bf16x8{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+            };
+            bf16x8 pf[4];  // the chunk's P fragments, read once for the four value tiles
+#pragma unroll
+            for (int a = 0; a < 4; ++a) pf[a] = *reinterpret_cast<const bf16x8 *>(&sm.p[pb][a][ln][0]);
+            bf16x8 va = vfrag(0);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const bf16x8 vn = j + 1 < 4 ? vfrag(j + 1) : va;
+                __builtin_amdgcn_s_setprio(1);
 #pragma unroll
                 for (int a = 0; a < 4; ++a)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) o[a][j][i] *= alpha[a];
+                    o[a][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pf[a], o[a][j], 0, 0, 0);
+                __builtin_amdgcn_s_setprio(0);
+                va = vn;
+                __builtin_amdgcn_sched_barrier(0);
             }
-            __syncthreads();  // P formed again; maxima and flags read
         }
-        l_part += quad_sum(ps);
-        // One value fragment at a time (its 8 keys read from the raw rows);
-        // the four P fragments are read once per chunk and kept in registers
-        // (reading them for each value tile was 96 KB of LDS reads per chunk
-        // more: 605 -> 585 us). Nothing spills, so no vector-memory
-        // instruction but the gathers runs in this loop.
-        const int ln = lane, g = lane >> 4, i16 = lane & 15;
-        const int kr0 = 4 * g + (i16 >> 2), kr1 = kr0 + 16;  // the two key runs of lane group g
-        bf16x8 pf[4];  // the chunk's P fragments, read once for the four value tiles
-#pragma unroll
-        for (int a = 0; a < 4; ++a) pf[a] = *reinterpret_cast<const bf16x8 *>(&sm.p[pb][a][ln][0]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            // Transposed LDS reads: lane 4q + c of a 16-lane group points at
-            // 4 values (dims dv0 + 4c ..) of key 4g + q (then 16 + 4g + q),
-            // and lane i of the group receives dim dv0 + i of those 4 keys.
-            const int col = (4 * wid + j) * 16 + 4 * (i16 & 3);
-            auto trv = [&](int key) {
-                const char *p = reinterpret_cast<const char *>(&sm.head[b][key * MAIN16 + ((col >> 3) ^ (key & 15))]) +
-                                (col & 7) * 2;
-                return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s *)p);
-            };
-            const v4s lo = trv(kr0), hi = trv(kr1);
-            const bf16x8 va = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-            __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-            for (int a = 0; a < 4; ++a)
-                o[a][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pf[a], o[a][j], 0, 0, 0);
-            __builtin_amdgcn_s_setprio(0);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    }
 
-    // The two key tiles' sums of each head, added once. (The maxima are read
-    // only between a chunk's barrier and the barrier that ends its rescale,
-    // so their array is free here.)
-    if (lane < 16) sm.pmax[kt][ht * 16 + lane] = l_part;
-    __syncthreads();
-    float l_run[4];
+        // The two key tiles' sums of each head, added once.
+        if (lane < 16) sm.psum[kt][ht * 16 + lane] = l_part;
+        __syncthreads();
+        float l_run[4];
 #pragma unroll
-    for (int a = 0; a < 4; ++a) l_run[a] = sm.pmax[0][a * 16 + (lane & 15)] + sm.pmax[1][a * 16 + (lane & 15)];
-
-    // O^T tile (value tile 4 wid + j, head tile a): lane holds head 16 a +
-    // lane % 16 and value dims 16 (4 wid + j) + 4 (lane / 16) .. +3.
+        for (int a = 0; a < 4; ++a) l_run[a] = sm.psum[0][a * 16 + (lane & 15)] + sm.psum[1][a * 16 + (lane & 15)];
+        if (carry) {
+            wait_vm<0>();
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-        const float inv = l_run[a] > 0.0f ? 1.0f / l_run[a] : 0.0f;
-        const long long orow = (row * H + h0 + a * 16 + (lane & 15)) * DV;
+            for (int ks = 0; ks < NQK; ++ks) asm volatile("" : "+v"(qf[ks]));
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int dv = (4 * wid + j) * 16 + 4 * (lane >> 4);
-            *reinterpret_cast<uint2 *>(&O[orow + dv]) =
-                make_uint2(pack_bf16x2(o[a][j][0] * inv, o[a][j][1] * inv), pack_bf16x2(o[a][j][2] * inv, o[a][j][3] * inv));
+            for (int j = 0; j < 4; ++j) asm volatile("" : "+v"(nxt[j]));
+            validate(nxt, par);  // the item after next; this item's bits are no longer read
         }
-        if (lse && wid == 0 && lane < 16)
-            lse[row * H + h0 + a * 16 + lane] =
-                l_run[a] > 0.0f ? (m_run[a] + log2f(l_run[a])) * 0.69314718055994530942f : -INFINITY;
+
+        // O^T tile (value tile 4 wid + j, head tile a): lane holds head 16 a +
+        // lane % 16 and value dims 16 (4 wid + j) + 4 (lane / 16) .. +3.
+        const long long row = cp.row;
+        const int h0 = cp.tile * AH;
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            const float inv = l_run[a] > 0.0f ? 1.0f / l_run[a] : 0.0f;
+            const long long orow = (row * H + h0 + a * 16 + (lane & 15)) * DV;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int dv = (4 * wid + j) * 16 + 4 * (lane >> 4);
+                *reinterpret_cast<uint2 *>(&O[orow + dv]) = make_uint2(pack_bf16x2(o[a][j][0] * inv, o[a][j][1] * inv),
+                                                                        pack_bf16x2(o[a][j][2] * inv, o[a][j][3] * inv));
+            }
+            if (lse && wid == 0 && lane < 16)
+                lse[row * H + h0 + a * 16 + lane] =
+                    l_run[a] > 0.0f ? (m_run[a] + log2f(l_run[a])) * 0.69314718055994530942f : -INFINITY;
+        }
+        if (!more) break;
+        if (!carry) {
+            // Items of fewer than NBUF - 1 chunks: the next one starts as the
+            // first did (its bits go to the other parity, whose item is done).
+            load_sel(np.row, cur);
+            load_q(np);
+            wait_vm<0>();
+#pragma unroll
+            for (int ks = 0; ks < NQK; ++ks) asm volatile("" : "+v"(qf[ks]));
+#pragma unroll
+            for (int j = 0; j < 4; ++j) asm volatile("" : "+v"(cur[j]));
+            validate(cur, par ^ 1);
+            for (int c = 0; c < nchunk; ++c) {
+                int e[4];
+                rows_of(cur, c, e);
+                issue(np.cache, e, (g + c) & (NBUF - 1));
+            }
+            if (nchunk == 2) wait_vm<5>();
+            else wait_vm<0>();
+            __syncthreads();  // its chunk 0 and validity bits visible
+        }
+        ++n;
+        cp = np;
+        np = advance(np);
+        par ^= 1;
+        fresh = carry;
     }
 }
 
@@ -411,9 +537,17 @@ hipError_t launch_sparse_attention(const AttnProblem &p, const void *Q, const vo
                                    float *lse, hipStream_t st)
 {
     const float scale_log2 = (float)((double)p.softmax_scale * 1.4426950408889634);
-    hipLaunchKernelGGL(sparse_attention_kernel, dim3((unsigned)((long long)p.B * p.T), (unsigned)(p.H / AH)),
-                       dim3(ATHREADS), 0, st, static_cast<const uint16_t *>(Q), static_cast<const uint16_t *>(KV), idx,
-                       p.T, p.S, p.H, p.topk, scale_log2, static_cast<uint16_t *>(O), lse);
+    const long long items = (long long)p.B * p.T * (p.H / AH);
+    // One workgroup per CU (the LDS ring allows no more), each walking its
+    // items, with the gather ring carried from one item into the next.
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    const long long grid = cus > 0 && cus < items ? cus : items;
+    hipLaunchKernelGGL(sparse_attention_kernel, dim3((unsigned)grid), dim3(ATHREADS), 0, st,
+                       static_cast<const uint16_t *>(Q), static_cast<const uint16_t *>(KV), idx, p.T, p.S, p.H, p.topk,
+                       items, scale_log2, static_cast<uint16_t *>(O), lse);
     return hipGetLastError();
 }
 

@@ -170,3 +170,25 @@ def test_prefill_chunk_full_size_sampled():
     g = np.random.Generator(np.random.PCG64(21))
     rows = np.unique(np.concatenate([[0, 4095], g.integers(0, 4096, 22)]))
     check(a, go, glse, rows=rows)
+
+
+@pytest.mark.parametrize("seed,B,T,S,H,k,pad,sample", [
+    (30, 1, 700, 3000, 64, 40, 0.0, None),    # 2 chunks per item: each item starts its own gathers
+    (31, 2, 300, 2000, 64, 70, 0.0, None),    # 3 chunks (the last ragged): gathers run on into the next item
+    (32, 1, 200, 5000, 128, 512, 0.0, None),  # two head tiles per query row
+    (33, 3, 120, 900, 192, 96, 0.3, None),    # three head tiles, streams change within a workgroup's run
+    (34, 1, 300, 4096, 64, 2048, 0.0, 40),    # the largest selection, 64 chunks
+])
+def test_many_items_per_workgroup(seed, B, T, S, H, k, pad, sample):
+    # More (query row, head tile) items than CUs, so every workgroup takes a
+    # run of consecutive items, carrying its gather ring (or restarting it)
+    # from one item to the next; every row (or a sample with both ends)
+    # against the oracle
+    a = W.attention(seed=seed, B=B, T=T, S=S, H=H, topk=k, pad_frac=pad)
+    _say(f"sparse attention many items seed={seed} B={B} T={T} S={S} H={H} k={k} pad={pad}")
+    go, glse = run_attention(a)
+    rows = None
+    if sample:
+        g = np.random.Generator(np.random.PCG64(seed))
+        rows = np.unique(np.concatenate([[0, B * T - 1], g.integers(0, B * T, sample - 2)]))
+    check(a, go, glse, rows=rows)
