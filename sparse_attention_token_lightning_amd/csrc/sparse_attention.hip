@@ -111,6 +111,13 @@ __device__ __forceinline__ void gather16(const void *src, uint32_t lds)
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory", "m0");
 }
 
+// The same from a wavefront-uniform base (scalar registers) plus a 32-bit
+// per-lane byte offset: no per-lane 64-bit address arithmetic.
+__device__ __forceinline__ void gather16_at(const void *base, uint32_t off, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds) : "memory", "m0");
+}
+
 // Max / sum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (one head of a
 // 16 x 16 accumulator tile) with the permlane swaps, VALU only.
 __device__ __forceinline__ float quad_max(float x)
@@ -229,8 +236,8 @@ __global__ __launch_bounds__(ATHREADS, 1) void sparse_attention_kernel(
         for (int j = 0; j < 4; ++j) {
             const int r = 4 * wid + j;
             e4 = ((l >> 3) & 3) == j ? e[j] : e4;
-            const char *src = Cb + (long long)e[j] * (DQK * 2) + ((l ^ (r & 15)) * 16);
-            gather16(src, __builtin_amdgcn_readfirstlane(lds_addr(&sm.head[b][r * MAIN16])));
+            gather16_at(Cb + (long long)e[j] * (DQK * 2), (uint32_t)((lane ^ (r & 15)) * 16),
+                        __builtin_amdgcn_readfirstlane(lds_addr(&sm.head[b][r * MAIN16])));
         }
         const int r = 4 * wid + ((l >> 3) & 3);
         const char *src = Cb + (long long)e4 * (DQK * 2) + DV * 2 + (((l & 7) ^ (r & 7)) * 16);
@@ -313,9 +320,14 @@ __global__ __launch_bounds__(ATHREADS, 1) void sparse_attention_kernel(
                 // The fragment reads run three ahead of the MFMAs, so their
                 // LDS latency stays hidden behind the chain; scheduling
                 // barriers keep that order under register pressure.
+                // Piece 4 ks + lane / 16 of the row, swizzled: for k-step
+                // 4a + c (a, c < 4) that is piece 16a + ((4c + lane / 16) ^
+                // (r & 15)), so the four k-steps of each c share one address
+                // and differ by an immediate offset.
                 auto frag = [&](int ks) {
-                    const int pc = ks * 4 + (lane >> 4);
-                    return pc < MAIN16 ? hr[pc ^ (r & 15)] : tr[(pc - MAIN16) ^ (r & 7)];
+                    const int q = lane >> 4;
+                    return ks < 16 ? hr[((4 * (ks & 3) + q) ^ (r & 15)) + 16 * (ks >> 2)]
+                                   : tr[(4 * (ks - 16) + q) ^ (r & 7)];
                 };
                 uint4 v0 = frag(0), v1 = frag(1), v2 = frag(2);
                 __builtin_amdgcn_sched_barrier(0);
