@@ -27,8 +27,8 @@ prefill (2048 queries after 1,046,528 cached E4M3 keys).
 
 Before each timed 64k step a 512 MB buffer is written so the step starts
 with a cold last-level cache (--no-flush to skip). Also reported: measured
-ceilings in plain torch (an HBM read of 277 MB rotated over three copies, an
-8192^3 bf16 matmul), and the CPU oracle timed per workload with the host's
+ceilings in plain torch (HBM reads of 277 MB rotated over three copies by a sum
+and by a library GEMV, a 277 MB device copy, an 8192^3 bf16 matmul), and the CPU oracle timed per workload with the host's
 core count, CPU model and a one-thread rate.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
@@ -71,7 +71,7 @@ def _parse():
                     help="skip the per-workload oracle timings (every row of the tiny, 8k, 8k-int and "
                          "decode workloads; sampled rows of the 64k and 1M prefills)")
     ap.add_argument("--no-ceilings", action="store_true",
-                    help="skip the measured ceilings (torch read of 3 x 277 MB rotated; bf16 matmul)")
+                    help="skip the measured ceilings (torch sum, GEMV and copy over 277 MB; bf16 matmul)")
     ap.add_argument("--no-flush", action="store_true",
                     help="do not write a 512 MB buffer before each timed 64k step")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -516,7 +516,27 @@ def main():
 
         rus = _time_calls(rstep, 30, stream, args.warm_ms)
         rmed = rus[len(rus) // 2]
-        del bufs
+        # a library GEMV reads its matrix once: [16906 x 4096] fp32, the first 276,987,904 B
+        grow = nbytes // 4 // 4096
+        gbytes = grow * 4096 * 4
+        mats = [b[:grow * 4096].view(grow, 4096) for b in bufs]
+        vec = torch.ones(4096, dtype=torch.float32, device=dev)
+        res = torch.empty(grow, dtype=torch.float32, device=dev)
+
+        def gstep(i):
+            torch.mv(mats[i % 3], vec, out=res)
+
+        gus = _time_calls(gstep, 30, stream, args.warm_ms)
+        gmed = gus[len(gus) // 2]
+        # a device copy of 277 MB (read + write)
+        dst = torch.empty(nbytes // 4, dtype=torch.float32, device=dev)
+
+        def cstep(i):
+            dst.copy_(bufs[i % 3])
+
+        cus_ = _time_calls(cstep, 30, stream, args.warm_ms)
+        cmed = cus_[len(cus_) // 2]
+        del bufs, mats, vec, res, dst
         n = 8192
         ma = torch.randn((n, n), dtype=torch.bfloat16, device=dev)
         mb = torch.randn((n, n), dtype=torch.bfloat16, device=dev)
@@ -528,10 +548,16 @@ def main():
         mus = _time_calls(mstep, 20, stream, args.warm_ms)
         mmed = mus[len(mus) // 2]
         del ma, mb, mc
+        def rate(nb, us):
+            return {"us_median": round(us, 2), "GB_s": round(nb / (us * 1e-6) / 1e9, 1),
+                    "frac_of_peak": round(nb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+
         extra["ceilings"] = {
-            "hbm_read": {"what": "torch.sum over 276,989,952 B, rotated over 3 copies",
-                         "us_median": round(rmed, 2), "GB_s": round(nbytes / (rmed * 1e-6) / 1e9, 1),
-                         "frac_of_peak": round(nbytes / (rmed * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
+            "hbm_read": {"what": "torch.sum over 276,989,952 B, rotated over 3 copies", **rate(nbytes, rmed)},
+            "hbm_read_gemv": {"what": "torch.mv of a [16906 x 4096] fp32 matrix (276,987,904 B), rotated over "
+                                      "3 copies", **rate(gbytes, gmed)},
+            "hbm_copy": {"what": "torch copy_ of 276,989,952 B (read + write, counted twice)",
+                         **rate(2 * nbytes, cmed)},
             "bf16_matmul": {"what": "torch.matmul 8192 x 8192 x 8192 bf16",
                             "us_median": round(mmed, 2),
                             "tflops": round(2 * n ** 3 / (mmed * 1e-6) / 1e12, 1),
