@@ -72,18 +72,24 @@ constexpr int kSplitPartLens[3] = {8192, 12288, 16384};
 constexpr int kSplitCUs = 256;  // compute units of an MI355X: one split workgroup each
 int set_split_len(int len);     // 0 = automatic; returns the previous value, -1 if unsupported
 int get_split_len();
+// Ragged batches of at most kSplitPlanRows query rows and streams, with the
+// automatic length, take planned partitions: every row's keys split into
+// equal parts of a length chosen on the device so that all parts start in
+// one round on the kSplitCUs compute units (see the kernel).
+constexpr int kSplitPlanRows = 256;
 struct SplitWorkspace {
     uint32_t *ctr;         // [rows] arrival counters, zero between calls
-    uint64_t *meta;        // [rows, P, 2] short-list edge << 32 | m-th largest key (~0: none); largest key
-    uint64_t *full_list;   // [rows, P, slots] (index << 32 | order key), key 0 = empty slot
-    uint64_t *short_list;  // [rows, P, short slots], same format
-};
+    uint64_t *meta;        // [lists, 2] short-list edge << 32 | m-th largest key (~0: none); largest key
+    uint64_t *full_list;   // [lists, slots] (index << 32 | order key), key 0 = empty slot
+    uint64_t *short_list;  // [lists, short slots], same format
+};                         // lists: rows x partitions per row, or the planned launch's blocks
 // Rows of a split-key launch, the most keys a row sees, and the row length the
 // merge's short lists are sized for (rows with fewer full partitions fall back
 // to the full lists, which for short rows are few).
 struct SplitShape {
     long long rows, max_len, short_len;
-    int part;  // partition length (keys), one of kSplitPartLens
+    int part;      // partition length (keys), one of kSplitPartLens; the longest for planned parts
+    int plan = 0;  // planned parts: blocks launched (at least the parts of any plan), else 0
 };
 SplitShape split_shape(const Problem &p);
 SplitShape split_shape(const VarlenProblem &p);

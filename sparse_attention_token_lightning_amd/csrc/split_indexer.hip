@@ -108,6 +108,12 @@ struct SplitSmem {
     uint32_t nl;
     uint32_t pn[kSplitMaxParts];      // merge: full-list length per partition
     int last;
+    // the planned partitioning of a ragged batch (see plan_block)
+    long long pk[kSplitPlanRows + 1];  // clamped key prefix sums
+    int pq[kSplitPlanRows + 1];        // clamped query prefix sums
+    int own[kSplitPlanRows];           // the stream of each query row
+    long long plan_k0, plan_L;
+    int plan_r, plan_p, plan_n, plan_len, plan_base;
 };
 
 // A candidate slot: order key in the low word (0 = empty), key index in the high word.
@@ -409,11 +415,112 @@ __device__ __forceinline__ float score_sub(const Raw<KFP8> &r, const uint16_t *q
     return (s4[0] + s4[1]) + (s4[2] + s4[3]);
 }
 
+// Planned partitions for a ragged batch of at most kSplitPlanRows query rows
+// (and streams): the keys each row sees are split into n_r equal parts of at
+// most T keys, T being the shortest multiple of 512 (at most PL_MAX) for which
+// all the parts start in one round on the GPU's CUs; blocks take the parts in
+// row order. Every block works the plan out alike from the prefix sums (no
+// host synchronisation): rows are found as in wave_row_stream (the first
+// stream whose clamped range holds the row), so malformed prefix sums give
+// wrong rows but still one owner per row. Returns false for a block past the
+// last part. The host launches at least sum_r ceil(L_r / PL_MAX) blocks.
+__device__ bool plan_block(SplitSmem &sm, const Ragged &rg, int max_k, int tid, int lane, int wid, long long &r,
+                           int &p, long long &L, long long &k0, int &nparts, int &plen, long long &lbase)
+{
+    const int B = rg.B, TQ = rg.total_q;
+    for (int i = tid; i <= B; i += THREADS) {
+        const int q = rg.cu_q[i];
+        const long long k = rg.cu_k[i];
+        sm.pq[i] = q < 0 ? 0 : (q > TQ ? TQ : q);
+        sm.pk[i] = k < 0 ? 0 : (k > rg.total_k ? rg.total_k : k);
+    }
+    for (int i = tid; i < TQ; i += THREADS) sm.own[i] = 0x7fffffff;
+    __syncthreads();
+    if (tid < B)
+        for (int i = sm.pq[tid]; i < sm.pq[tid + 1]; ++i) atomicMin(&sm.own[i], tid);
+    __syncthreads();
+    if (wid == 0) {
+        constexpr int RPL = kSplitPlanRows / 64;  // rows per lane: lane + 64 i
+        uint32_t lr[RPL];
+#pragma unroll
+        for (int i = 0; i < RPL; ++i) {
+            const int row = lane + 64 * i;
+            lr[i] = 0;
+            if (row < TQ && sm.own[row] != 0x7fffffff) {
+                const int b = sm.own[row];
+                const int tb = sm.pq[b + 1] > sm.pq[b] ? sm.pq[b + 1] - sm.pq[b] : 0;
+                const long long sb = sm.pk[b + 1] > sm.pk[b] ? sm.pk[b + 1] - sm.pk[b] : 0;
+                const long long l = sb - tb + (row - sm.pq[b]) + 1;
+                // at most max_k <= PL_MAX * kSplitMaxParts (the host checks)
+                lr[i] = l < 0 ? 0u : (uint32_t)(l < max_k ? l : max_k);
+            }
+        }
+        // parts of row (lane + 64 i) at part length tk: one for a row with no key
+        auto parts = [&](int i, uint32_t tk) {
+            return lane + 64 * i < TQ ? (lr[i] == 0u ? 1u : (lr[i] + tk - 1u) / tk) : 0u;
+        };
+        auto total = [&](uint32_t tk) {
+            uint32_t s = 0;
+#pragma unroll
+            for (int i = 0; i < RPL; ++i) s += parts(i, tk);
+            return wave_total(wave_scan_incl(s, 0u, OpAdd{}));
+        };
+        // at most one round of CUs, and never more parts than blocks (at
+        // PL_MAX there are at most as many parts as blocks)
+        const uint32_t target = gridDim.x < (unsigned)kSplitCUs ? gridDim.x : (uint32_t)kSplitCUs;
+        // Lengths are multiples of 512 keys: whole pairs of 256-key rounds,
+        // as the scoring loop finishes its sub-blocks in pairs.
+        constexpr int NT = PL_MAX / 512;
+        int lo = 1, hi = NT;
+        if (total(512u * NT) > target) lo = NT;
+        while (lo < hi) {
+            const int mid = (lo + hi) / 2;
+            if (total(512u * (uint32_t)mid) <= target) hi = mid;
+            else lo = mid + 1;
+        }
+        const uint32_t tk = 512u * (uint32_t)lo;
+        const uint32_t j = blockIdx.x;
+        uint32_t base = 0;
+        int found = 0;
+#pragma unroll
+        for (int i = 0; i < RPL; ++i) {
+            const uint32_t n = parts(i, tk);
+            const uint32_t incl = wave_scan_incl(n, 0u, OpAdd{});
+            const uint32_t first = base + incl - n;
+            const uint64_t m = wave_ballot(!found && n > 0u && j >= first && j < first + n);
+            if (m && lane == __builtin_ctzll(m)) {
+                const int row = lane + 64 * i;
+                const uint32_t per = (lr[i] + n - 1u) / n;  // <= tk
+                sm.plan_r = row;
+                sm.plan_p = (int)(j - first);
+                sm.plan_n = (int)n;
+                sm.plan_len = (int)((per + 511u) / 512u * 512u);
+                sm.plan_base = (int)first;
+                sm.plan_L = lr[i];
+                sm.plan_k0 = sm.own[row] != 0x7fffffff ? sm.pk[sm.own[row]] : 0;
+            }
+            found |= m != 0;
+            base += wave_total(incl);
+        }
+        if (lane == 0 && !found) sm.plan_r = -1;
+    }
+    __syncthreads();
+    if (sm.plan_r < 0) return false;
+    r = sm.plan_r;
+    p = sm.plan_p;
+    L = sm.plan_L;
+    k0 = sm.plan_k0;
+    nparts = sm.plan_n;
+    plen = sm.plan_len;
+    lbase = sm.plan_base;
+    return true;
+}
+
 // Ragged batches (VARLEN): row r belongs to the stream of rg whose query
 // rows hold it (see StreamGeo); rows of no stream see no keys. Every
 // partition of every row still takes part in the arrival, so the counters
 // return to zero.
-template <bool KFP8, bool VARLEN, int PART>
+template <bool KFP8, bool VARLEN, int PART, bool PLAN = false>
 __global__ __launch_bounds__(THREADS, 1) void split_indexer_kernel(
     const uint16_t *__restrict__ Q, const uint8_t *__restrict__ K, const float *__restrict__ Ks,
     const float *__restrict__ W, int T, int S, long long offset, int topk, int P, int slots, int s1,
@@ -428,18 +535,18 @@ __global__ __launch_bounds__(THREADS, 1) void split_indexer_kernel(
     // dispatch first, spread over the XCDs (consecutive blocks go to
     // consecutive XCDs), and the short ones fill the gaps. Uniform rows keep
     // the plain mapping.
+    static_assert(!PLAN || (VARLEN && PART == PL_MAX), "planned parts are a ragged feature");
     int p;
     long long r;  // query row
-    if constexpr (VARLEN) {
+    long long L, k0;  // keys this row sees; first key row of its stream
+    int nparts = P, plen = PART;  // the row's partitions; this partition's length
+    long long lbase = 0;          // list index of the row's first partition (planned parts)
+    if constexpr (PLAN) {
+        if (!plan_block(sm, rg, S, tid, lane, wid, r, p, L, k0, nparts, plen, lbase)) return;
+    } else if constexpr (VARLEN) {
         const long long i = blockIdx.x + (long long)P * blockIdx.y;
         p = (int)(i / gridDim.y);
         r = i % gridDim.y;
-    } else {
-        p = blockIdx.x;
-        r = blockIdx.y;
-    }
-    long long L, k0;  // keys this row sees; first key row of its stream
-    if constexpr (VARLEN) {
         const int bs = wave_row_stream(rg.cu_q, rg.cu_k, rg.B, rg.total_q, rg.total_k, r, lane);
         L = 0;
         k0 = 0;
@@ -450,13 +557,17 @@ __global__ __launch_bounds__(THREADS, 1) void split_indexer_kernel(
             k0 = g.k0;
         }
     } else {
+        p = blockIdx.x;
+        r = blockIdx.y;
         const int b = (int)(r / T), t = (int)(r % T);
         L = offset + t + 1;
         k0 = (long long)b * S;
     }
     static_assert(PART % (NW * 32 * 4) == 0 && PART <= PL_MAX, "whole rounds, whole ring cycles");
     constexpr int NSUB = PART / (NW * 32);  // 32-key sub-blocks per wavefront
-    const long long pbase = (long long)p * PART;
+    const long long pbase = (long long)p * plen;
+    const long long Lend = PLAN ? (L < pbase + plen ? L : pbase + plen) : L;  // this partition's end
+    const long long lidx = PLAN ? lbase + p : r * P + p;  // this partition's lists
 
     // This wavefront's keys: the partition is read in PART / 256 rounds of
     // 256 consecutive keys, the eight wavefronts taking 32 keys each, and a
@@ -474,16 +585,17 @@ __global__ __launch_bounds__(THREADS, 1) void split_indexer_kernel(
     // that sub-block (cached) rather than skip the load, so that every slot is
     // filled by the same instructions (see load_sub).
     constexpr int RKEYS = NW * 32;           // keys per round
-    constexpr int NROUND = NSUB;             // rounds per partition
+    constexpr int NROUND = NSUB;             // rounds of the longest partition
+    const int nround = PLAN ? plen / RKEYS : NROUND;  // rounds of a full partition
     const long long wbase = pbase + (long long)wid * 32;
-    const bool full_part = L - pbase >= PART;
-    const long long wrem = L - wbase;
-    const int nsub = full_part ? NROUND
+    const bool full_part = Lend - pbase >= plen;
+    const long long wrem = Lend - wbase;
+    const int nsub = full_part ? nround
                      : wrem <= 0 ? 0 : (int)(((wrem + RKEYS - 1) / RKEYS + 1) & ~1LL);  // even: whole pairs
-    const int rot0 = full_part ? p % NROUND : 0;
+    const int rot0 = full_part ? p % nround : 0;
     auto sbase = [&](int sb) {
         const int rr = sb + rot0;
-        return wbase + (long long)(rr >= NROUND ? rr - NROUND : rr) * RKEYS;
+        return wbase + (long long)(rr >= nround ? rr - nround : rr) * RKEYS;
     };
     const uint8_t *Kr = K + (size_t)k0 * (KFP8 ? D : 2 * D);
     const float *Ksr = KFP8 ? Ks + (size_t)k0 : nullptr;
@@ -536,8 +648,8 @@ __global__ __launch_bounds__(THREADS, 1) void split_indexer_kernel(
                         if (KFP8) sc *= lane < 32 ? pscale : buf[i].scale;
                         const long long key = sbase(lane < 32 ? sb - 1 : sb) + (lane & 31);
                         const uint32_t ok = ord_key(canon(sc));
-                        sm.sc[scx((int)(key - pbase))] = key < L ? ok : 0u;
-                        if (key < L && ok != 0u) atomicAdd(&sm.hist[hidx(ok >> HSHIFT)], 1u);
+                        sm.sc[scx((int)(key - pbase))] = key < Lend ? ok : 0u;
+                        if (key < Lend && ok != 0u) atomicAdd(&sm.hist[hidx(ok >> HSHIFT)], 1u);
                     } else {
                         prev = part;
                     }
@@ -560,9 +672,11 @@ __global__ __launch_bounds__(THREADS, 1) void split_indexer_kernel(
     // full partitions of the row (PART keys each) alone hold fullp*m >= k
     // keys. Only nonzero keys are counted: the all-ones NaN pattern maps to
     // key 0, which reads as "no key" everywhere.
-    const uint32_t fullp = (uint32_t)(L / PART);
+    const uint32_t fullp = (uint32_t)(L / plen);
     const uint32_t mth = fullp > 0 ? ((uint32_t)topk + fullp - 1) / fullp : 0u;  // 0: no bound
-    const uint32_t c1 = (uint32_t)(s1 / 4);
+    // c1 = 4m. With planned parts the lists have room for 2k (the largest
+    // m); fixed lengths size them for this m.
+    const uint32_t c1 = PLAN && mth > 0 && 4 * mth < (uint32_t)(s1 / 4) ? 4 * mth : (uint32_t)(s1 / 4);
     uint32_t mykmax = 0, kmax;
 #pragma unroll
     for (int j = 0; j < KPT; ++j) mykmax = u[j] > mykmax ? u[j] : mykmax;
@@ -580,8 +694,8 @@ __global__ __launch_bounds__(THREADS, 1) void split_indexer_kernel(
     const uint32_t edge1 = nkeys < c1 ? 1u : (f1.bin << HSHIFT);
     const uint32_t n1 = nkeys < c1 ? nkeys : f1.above + f1.cnt;
     const bool short_ok = n1 <= (uint32_t)s1;
-    const long long cb = (r * P + p) * (long long)slots;
-    const long long cb1 = (r * P + p) * (long long)s1;
+    const long long cb = lidx * (long long)slots;
+    const long long cb1 = lidx * (long long)s1;
     // This partition's bound, published with the short list's edge, the
     // largest key and the full list's length: the lower edge of its m-th
     // key's bin (m keys at or above it; ~0 = no bound from this partition).
@@ -593,8 +707,8 @@ __global__ __launch_bounds__(THREADS, 1) void split_indexer_kernel(
         if (wid != 0) return;
         const uint32_t tp = has_m ? (fm.bin << HSHIFT) : ~0u;
         if (lane == 0) {
-            store_agent(&meta[2 * (r * P + p)], ((uint64_t)(short_ok ? edge1 : ~0u) << 32) | tp);
-            store_agent(&meta[2 * (r * P + p) + 1], ((uint64_t)nfull << 32) | kmax);
+            store_agent(&meta[2 * lidx], ((uint64_t)(short_ok ? edge1 : ~0u) << 32) | tp);
+            store_agent(&meta[2 * lidx + 1], ((uint64_t)nfull << 32) | kmax);
         }
     };
     const bool direct = F <= (uint32_t)slots;
@@ -674,15 +788,16 @@ __global__ __launch_bounds__(THREADS, 1) void split_indexer_kernel(
     __syncthreads();
     if (tid == 0)
         sm.last = __hip_atomic_fetch_add(&ctr[r], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                  (uint32_t)(P - 1);
+                  (uint32_t)(nparts - 1);
     __syncthreads();
     if (!sm.last) return;
 
     int *io = idx + r * topk;
     float *vo = vals ? vals + r * topk : nullptr;
-    const uint64_t *rs = short_list + r * P * (long long)s1;
-    const uint64_t *rf = full_list + r * P * (long long)slots;
-    const int G1 = P * (s1 / 64), GF = P * (slots / 64);
+    const long long lrow = PLAN ? lbase : r * P;  // list index of the row's first partition
+    const uint64_t *rs = short_list + lrow * s1;
+    const uint64_t *rf = full_list + lrow * slots;
+    const int G1 = nparts * (s1 / 64), GF = nparts * (slots / 64);
 
     // Survivors of the bound from a slot grid (every partition's list padded
     // to `per` slots with empty ones) in slot = index order: 64-slot group g,
@@ -759,9 +874,9 @@ __global__ __launch_bounds__(THREADS, 1) void split_indexer_kernel(
     uint64_t v0[GB];
     load_batch(v0, rs, G1, 0);
     uint32_t tq = ~0u, eq1 = 0u, mq = 0u;
-    for (int q = lane; q < P; q += 64) {
-        const uint64_t a = load_agent(&meta[2 * (r * P + q)]);
-        const uint64_t b = load_agent(&meta[2 * (r * P + q) + 1]);
+    for (int q = lane; q < nparts; q += 64) {
+        const uint64_t a = load_agent(&meta[2 * (lrow + q)]);
+        const uint64_t b = load_agent(&meta[2 * (lrow + q) + 1]);
         const uint32_t t = (uint32_t)a, e1 = (uint32_t)(a >> 32), km = (uint32_t)b;
         tq = t < tq ? t : tq;
         eq1 = e1 > eq1 ? e1 : eq1;
@@ -919,7 +1034,7 @@ __global__ __launch_bounds__(THREADS, 1) void split_indexer_kernel(
         } else {
             // The bound left too many survivors (many equal scores): the same
             // selection over every full-list slot, read from the workspace.
-            const int E = P * slots;
+            const int E = nparts * slots;
             auto valid = [&](int e) { return (uint32_t)(e % slots) < sm.pn[e / slots]; };
             auto each = [&](auto f) {
                 for (int e = tid; e < E; e += THREADS) {
@@ -980,6 +1095,16 @@ hipError_t launch_t(const Problem &p, const SplitShape &sh, const Ragged &rg, co
                            p.offset, k, P, split_slots(k), split_short_slots(sh, k), w.ctr, w.meta, w.full_list,
                            w.short_list, idx, vals, rg);
     };
+    if constexpr (VARLEN) {
+        if (sh.plan) {
+            // One block per planned part; S carries the most keys a row may see.
+            hipLaunchKernelGGL((split_indexer_kernel<KFP8, true, PL_MAX, true>), dim3(sh.plan), dim3(THREADS), 0,
+                               st, static_cast<const uint16_t *>(Q), static_cast<const uint8_t *>(K), Ks, W, 0,
+                               (int)sh.max_len, 0LL, k, sh.plan, split_slots(k), split_short_slots(sh, k), w.ctr,
+                               w.meta, w.full_list, w.short_list, idx, vals, rg);
+            return hipGetLastError();
+        }
+    }
     if (sh.part == kSplitPartLens[2]) go(split_indexer_kernel<KFP8, VARLEN, kSplitPartLens[2]>);
     else if (sh.part == kSplitPartLens[1]) go(split_indexer_kernel<KFP8, VARLEN, kSplitPartLens[1]>);
     else go(split_indexer_kernel<KFP8, VARLEN, kSplitPartLens[0]>);
@@ -1048,6 +1173,15 @@ SplitShape split_shape(const VarlenProblem &p)
     // nonempty partitions number at most total_k / len + B, exactly
     // B ceil(max_k / len) when every stream holds max_k keys; with several
     // queries per stream there is no such bound here.
+    if (split_len_now() == 0 && p.total_q >= 1 && p.total_q <= kSplitPlanRows && p.B <= kSplitPlanRows &&
+        p.max_k <= (long long)PL_MAX * kSplitMaxParts) {
+        // Planned parts. A row seeing L <= max_k keys takes at most
+        // ceil(L / PL_MAX) parts in any plan, so this many blocks suffice;
+        // at least one per CU, so that short rows spread over all of them.
+        const long long need = p.total_q * ((p.max_k + PL_MAX - 1) / PL_MAX);
+        const long long blocks = need > kSplitCUs ? need : kSplitCUs;
+        return SplitShape{p.total_q, p.max_k, p.max_k, PL_MAX, (int)blocks};
+    }
     const int part = pick_part([&](long long l) {
         if (p.total_q != p.B) return (long long)p.total_q * ((p.max_k + l - 1) / l);
         if (p.total_k == (long long)p.B * p.max_k) return (long long)p.B * ((p.max_k + l - 1) / l);
@@ -1062,6 +1196,7 @@ int split_slots(int k) { return (2 * k + 63) / 64 * 64; }
 
 int split_short_slots(const SplitShape &sh, int k)
 {
+    if (sh.plan) return split_slots(k);  // the kernel takes c1 = 4m per row, m up to k
     // Room for the keys from the bin of the c1-th largest up, c1 = 4m (m =
     // ceil(k / full partitions) of the row with the fewest): the kernel takes
     // c1 = slots / 4, so the bin may hold up to 3 c1 further keys.
@@ -1074,24 +1209,30 @@ int split_short_slots(const SplitShape &sh, int k)
 
 static size_t align256(size_t n) { return (n + 255) / 256 * 256; }
 
+// Candidate lists: one per partition of every row, or per planned block.
+static size_t split_lists(const SplitShape &sh)
+{
+    return sh.plan ? (size_t)sh.plan : (size_t)sh.rows * (size_t)split_parts(sh);
+}
+
 size_t split_workspace_bytes(const SplitShape &sh, int k)
 {
-    const size_t rows = (size_t)sh.rows, P = (size_t)split_parts(sh);
-    return align256(rows * 4) + align256(rows * P * 16) + align256(rows * P * (size_t)split_slots(k) * 8) +
-           align256(rows * P * (size_t)split_short_slots(sh, k) * 8);
+    const size_t rows = (size_t)sh.rows, n = split_lists(sh);
+    return align256(rows * 4) + align256(n * 16) + align256(n * (size_t)split_slots(k) * 8) +
+           align256(n * (size_t)split_short_slots(sh, k) * 8);
 }
 
 SplitWorkspace split_workspace(void *ws, const SplitShape &sh, int k)
 {
-    const size_t rows = (size_t)sh.rows, P = (size_t)split_parts(sh);
+    const size_t rows = (size_t)sh.rows, n = split_lists(sh);
     char *c = static_cast<char *>(ws);
     SplitWorkspace w;
     w.ctr = reinterpret_cast<uint32_t *>(c);
     c += align256(rows * 4);
     w.meta = reinterpret_cast<uint64_t *>(c);
-    c += align256(rows * P * 16);
+    c += align256(n * 16);
     w.full_list = reinterpret_cast<uint64_t *>(c);
-    c += align256(rows * P * (size_t)split_slots(k) * 8);
+    c += align256(n * (size_t)split_slots(k) * 8);
     w.short_list = reinterpret_cast<uint64_t *>(c);
     return w;
 }

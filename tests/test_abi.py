@@ -227,18 +227,35 @@ def test_varlen_empty_batch_is_a_no_op():
     assert _vselect(_vprob(total_q=0)) == ds.OK
 
 
+def _a256(n):
+    return (n + 255) // 256 * 256
+
+
 def test_varlen_workspace_matches_uniform_decode():
-    # 8 streams of one query over 262144 keys: the same split-key workspace as
-    # the uniform decode problem, under the automatic and every fixed
-    # partition length
+    # 8 streams of one query over 262144 keys: under every fixed partition
+    # length the same split-key workspace as the uniform decode problem;
+    # under the automatic length the ragged batch takes planned parts, whose
+    # lists are sized per launched block: max(rows * ceil(max_k / 16384), 256)
+    # blocks, each with 2k full-list and 2k short-list slots, plus a counter
+    # per row
     v = _vprob(B=8, total_q=8, total_k=8 * 262144, max_k=262144)
     u = ds.Problem(8, 1, 262144, 64, 128, 262143, ds.BF16, ds.FP8_E4M3)
     prev = ds.set_split(0)
     try:
-        for keys in (0,) + ds.SPLIT_LENS:
+        for keys in ds.SPLIT_LENS:
             ds.set_split(keys)
             assert ds.lib().ds4idx_varlen_workspace_bytes(ctypes.byref(v), 512) == \
                 ds.lib().ds4idx_workspace_bytes(ctypes.byref(u), 512, ds.OP_SELECT)
+        ds.set_split(0)
+        blocks = max(8 * (262144 // 16384), 256)
+        assert ds.lib().ds4idx_varlen_workspace_bytes(ctypes.byref(v), 512) == \
+            _a256(8 * 4) + _a256(blocks * 16) + 2 * _a256(blocks * 1024 * 8)
+        # more rows than a plan takes: fixed-length partitions again
+        w = _vprob(B=300, total_q=300, total_k=300 * 4096, max_k=4096)
+        ds.set_split(8192)
+        fixed = ds.lib().ds4idx_varlen_workspace_bytes(ctypes.byref(w), 512)
+        ds.set_split(0)
+        assert ds.lib().ds4idx_varlen_workspace_bytes(ctypes.byref(w), 512) == fixed
     finally:
         ds.set_split(prev)
 
@@ -265,14 +282,17 @@ def test_split_length_switch_and_automatic_choice():
         assert ds.workspace_bytes(ten, 512) == auto10
         ds.set_split(0)
         # the ragged decode mix: 64 streams of 4096 + 910 b keys (2,096,704 in
-        # all, at most 61426): 2096704 / 8192 + 64 > 256 partitions, so 12288
+        # all, at most 61426). With a fixed length, 2096704 / 8192 + 64 > 256
+        # partitions of 8192 keys: the workspace for 8192 exceeds that for
+        # 12288. The automatic length plans the parts on the device, with
+        # lists for max(64 * ceil(61426 / 16384), 256) = 256 blocks.
         lens = [4096 + 910 * b for b in range(64)]
         v = _vprob(B=64, total_q=64, total_k=sum(lens), max_k=max(lens))
-        autov = ds.varlen_workspace_bytes(v, 512)
+        assert ds.varlen_workspace_bytes(v, 512) == _a256(64 * 4) + _a256(256 * 16) + 2 * _a256(256 * 1024 * 8)
         ds.set_split(12288)
-        assert ds.varlen_workspace_bytes(v, 512) == autov
+        w12 = ds.varlen_workspace_bytes(v, 512)
         ds.set_split(8192)
-        assert ds.varlen_workspace_bytes(v, 512) > autov
+        assert ds.varlen_workspace_bytes(v, 512) > w12
     finally:
         ds.set_split(prev)
 

@@ -255,3 +255,33 @@ def test_ragged_prefill_key_parts_identical(keys):
                 check_against_oracle(rg, gi, gv, exact=(kind == "int"), n=8)
     finally:
         ds.set_prefill_split(prev)
+
+
+PLAN_CASES = [
+    ("110 short streams", [(1, 300 + 37 * b) for b in range(110)], 512, 61),
+    ("one long stream, 50 short", [(1, 1_000_000)] + [(1, 1000 + 13 * b) for b in range(50)], 512, 62),
+    ("k = 2048", [(1, 40000 + 1000 * b) for b in range(24)], 2048, 63),
+    ("several queries per stream", [(5, 9000), (1, 120000), (12, 40000), (1, 513), (0, 10), (3, 3)], 512, 64),
+]
+
+
+@pytest.mark.parametrize("name,mix,topk,seed", PLAN_CASES, ids=[c[0] for c in PLAN_CASES])
+def test_planned_parts_match_fixed_length(name, mix, topk, seed):
+    # With the automatic length a batch of at most 256 rows takes parts
+    # planned on the device (equal parts per row, the shortest length whose
+    # parts start in one round); a fixed length takes the plain partitions.
+    # Both select exactly, so they agree bit for bit; rows against the oracle.
+    rg = W.ragged(seed, mix, topk=topk)
+    assert _route_is_split(rg, topk)
+    dev = _dev(rg)
+    prev = ds.set_split(0)
+    try:
+        _say(f"planned parts: {name}, k={topk}")
+        ai, av = run_varlen(rg, topk=topk, dev=dev)
+        ds.set_split(16384)
+        gi, gv = run_varlen(rg, topk=topk, dev=dev)
+    finally:
+        ds.set_split(prev)
+    assert np.array_equal(ai, gi), f"{name}: indices differ from the fixed length"
+    assert np.array_equal(av.view(np.uint32), gv.view(np.uint32)), f"{name}: values differ"
+    check_against_oracle(rg, ai, av, exact=False, topk=topk, n=4)
