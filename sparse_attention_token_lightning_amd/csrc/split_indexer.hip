@@ -252,17 +252,26 @@ __device__ __forceinline__ uint32_t hist_find(SplitSmem &sm, const uint32_t (&tg
 __device__ __forceinline__ void list_rank(const SplitSmem &sm, uint32_t n, uint32_t r, uint32_t &kth,
                                           uint32_t &gt_out)
 {
+    // Bit by bit from the highest bit in which the keys differ: among the
+    // keys that match the bits chosen so far, those with the next bit set are
+    // the larger; one ballot counts them.
     const int lane = threadIdx.x & 63;
-    const uint32_t mine = lane < (int)n ? sm.lk[lane] : 0u;
-    uint32_t gt = 0, ge = 0;
-    for (uint32_t j = 0; j < n; ++j) {
-        const uint32_t v = (uint32_t)__builtin_amdgcn_readlane((int)mine, (int)j);
-        gt += v > mine ? 1u : 0u;
-        ge += v >= mine ? 1u : 0u;
+    const bool live = lane < (int)n;
+    const uint32_t mine = live ? sm.lk[lane] : 0u;
+    const uint32_t a = wave_and(live ? mine : ~0u), o = wave_or(mine);
+    const uint32_t diff = a ^ o;
+    const int hb = diff ? 31 - __builtin_clz(diff) : -1;
+    const uint32_t low = hb < 0 ? 0u : (hb == 31 ? ~0u : (2u << hb) - 1u);  // bits still open
+    uint32_t prefix = a & ~low, pmask = ~low, rem = r;
+    for (int b = hb; b >= 0; --b) {
+        const uint32_t bit = 1u << b;
+        const uint32_t c = (uint32_t)__builtin_popcountll(wave_ballot(live && (mine & pmask) == prefix && (mine & bit)));
+        if (c >= rem) prefix |= bit;
+        else rem -= c;
+        pmask |= bit;
     }
-    const int src = __builtin_ctzll(wave_ballot(lane < (int)n && gt < r && r <= ge));
-    kth = (uint32_t)__builtin_amdgcn_readlane((int)mine, src);
-    gt_out = (uint32_t)__builtin_amdgcn_readlane((int)gt, src);
+    kth = prefix;
+    gt_out = (uint32_t)__builtin_popcountll(wave_ballot(live && mine > prefix));
 }
 
 // Appends the calling wavefront's keys that satisfy `in` to sm.lk (order
@@ -959,8 +968,7 @@ __global__ __launch_bounds__(THREADS, 1) void split_indexer_kernel(
                     (uint32_t)topk, sm, tau, ties);
             }
         }
-        // Ordered output through LDS (the histogram's words are free now),
-        // then coalesced stores of the whole row.
+        // Ordered output: each thread's kept keys at their places in the row.
         uint32_t ngt = 0, neq = 0;
 #pragma unroll
         for (int j = 0; j < KPT; ++j) {
@@ -971,19 +979,17 @@ __global__ __launch_bounds__(THREADS, 1) void split_indexer_kernel(
         const uint32_t ex = block_excl_scan(ngt | (neq << 16), sm, tot);  // counts < 2^14
         uint32_t eqb = ex >> 16;
         uint32_t pos = (ex & 0xffffu) + (eqb < ties ? eqb : ties);
-        uint2 *stage = reinterpret_cast<uint2 *>(sm.hist);  // k <= DS4IDX_MAX_TOPK pairs fit
+        // Written in place: consecutive threads hold consecutive positions,
+        // so each store instruction covers a short run of the row.
 #pragma unroll
         for (int j = 0; j < KPT; ++j) {
             bool keep = kk[j] > tau;
             if (kk[j] != 0u && kk[j] == tau) keep = eqb++ < ties;
-            if (keep) stage[pos++] = make_uint2((uint32_t)sm.sv.idx[KPT * tid + j], kk[j]);
-        }
-        __syncthreads();
-        const uint32_t nsel = total < (uint32_t)topk ? total : (uint32_t)topk;
-        for (int j = tid; j < (int)nsel; j += THREADS) {
-            const uint2 e = stage[j];
-            io[j] = (int)e.x;
-            if (vo) vo[j] = key_float(e.y);
+            if (keep) {
+                io[pos] = sm.sv.idx[KPT * tid + j];
+                if (vo) vo[pos] = key_float(kk[j]);
+                ++pos;
+            }
         }
         m_out = total < (uint32_t)topk ? total : (uint32_t)topk;
     } else {
