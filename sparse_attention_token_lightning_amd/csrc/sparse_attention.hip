@@ -215,11 +215,14 @@ __global__ __launch_bounds__(ATHREADS, 1) void sparse_attention_kernel(
     };
     // Q^T fragments of head tile ht: head h0 + 16 ht + lane % 16, dims 32 ks + 8 (lane / 16) ..
     bf16x8 qf[NQK];
-    auto load_q = [&](const ItemPos &q) {
+    auto q_ptr = [&](const ItemPos &q) {
         const uint16_t *qb = Q + (q.row * H + q.tile * AH + ht * 16) * DQK;
         int l = lane;
         asm volatile("" : "+v"(l));
-        const bf16x8 *qp = reinterpret_cast<const bf16x8 *>(qb + ((l & 15) * DQK + (l >> 4) * 8));
+        return reinterpret_cast<const bf16x8 *>(qb + ((l & 15) * DQK + (l >> 4) * 8));
+    };
+    auto load_q = [&](const ItemPos &q) {
+        const bf16x8 *qp = q_ptr(q);
 #pragma unroll
         for (int ks = 0; ks < NQK; ++ks) qf[ks] = qp[ks * 4];
     };
@@ -330,10 +333,16 @@ __global__ __launch_bounds__(ATHREADS, 1) void sparse_attention_kernel(
                                    : tr[(4 * (ks - 16) + q) ^ (r & 7)];
                 };
                 uint4 v0 = frag(0), v1 = frag(1), v2 = frag(2);
+                // In an item's last chunk, when the ring runs on, each Q
+                // fragment of the next item is loaded as soon as the MFMA that
+                // used this item's has been issued.
+                const bool nextq = c == nchunk - 1 && carry;
+                const bf16x8 *qn = q_ptr(np);
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int ks = 0; ks < NQK; ++ks) {
                     s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v0), qf[ks], s, 0, 0, 0);
+                    if (nextq) qf[ks] = qn[ks * 4];
                     v0 = v1;
                     v1 = v2;
                     if (ks + 3 < NQK) v2 = frag(ks + 3);
@@ -375,7 +384,9 @@ __global__ __launch_bounds__(ATHREADS, 1) void sparse_attention_kernel(
             }
             *reinterpret_cast<uint2 *>(&sm.p[pb][ht][lane][kt * 4]) =
                 make_uint2(pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]));
-            if (!fresh || c >= 2) {
+            if (c == nchunk - 1 && carry) {
+                wait_vm<5 + NQK>();  // the next item's Q loads were issued after chunk g + 2's gathers
+            } else if (!fresh || c >= 2) {
                 if (c + 2 < nchunk || carry) wait_vm<5>();
                 else wait_vm<0>();
             }
@@ -392,10 +403,9 @@ __global__ __launch_bounds__(ATHREADS, 1) void sparse_attention_kernel(
                 }
             }
             if (c == nchunk - 1 && carry) {
-                // The scores of this item are done: the next item's Q and the
-                // row indices of the one after it are loaded now, waited for
-                // at the end of the item.
-                load_q(np);
+                // The row indices of the item after next are loaded now, and
+                // they and the next item's Q (loaded during the scores) are
+                // waited for at the end of the item.
 #pragma unroll
                 for (int j = 0; j < 4; ++j) cur[j] = nxt[j];
                 load_sel(n + 2 < end ? advance(np).row : np.row, nxt);
