@@ -28,7 +28,9 @@ prefill (2048 queries after 1,046,528 cached E4M3 keys).
 Before each timed 64k step a 512 MB buffer is written so the step starts
 with a cold last-level cache (--no-flush to skip). Also reported: measured
 ceilings in plain torch (HBM reads of 277 MB rotated over three copies by a sum
-and by a library GEMV, a 277 MB device copy, an 8192^3 bf16 matmul), and the CPU oracle timed per workload with the host's
+and by a library GEMV, a 277 MB device copy, an 8192^3 bf16 matmul) and from
+the probe library's two kernels (a grid-stride read of the same bytes, an
+MFMA-only loop), and the CPU oracle timed per workload with the host's
 core count, CPU model and a one-thread rate.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
@@ -50,8 +52,8 @@ HBM_PEAK_GBS = 8000.0
 def _parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=5)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--decode-iters", type=int, default=60)
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
@@ -245,6 +247,7 @@ def main():
     # is bracketed by synchronisations and timed on the host clock.
     flush = None if args.no_flush else torch.empty(512 << 20, dtype=torch.uint8, device=dev)
     elapsed = 0.0
+    step_ms = []
     for s in range(args.steps):
         if flush is not None:
             flush.fill_(s & 0xff)
@@ -252,8 +255,11 @@ def main():
         t_start = time.perf_counter()
         step(events[s])
         torch.cuda.synchronize()
-        elapsed += time.perf_counter() - t_start
+        dt = time.perf_counter() - t_start
+        elapsed += dt
+        step_ms.append(dt * 1e3)
     del flush
+    step_ms.sort()
     launch_ms = [ev[0].elapsed_time(ev[1]) for st in events for ev in st]
     ms_per_step = elapsed * 1e3 / args.steps
     value = wl.T * args.steps / elapsed
@@ -280,7 +286,8 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    extra = {"kernel_ms_per_step": round(sum(launch_ms) / args.steps, 3),
+    extra = {"step_ms_median": round(step_ms[len(step_ms) // 2], 3), "step_ms_min": round(step_ms[0], 3),
+             "kernel_ms_per_step": round(sum(launch_ms) / args.steps, 3),
              "bf16_tflops_step_wall": round(flops / (ms_per_step * 1e-3) / 1e12, 1)}
 
     # ---------------------------------------------------------------- fp8 x fp8 prefill
@@ -536,6 +543,39 @@ def main():
 
         cus_ = _time_calls(cstep, 30, stream, args.warm_ms)
         cmed = cus_[len(cus_) // 2]
+        # The probe library's kernels: a plain grid-stride read of the same
+        # rotated bytes (256 x 512 threads, four 16-byte loads in flight per
+        # lane) and back-to-back 32x32x16 bf16 MFMAs (four chains per
+        # wavefront, two wavefronts per SIMD).
+        probe = None
+        plib = os.path.join(os.path.dirname(CSRC), "libds4probe.so")
+        if os.path.exists(plib):
+            import ctypes
+            probe = ctypes.CDLL(plib)
+            probe.ds4probe_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_longlong, ctypes.c_void_p, ctypes.c_int,
+                                                ctypes.c_void_p]
+            probe.ds4probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+            sink = torch.empty(256 * 512, dtype=torch.int32, device=dev)
+            sst = ctypes.c_void_p(stream.cuda_stream)
+
+            def pstep(i):
+                st = probe.ds4probe_hbm_read(bufs[i % 3].data_ptr(), nbytes, sink.data_ptr(), 256, sst)
+                assert st == 0, st
+
+            pus = _time_calls(pstep, 30, stream, args.warm_ms)
+            pmed = pus[len(pus) // 2]
+            cus_n = torch.cuda.get_device_properties(dev).multi_processor_count
+            msink = torch.empty(2 * cus_n * 256, dtype=torch.float32, device=dev)
+            iters = 8192
+
+            def mfstep(i):
+                st = probe.ds4probe_mfma(iters, 2 * cus_n, msink.data_ptr(), sst)
+                assert st == 0, st
+
+            mfus = _time_calls(mfstep, 10, stream, args.warm_ms)
+            mfmed = mfus[len(mfus) // 2]
+            mflop = 2 * cus_n * 4 * iters * 4 * 32768
+            del sink, msink
         del bufs, mats, vec, res, dst
         n = 8192
         ma = torch.randn((n, n), dtype=torch.bfloat16, device=dev)
@@ -558,6 +598,15 @@ def main():
                                       "3 copies", **rate(gbytes, gmed)},
             "hbm_copy": {"what": "torch copy_ of 276,989,952 B (read + write, counted twice)",
                          **rate(2 * nbytes, cmed)},
+            **({"probe_hbm_read": {"what": "probe kernel: grid-stride read of 276,989,952 B, rotated over 3 copies, "
+                                           "256 x 512 threads, four 16-byte loads in flight per lane",
+                                   **rate(nbytes, pmed)},
+                "probe_mfma_bf16": {"what": "probe kernel: v_mfma_f32_32x32x16_bf16, four chains per wavefront, "
+                                            "two wavefronts per SIMD, register operands",
+                                    "us_median": round(mfmed, 2),
+                                    "tflops": round(mflop / (mfmed * 1e-6) / 1e12, 1),
+                                    "frac_of_peak": round(mflop / (mfmed * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4)}}
+               if probe is not None else {}),
             "bf16_matmul": {"what": "torch.matmul 8192 x 8192 x 8192 bf16",
                             "us_median": round(mmed, 2),
                             "tflops": round(2 * n ** 3 / (mmed * 1e-6) / 1e12, 1),

@@ -1,4 +1,5 @@
-"""Build libds4idx.so (the C-ABI library) in-tree with hipcc for gfx950.
+"""Build libds4idx.so (the C-ABI library) in-tree with hipcc for gfx950, and
+libds4probe.so (the benchmark's ceiling probes, outside that ABI).
 
     python -m sparse_attention_token_lightning_amd.build
 """
@@ -14,12 +15,14 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libds4idx.so")
+PROBE_LIB = os.path.join(PKG, "libds4probe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "ref_kernels.hip", "mfma_indexer.hip", "split_indexer.hip", "k_cache_writer.hip",
            "sparse_attention.hip"]
 HEADERS = ["kernels.h", "device_common.h"]
+PROBE_SOURCES = ["probes.hip"]
 
 # Packed fp32 VALU forms are kept out of generated code on this target.
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
@@ -36,18 +39,23 @@ def _compile(src: str) -> str:
     return out
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(OBJ, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(OBJ, exist_ok=True)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES) + len(PROBE_SOURCES)) as ex:
+        objs = list(ex.map(_compile, SOURCES + PROBE_SOURCES))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], PROBE_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBE_LIB}")
     return LIB
 
 

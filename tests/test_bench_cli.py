@@ -63,3 +63,18 @@ def test_digest_ignores_comments_and_layout_only():
     assert bench._code_only(src) == bench._code_only(same)
     assert bench._code_only(src) != bench._code_only(changed)
     assert bench._code_only(src) != bench._code_only(literal)   # inside a literal, text counts
+
+
+def test_probe_library_exports_its_two_kernels():
+    # the ceiling probes bench.py times live in their own library, outside
+    # the indexer's C ABI
+    import ctypes
+    path = os.path.join(ROOT, "sparse_attention_token_lightning_amd", "libds4probe.so")
+    assert os.path.exists(path), "built by __graft_entry__.build()"
+    lib = ctypes.CDLL(path)
+    assert hasattr(lib, "ds4probe_hbm_read") and hasattr(lib, "ds4probe_mfma")
+    # argument checks come before any HIP call
+    lib.ds4probe_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_longlong, ctypes.c_void_p, ctypes.c_int,
+                                      ctypes.c_void_p]
+    assert lib.ds4probe_hbm_read(ctypes.c_void_p(0x1000), 24, ctypes.c_void_p(0x2000), 1, None) != 0  # not x16
+    assert lib.ds4probe_hbm_read(None, 32, ctypes.c_void_p(0x2000), 1, None) != 0
