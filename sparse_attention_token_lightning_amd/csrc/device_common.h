@@ -86,6 +86,44 @@ __device__ __forceinline__ void wave_lds_sync()
     __builtin_amdgcn_wave_barrier();
 }
 
+// LDS byte address of a __shared__ object.
+__device__ __forceinline__ uint32_t lds_addr(const void *p)
+{
+    return (uint32_t)(size_t)(const __attribute__((address_space(3))) void *)p;
+}
+
+// One 16-byte load per lane straight into LDS (global_load_lds_dwordx4) from
+// a wavefront-uniform base in scalar registers plus a 32-bit per-lane byte
+// offset: lane i's bytes land at LDS address lds + 16 i (lds wavefront-
+// uniform, carried in M0). Issued as inline assembly so that the compiler
+// does not treat it as an LDS store that it must drain (vmcnt(0)) before every
+// later LDS read; the caller awaits completion with wait_vm, counting these
+// loads itself.
+__device__ __forceinline__ void gather16_at(const void *base, uint32_t off, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds) : "memory", "m0");
+}
+
+// A pointer that is the same in every lane, moved to scalar registers (the
+// base operand of gather16_at).
+template <class T>
+__device__ __forceinline__ const T *uniform_ptr(const T *p)
+{
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+    return reinterpret_cast<const T *>(((uint64_t)hi << 32) | lo);
+}
+
+// Wait until at most N of this wavefront's vector-memory operations are
+// outstanding (expcnt and lgkmcnt left free).
+template <int N>
+__device__ __forceinline__ void wait_vm()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
 // Exact OCP E4M3FN decode by bit fields (sign, exponent bias 7, 3-bit
 // mantissa, exponent 0 subnormal, S.1111.111 NaN). Used by the plain kernels.
 __device__ __forceinline__ float e4m3_value(uint32_t c)

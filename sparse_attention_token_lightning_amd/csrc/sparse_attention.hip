@@ -101,22 +101,13 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 // with wait_vm, and no other vector-memory instruction runs in the main
 // loop. M0 carries the (wavefront-uniform) LDS address; this kernel uses M0
 // for nothing else.
-__device__ __forceinline__ uint32_t lds_addr(const void *p)
-{
-    return (uint32_t)(size_t)(const __attribute__((address_space(3))) void *)p;
-}
-
 __device__ __forceinline__ void gather16(const void *src, uint32_t lds)
 {
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory", "m0");
 }
 
-// The same from a wavefront-uniform base (scalar registers) plus a 32-bit
-// per-lane byte offset: no per-lane 64-bit address arithmetic.
-__device__ __forceinline__ void gather16_at(const void *base, uint32_t off, uint32_t lds)
-{
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds) : "memory", "m0");
-}
+// gather16_at (shared device helpers) does the same from a wavefront-uniform
+// base plus a 32-bit per-lane offset: no per-lane 64-bit address arithmetic.
 
 // Max / sum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (one head of a
 // 16 x 16 accumulator tile) with the permlane swaps, VALU only.
@@ -134,15 +125,6 @@ __device__ __forceinline__ float quad_sum(float x)
     x = __uint_as_float(w[0]) + __uint_as_float(w[1]);
     w = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return __uint_as_float(w[0]) + __uint_as_float(w[1]);
-}
-
-// Wait until at most N of this wavefront's vector-memory operations are
-// outstanding (expcnt and lgkmcnt left free).
-template <int N>
-__device__ __forceinline__ void wait_vm()
-{
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 
 // Where an item (query row, head tile) is: uniform values that step from

@@ -80,13 +80,26 @@ typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 
 constexpr int QROW = D + 8;  // bf16 per LDS query row: 272 B keeps 16-byte reads conflict-free
 
+// The scoring area of the LDS, for partitions of PART keys: the partition's
+// score keys (sc_words words, at scx(i)), then for E4M3 keys each
+// wavefront's ring of RING_SLOTS key sub-blocks (32 keys x 128 B, RING16
+// 16-byte pieces each) and its two pair-scale slots (64 floats each), or for
+// bf16 keys the row's query (H rows of QROW bf16). Two slots, one sub-block
+// in flight while the other is scored, streamed the 8 x 262144-key decode as
+// fast as three (61.6-64.2 against 63.6-64.3 us per call).
+constexpr int RING16 = 256;
+constexpr int RING_SLOTS = 2;
+__host__ __device__ constexpr int sc_words(int part) { return part + part / 16; }
+constexpr int RING_BYTES = NW * RING_SLOTS * RING16 * 16;
+constexpr int PSCALE_BYTES = NW * 2 * 64 * 4;
+__host__ __device__ constexpr int e4m3_area(int part) { return sc_words(part) * 4 + RING_BYTES + PSCALE_BYTES; }
+__host__ __device__ constexpr int imax(int a, int b) { return a > b ? a : b; }
+constexpr int SCORE_BYTES = imax(imax(e4m3_area(8192), e4m3_area(12288)),
+                                 imax(e4m3_area(16384), sc_words(PL_MAX) * 4 + H * QROW * 2));
+
 struct SplitSmem {
     union {
-        struct {
-            uint32_t sc[PL_MAX + PL_MAX / 16];  // partition score keys (0 = no key) at scx(i)
-            uint16_t q[H * QROW];           // the row's query, head-major (scoring only)
-            float wl[H];                    // the row's head weights (scoring only)
-        };
+        alignas(16) uint8_t area[SCORE_BYTES];  // scoring (see above)
         struct {
             uint32_t key[MSURV + MSURV / 16];  // merge survivors, index order (direct path: at scx)
             int idx[MSURV];
@@ -95,7 +108,14 @@ struct SplitSmem {
             uint64_t full[MAX_SLOTS];    // partition lists, compacted before
             uint64_t shortl[MAX_SLOTS];  // coalesced stores
         } st;
+        struct {
+            // the planned partitioning of a ragged batch (plan_block only)
+            long long pk[kSplitPlanRows + 1];  // clamped key prefix sums
+            int pq[kSplitPlanRows + 1];        // clamped query prefix sums
+            int own[kSplitPlanRows];           // the stream of each query row
+        } pl;
     };
+    float wl[H];                     // the row's head weights (scoring only)
     alignas(8) uint32_t hist[HWORDS];  // also the merge's output staging (k pairs)
     uint32_t lk[NLIST];              // keys of one bin, for exact ranking
     uint32_t gcnt[NW * GB];          // merge: survivors per 64-slot group
@@ -108,11 +128,7 @@ struct SplitSmem {
     uint32_t nl;
     uint32_t pn[kSplitMaxParts];      // merge: full-list length per partition
     int last;
-    // the planned partitioning of a ragged batch (see plan_block)
-    long long pk[kSplitPlanRows + 1];  // clamped key prefix sums
-    int pq[kSplitPlanRows + 1];        // clamped query prefix sums
-    int own[kSplitPlanRows];           // the stream of each query row
-    long long plan_k0, plan_L;
+    long long plan_k0, plan_L;        // plan_block's result for this block
     int plan_r, plan_p, plan_n, plan_len, plan_base;
 };
 
@@ -358,32 +374,48 @@ __device__ __forceinline__ void block_kth(Each each, uint32_t k, SplitSmem &sm, 
     }
 }
 
-// This lane's half of one key row of a 32-key sub-block (key = base + lane%32,
-// dims half*64 .. +63): 64 bytes of E4M3 codes or 128 bytes of bf16, and for
-// E4M3 keys the scale of key base + lane%32.
+// One 32-key sub-block of a wavefront in the MFMA layout: lane l holds key
+// base + l%32, dims (l/32)*64 .. +63 (64 bytes of E4M3 codes or 128 bytes of
+// bf16).
 template <bool KFP8>
 struct Raw {
     uint4 v[KFP8 ? 4 : 8];
-    float scale;
 };
 
-// Every lane loads, whatever its key: keys at or past L read row L - 1
-// instead (L >= 1 wherever this is called), and their scores are dropped
-// when stored. With no branch around the loads, every ring slot is filled
-// by the same number of load instructions, so the compiler's wait counts
-// before a slot is read stay exact instead of draining all loads in flight.
-template <bool KFP8>
-__device__ __forceinline__ void load_sub(Raw<KFP8> &r, const uint8_t *Kr, const float *Ksr,
-                                         long long kbase, long long L, int lane)
+// bf16 keys go HBM -> VGPRs in the MFMA layout. Every lane loads, whatever
+// its key: keys at or past L read row L - 1 instead (L >= 1 wherever this is
+// called), and their scores are dropped when stored. With no branch around
+// the loads, every ring slot is filled by the same number of load
+// instructions, so the compiler's wait counts before a slot is read stay
+// exact instead of draining all loads in flight.
+__device__ __forceinline__ void load_sub_bf16(Raw<false> &r, const uint8_t *Kr, long long kbase, long long L,
+                                              int lane)
 {
-    constexpr int NV = KFP8 ? 4 : 8;
-    constexpr int ROWB = KFP8 ? D : 2 * D;
     const long long key = kbase + (lane & 31);
     const long long kc = key < L ? key : L - 1;
-    const uint4 *src = reinterpret_cast<const uint4 *>(Kr + kc * ROWB + (lane >> 5) * (ROWB / 2));
+    const uint4 *src = reinterpret_cast<const uint4 *>(Kr + kc * 2 * D + (lane >> 5) * D);
 #pragma unroll
-    for (int j = 0; j < NV; ++j) r.v[j] = src[j];
-    if (KFP8) r.scale = Ksr[kc];
+    for (int j = 0; j < 8; ++j) r.v[j] = src[j];
+}
+
+// E4M3 keys go HBM -> LDS (global_load_lds_dwordx4) into a ring of 4 KB slots
+// per wavefront, coalesced: instruction i moves keys base + 8i .. +7 whole,
+// each 8 lanes one 128-byte row. In the MFMA layout, where every instruction
+// touches 32 B of each of 32 rows, the same bytes stream ~8% slower. Key n's
+// 16-byte piece p sits at slot piece 8n + (p ^ ring_swz(n)), ring_swz(n) =
+// (n & 7) ^ ((n >> 3) & 1): lane l of instruction i (key n = 8i + l/8) lands
+// at piece 8n + l%8, so it loads piece (l%8) ^ ring_swz(n); the fragment
+// reads (one piece of each of 8 keys per 8 lanes) then hit eight distinct
+// 16-byte positions mod 128 bytes in every 8 consecutive lanes, and 16
+// distinct ones mod 256 bytes in every 16.
+__device__ __forceinline__ int ring_swz(int n) { return (n & 7) ^ ((n >> 3) & 1); }
+
+// One 4-byte word per lane straight into LDS (global_load_lds_dword: lane i's
+// word lands at lds + 4 i), from a wavefront-uniform base plus a 32-bit
+// per-lane byte offset; awaited like gather16_at.
+__device__ __forceinline__ void gather4_at(const void *base, uint32_t off, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(off), "s"(base), "s"(lds) : "memory", "m0");
 }
 
 // B operand of k-step ks: dims half*64 + ks*8 .. +7 of the lane's half row.
@@ -401,7 +433,22 @@ __device__ __forceinline__ bf16x8 b_operand(const Raw<KFP8> &r, int ks)
     }
 }
 
-// Partial score of one sub-block: this lane's 16 head rows of each head block.
+// The head-weighted ReLU sum of one sub-block's two 32-head accumulators:
+// this lane's 16 head rows of each head block.
+__device__ __forceinline__ float head_sum(const f32x16 (&acc)[2], const float *wl, int lane)
+{
+    float s4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            s4[i & 3] = fmaf(wl[hb * 32 + acc_row(i, lane)], __builtin_amdgcn_fmed3f(acc[hb][i], 0.0f, 3.0e38f),
+                             s4[i & 3]);
+    return (s4[0] + s4[1]) + (s4[2] + s4[3]);
+}
+
+// Partial score of one sub-block with the query's A operands read from LDS
+// (qa: head lane % 32, dims (lane / 32) * 64, rows QROW apart).
 template <bool KFP8>
 __device__ __forceinline__ float score_sub(const Raw<KFP8> &r, const uint16_t *qa, const float *wl, int lane)
 {
@@ -414,14 +461,21 @@ __device__ __forceinline__ float score_sub(const Raw<KFP8> &r, const uint16_t *q
             acc[hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                 *reinterpret_cast<const bf16x8 *>(qa + hb * 32 * QROW + ks * 8), bk, acc[hb], 0, 0, 0);
     }
-    float s4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    return head_sum(acc, wl, lane);
+}
+
+// The same with the A operands in registers: qf[hb][ks] = head hb * 32 +
+// lane % 32, dims (lane / 32) * 64 + ks * 8 .. +7.
+__device__ __forceinline__ float score_sub_q(const Raw<true> &r, const bf16x8 (&qf)[2][8], const float *wl, int lane)
+{
+    f32x16 acc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb)
+    for (int ks = 0; ks < 8; ++ks) {
+        const bf16x8 bk = b_operand<true>(r, ks);
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-            s4[i & 3] = fmaf(wl[hb * 32 + acc_row(i, lane)], __builtin_amdgcn_fmed3f(acc[hb][i], 0.0f, 3.0e38f),
-                             s4[i & 3]);
-    return (s4[0] + s4[1]) + (s4[2] + s4[3]);
+        for (int hb = 0; hb < 2; ++hb) acc[hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[hb][ks], bk, acc[hb], 0, 0, 0);
+    }
+    return head_sum(acc, wl, lane);
 }
 
 // Planned partitions for a ragged batch of at most kSplitPlanRows query rows
@@ -440,13 +494,13 @@ __device__ bool plan_block(SplitSmem &sm, const Ragged &rg, int max_k, int tid, 
     for (int i = tid; i <= B; i += THREADS) {
         const int q = rg.cu_q[i];
         const long long k = rg.cu_k[i];
-        sm.pq[i] = q < 0 ? 0 : (q > TQ ? TQ : q);
-        sm.pk[i] = k < 0 ? 0 : (k > rg.total_k ? rg.total_k : k);
+        sm.pl.pq[i] = q < 0 ? 0 : (q > TQ ? TQ : q);
+        sm.pl.pk[i] = k < 0 ? 0 : (k > rg.total_k ? rg.total_k : k);
     }
-    for (int i = tid; i < TQ; i += THREADS) sm.own[i] = 0x7fffffff;
+    for (int i = tid; i < TQ; i += THREADS) sm.pl.own[i] = 0x7fffffff;
     __syncthreads();
     if (tid < B)
-        for (int i = sm.pq[tid]; i < sm.pq[tid + 1]; ++i) atomicMin(&sm.own[i], tid);
+        for (int i = sm.pl.pq[tid]; i < sm.pl.pq[tid + 1]; ++i) atomicMin(&sm.pl.own[i], tid);
     __syncthreads();
     if (wid == 0) {
         constexpr int RPL = kSplitPlanRows / 64;  // rows per lane: lane + 64 i
@@ -455,11 +509,11 @@ __device__ bool plan_block(SplitSmem &sm, const Ragged &rg, int max_k, int tid, 
         for (int i = 0; i < RPL; ++i) {
             const int row = lane + 64 * i;
             lr[i] = 0;
-            if (row < TQ && sm.own[row] != 0x7fffffff) {
-                const int b = sm.own[row];
-                const int tb = sm.pq[b + 1] > sm.pq[b] ? sm.pq[b + 1] - sm.pq[b] : 0;
-                const long long sb = sm.pk[b + 1] > sm.pk[b] ? sm.pk[b + 1] - sm.pk[b] : 0;
-                const long long l = sb - tb + (row - sm.pq[b]) + 1;
+            if (row < TQ && sm.pl.own[row] != 0x7fffffff) {
+                const int b = sm.pl.own[row];
+                const int tb = sm.pl.pq[b + 1] > sm.pl.pq[b] ? sm.pl.pq[b + 1] - sm.pl.pq[b] : 0;
+                const long long sb = sm.pl.pk[b + 1] > sm.pl.pk[b] ? sm.pl.pk[b + 1] - sm.pl.pk[b] : 0;
+                const long long l = sb - tb + (row - sm.pl.pq[b]) + 1;
                 // at most max_k <= PL_MAX * kSplitMaxParts (the host checks)
                 lr[i] = l < 0 ? 0u : (uint32_t)(l < max_k ? l : max_k);
             }
@@ -506,7 +560,7 @@ __device__ bool plan_block(SplitSmem &sm, const Ragged &rg, int max_k, int tid, 
                 sm.plan_len = (int)((per + 511u) / 512u * 512u);
                 sm.plan_base = (int)first;
                 sm.plan_L = lr[i];
-                sm.plan_k0 = sm.own[row] != 0x7fffffff ? sm.pk[sm.own[row]] : 0;
+                sm.plan_k0 = sm.pl.own[row] != 0x7fffffff ? sm.pl.pk[sm.pl.own[row]] : 0;
             }
             found |= m != 0;
             base += wave_total(incl);
@@ -588,11 +642,9 @@ __global__ __launch_bounds__(THREADS, 1) void split_indexer_kernel(
     // (and a wavefront owning 128 KB of its partition was as slow as the
     // latter). Sub-block sb of the wavefront covers keys
     // pbase + rot(sb) * 256 + wid * 32 .. +31; pairs (2j, 2j+1) share one half
-    // swap. The first ring slots are loaded before the query staging below,
-    // so the key stream starts at once. A ring of NBUF raw sub-blocks keeps
-    // NBUF-1 loads in flight. Slots past the wave's last sub-block reload
-    // that sub-block (cached) rather than skip the load, so that every slot is
-    // filled by the same instructions (see load_sub).
+    // swap. Slots past the wave's last sub-block reload that sub-block
+    // (cached) rather than skip the load, so that every iteration issues the
+    // same loads and the wait counts stay exact.
     constexpr int RKEYS = NW * 32;           // keys per round
     constexpr int NROUND = NSUB;             // rounds of the longest partition
     const int nround = PLAN ? plen / RKEYS : NROUND;  // rounds of a full partition
@@ -606,75 +658,172 @@ __global__ __launch_bounds__(THREADS, 1) void split_indexer_kernel(
         const int rr = sb + rot0;
         return wbase + (long long)(rr >= nround ? rr - nround : rr) * RKEYS;
     };
-    const uint8_t *Kr = K + (size_t)k0 * (KFP8 ? D : 2 * D);
-    const float *Ksr = KFP8 ? Ks + (size_t)k0 : nullptr;
-    constexpr int NBUF = KFP8 ? 4 : 2;
-    Raw<KFP8> buf[NBUF];
-    if (nsub > 0) {
-#pragma unroll
-        for (int i = 0; i < NBUF - 1; ++i) load_sub<KFP8>(buf[i], Kr, Ksr, sbase(i < nsub ? i : nsub - 1), L, lane);
-    }
+    uint32_t *const sc = reinterpret_cast<uint32_t *>(sm.area);  // score keys at scx(key - pbase)
+    // A finished pair: lanes 0..31 hold sub-block sb - 1's scores, lanes
+    // 32..63 sub-block sb's; score key, LDS word and histogram count.
+    auto store_pair = [&](int sb, float s) {
+        const long long key = sbase(lane < 32 ? sb - 1 : sb) + (lane & 31);
+        const uint32_t ok = ord_key(canon(s));
+        sc[scx((int)(key - pbase))] = key < Lend ? ok : 0u;
+        if (key < Lend && ok != 0u) atomicAdd(&sm.hist[hidx(ok >> HSHIFT)], 1u);
+    };
 
     for (int i = tid; i < HWORDS; i += THREADS) sm.hist[i] = 0;
     if (tid == 0) sm.nl = 0;
-    // The row's query (H x D bf16, 16 KB) into LDS: thread t copies two
-    // 16-byte pieces, 16 per head row.
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int piece = tid + THREADS * j;  // 0 .. H * D / 8 - 1
-        const int h = piece >> 4, d8 = piece & 15;
-        *reinterpret_cast<uint4 *>(&sm.q[h * QROW + d8 * 8]) =
-            *reinterpret_cast<const uint4 *>(Q + (r * H + h) * D + d8 * 8);
-    }
-    if (tid < H) sm.wl[tid] = W[r * H + tid];
-    __syncthreads();
 
-    // ---- score this wavefront's 1024 keys into sm.sc and the histogram
-    if (nsub > 0) {
-        // A operands: head hb * 32 + lane % 32, dims (lane / 32) * 64 + ks * 8.
-        const uint16_t *qa = &sm.q[(lane & 31) * QROW + (lane >> 5) * 64];
-        float prev = 0.0f, pscale = 1.0f;
-        // Unrolled over the wave's NSUB sub-blocks, fully for E4M3 keys
-        // (bf16 keys' larger sub-blocks exceed the unroller's limit): with no
-        // loop back-edge the compiler counts the loads in flight exactly.
+    if constexpr (KFP8) {
+        // ---- E4M3 keys: a ring of NBL 4 KB LDS slots per wavefront (see
+        // ring_swz), NBL - 1 sub-blocks in flight while one is scored, and
+        // with each even sub-block the scales of its pair (two 128-byte
+        // pieces, one global_load_lds_dword) into one of two pair slots, laid
+        // out so that lane l reads the scale of the key whose score it
+        // finishes. The query's A operands live in registers. Every load in
+        // the loop is a gather into LDS awaited with explicit counts.
+        // Refilling a slot as soon as its fragments are in registers (with
+        // three slots: three sub-blocks in flight during the MFMAs) was
+        // slower, 70 against 64 us for the 8 x 262144-key decode: the extra
+        // requests in flight served the eight XCDs very unevenly (their
+        // blocks finished 45.6 to 55.8 us into the kernel).
+        constexpr int NBL = RING_SLOTS;
+        static_assert(e4m3_area(PART) <= SCORE_BYTES, "scoring area");
+        static_assert(H == 64 && H * D * 2 == 2 * THREADS * 16, "weights: one word per lane; query: two pieces per thread");
+        uint8_t *const rbytes = sm.area + sc_words(PART) * 4;
+        const uint32_t ring0 = __builtin_amdgcn_readfirstlane(lds_addr(rbytes + wid * NBL * RING16 * 16));
+        const float *const pscl = reinterpret_cast<const float *>(rbytes + RING_BYTES) + wid * 128;
+        const uint32_t psc0 = __builtin_amdgcn_readfirstlane(lds_addr(pscl));
+        const uint8_t *const Kp = uniform_ptr(K + (size_t)(k0 + pbase) * D);  // this partition's first key row
+        const float *const Ksp = uniform_ptr(Ks + (size_t)(k0 + pbase));
+        // Offsets are relative to pbase; keys at or past L read row L - 1.
+        const int lim = (int)(L - 1 - pbase < (long long)PART + RKEYS ? L - 1 - pbase : (long long)PART + RKEYS);
+        const uint32_t pc = (uint32_t)(((lane & 7) ^ (lane >> 3)) << 4);  // piece of instruction 0; ^16 for odd ones
+        auto issue = [&](int t) {  // sub-block t (clamped to the last), and with an even t its pair's scales
+            const int kb = (int)(sbase(t < nsub ? t : nsub - 1) - pbase);
 #pragma unroll
-        for (int sb0 = 0; sb0 < NSUB; sb0 += NBUF) {
-            if (sb0 >= nsub) break;
+            for (int i = 0; i < 4; ++i) {
+                const int key = kb + 8 * i + (lane >> 3);
+                gather16_at(Kp, (uint32_t)(key < lim ? key : lim) * D + (pc ^ (uint32_t)((i & 1) << 4)),
+                            ring0 + (uint32_t)((t % NBL) * RING16 * 16 + i * 1024));
+            }
+            if (!(t & 1)) {
+                const int t0 = t < nsub ? t : nsub - 2;
+                const int key = (int)(sbase(t0 + (lane >> 5)) - pbase) + (lane & 31);
+                gather4_at(Ksp, (uint32_t)(key < lim ? key : lim) * 4, psc0 + (uint32_t)(((t >> 1) & 1) * 256));
+            }
+        };
+        // Loads issued after sub-block sb's keys when it is awaited: its
+        // pair's scales if sb is even, and sub-blocks sb + 1 .. sb + NBL - 1.
+        static_assert(NBL <= 3, "a pair slot is refilled after the pair's scale is read");
+        constexpr int CNT_EVEN = 1 + 4 * (NBL - 1) + (NBL - 1) / 2;
+        constexpr int CNT_ODD = 4 * (NBL - 1) + NBL / 2;
+        constexpr int CNT_PRO = 4 * (NBL - 1) + NBL / 2;  // the ring's first NBL - 1 sub-blocks
+
+        // Head weights (wavefront 0) and the query (16 KB, into the score
+        // area, which is not scored into before every wavefront holds its
+        // fragments) first, then the ring's first sub-blocks. Query row h is
+        // 16 pieces of 16 B, logical piece j at position j ^ (h % 16).
+        if (wid == 0) gather4_at(uniform_ptr(W + r * H), (uint32_t)lane * 4, __builtin_amdgcn_readfirstlane(lds_addr(sm.wl)));
+        const uint16_t *const Qr = uniform_ptr(Q + r * H * D);
 #pragma unroll
-            for (int i = 0; i < NBUF; ++i) {
-                const int sb = sb0 + i;
-                const int nx = sb + NBUF - 1 < nsub ? sb + NBUF - 1 : nsub - 1;
-                load_sub<KFP8>(buf[(i + NBUF - 1) % NBUF], Kr, Ksr, sbase(nx), L, lane);
-                if (sb < nsub) {
-                    if (!(i & 1)) pscale = buf[i].scale;
-                    const float part = score_sub<KFP8>(buf[i], qa, sm.wl, lane);
-                    if (i & 1) {
-                        // lanes 0..31 finish the pair's first sub-block,
-                        // lanes 32..63 its second
-                        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(prev),
-                                                                         __float_as_uint(part), false, false);
-                        float sc = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-                        if (KFP8) sc *= lane < 32 ? pscale : buf[i].scale;
-                        const long long key = sbase(lane < 32 ? sb - 1 : sb) + (lane & 31);
-                        const uint32_t ok = ord_key(canon(sc));
-                        sm.sc[scx((int)(key - pbase))] = key < Lend ? ok : 0u;
-                        if (key < Lend && ok != 0u) atomicAdd(&sm.hist[hidx(ok >> HSHIFT)], 1u);
-                    } else {
-                        prev = part;
-                    }
+        for (int j = 0; j < 2; ++j) {
+            const int pos = j * THREADS + wid * 64 + lane, h = pos >> 4;
+            gather16_at(Qr, (uint32_t)(h * 256 + (((lane & 15) ^ (h & 15)) << 4)),
+                        __builtin_amdgcn_readfirstlane(lds_addr(sm.area + (j * THREADS + wid * 64) * 16)));
+        }
+        if (nsub > 0) {
+#pragma unroll
+            for (int t = 0; t < NBL - 1; ++t) issue(t);
+            wait_vm<CNT_PRO>();
+        } else {
+            wait_vm<0>();
+        }
+        __syncthreads();
+        bf16x8 qf[2][8];
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) {
+                const int h = hb * 32 + (lane & 31), j = (lane >> 5) * 8 + ks;
+                qf[hb][ks] = *reinterpret_cast<const bf16x8 *>(sm.area + h * 256 + ((j ^ (h & 15)) << 4));
+            }
+        __syncthreads();
+
+        if (nsub > 0) {
+            const int c = lane & 31, h4 = (lane >> 5) << 2;
+            int ro[4];  // this lane's fragment pieces within a slot
+#pragma unroll
+            for (int j = 0; j < 4; ++j) ro[j] = 8 * c + ((h4 + j) ^ ring_swz(c));
+            const uint4 *const rs = reinterpret_cast<const uint4 *>(rbytes) + wid * NBL * RING16;
+            // Fully unrolled in pairs (nsub is even): slot and wait counts
+            // are constants.
+#pragma unroll
+            for (int sb0 = 0; sb0 < NSUB; sb0 += 2) {
+                if (sb0 >= nsub) continue;
+                float part[2];
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const int sb = sb0 + i;
+                    // the slot refilled now was last read one iteration ago
+                    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+                    issue(sb + NBL - 1);
+                    if (i) wait_vm<CNT_ODD>();
+                    else wait_vm<CNT_EVEN>();
+                    Raw<true> rw;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) rw.v[j] = rs[(sb % NBL) * RING16 + ro[j]];
+                    part[i] = score_sub_q(rw, qf, sm.wl, lane);
                 }
+                const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0]), __float_as_uint(part[1]),
+                                                                 false, false);
+                store_pair(sb0 + 1,
+                           (__uint_as_float(sw[0]) + __uint_as_float(sw[1])) * pscl[((sb0 >> 1) & 1) * 64 + lane]);
+            }
+            wait_vm<0>();  // the reloads past the last sub-block: nothing may land in the area later
+        }
+    } else {
+        // ---- bf16 keys: a ring of two sub-blocks in registers, loaded in
+        // the MFMA layout before the query staging below, so the key stream
+        // starts at once; the query's A operands are read from LDS.
+        constexpr int NBUF = 2;
+        static_assert(sc_words(PART) * 4 + H * QROW * 2 <= SCORE_BYTES, "scoring area");
+        uint16_t *const qs = reinterpret_cast<uint16_t *>(sm.area + sc_words(PART) * 4);
+        const uint8_t *Kr = K + (size_t)k0 * 2 * D;
+        Raw<false> buf[NBUF];
+        if (nsub > 0) load_sub_bf16(buf[0], Kr, sbase(0), L, lane);
+        // The row's query (H x D bf16, 16 KB) into LDS: thread t copies two
+        // 16-byte pieces, 16 per head row.
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int piece = tid + THREADS * j;  // 0 .. H * D / 8 - 1
+            const int h = piece >> 4, d8 = piece & 15;
+            *reinterpret_cast<uint4 *>(&qs[h * QROW + d8 * 8]) =
+                *reinterpret_cast<const uint4 *>(Q + (r * H + h) * D + d8 * 8);
+        }
+        if (tid < H) sm.wl[tid] = W[r * H + tid];
+        __syncthreads();
+        if (nsub > 0) {
+            // A operands: head hb * 32 + lane % 32, dims (lane / 32) * 64 + ks * 8.
+            const uint16_t *qa = &qs[(lane & 31) * QROW + (lane >> 5) * 64];
+            float prev = 0.0f;
+            for (int sb = 0; sb < nsub; sb += 2) {
+                load_sub_bf16(buf[1], Kr, sbase(sb + 1), L, lane);
+                prev = score_sub<false>(buf[0], qa, sm.wl, lane);
+                load_sub_bf16(buf[0], Kr, sbase(sb + 2 < nsub ? sb + 2 : nsub - 1), L, lane);
+                const float part = score_sub<false>(buf[1], qa, sm.wl, lane);
+                const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(prev), __float_as_uint(part), false,
+                                                                 false);
+                store_pair(sb + 1, __uint_as_float(sw[0]) + __uint_as_float(sw[1]));
             }
         }
     }
     // Rounds this wavefront did not score (a partial partition reads its
     // rounds in order, so they are the last ones) hold no key.
-    for (int i = nsub + (lane >> 5); i < NROUND; i += 2) sm.sc[scx(i * RKEYS + wid * 32 + (lane & 31))] = 0u;
+    for (int i = nsub + (lane >> 5); i < NROUND; i += 2) sc[scx(i * RKEYS + wid * 32 + (lane & 31))] = 0u;
     __syncthreads();
     // From here on thread t holds the keys of indices pbase + KPT t .. +KPT-1.
     constexpr int KPT = PART / THREADS;  // 16, 24 or 32
     uint32_t u[KPT];
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) u[j] = sm.sc[scx(KPT * tid + j)];
+    for (int j = 0; j < KPT; ++j) u[j] = sc[scx(KPT * tid + j)];
     const long long ibase = pbase + (long long)KPT * tid;
 
     // ---- bins of the partition's k-th, m-th and c1-th largest keys. The
