@@ -105,8 +105,10 @@ struct SplitSmem {
             int idx[MSURV];
         } sv;
         struct {
-            uint64_t full[MAX_SLOTS];    // partition lists, compacted before
-            uint64_t shortl[MAX_SLOTS];  // coalesced stores
+            // partition lists, compacted before coalesced stores; the last 64
+            // entries of each are per-lane trash slots (branch-free writes)
+            uint64_t full[MAX_SLOTS + 64];
+            uint64_t shortl[MAX_SLOTS + 64];
         } st;
         struct {
             // the planned partitioning of a ragged batch (plan_block only)
@@ -884,18 +886,27 @@ __global__ __launch_bounds__(THREADS, 1) void split_indexer_kernel(
     uint32_t tf;
     const uint32_t exfs = block_excl_scan(cf | (cs << 16), sm, tf);  // counts < 2^14
     // The counts are exact, so positions stay below F <= slots and n1 <= s1.
+    // Every key is written, those not in a list to this lane's trash slot:
+    // with no branch per key, the compiler does not move the writes out of
+    // line into blocks at the far end of the kernel's code.
     const uint32_t ib = (uint32_t)ibase;
     if (direct) {
         uint32_t pf = exfs & 0xffffu;
 #pragma unroll
-        for (int j = 0; j < KPT; ++j)
-            if (u[j] >= edge) sm.st.full[pf++] = ((uint64_t)(ib + j) << 32) | u[j];
+        for (int j = 0; j < KPT; ++j) {
+            const bool in = u[j] >= edge;
+            sm.st.full[in ? pf : (uint32_t)(MAX_SLOTS + lane)] = ((uint64_t)(ib + j) << 32) | u[j];
+            pf += in ? 1u : 0u;
+        }
     }
     if (short_ok) {
         uint32_t ps = exfs >> 16;
 #pragma unroll
-        for (int j = 0; j < KPT; ++j)
-            if (u[j] >= edge1) sm.st.shortl[ps++] = ((uint64_t)(ib + j) << 32) | u[j];
+        for (int j = 0; j < KPT; ++j) {
+            const bool in = u[j] >= edge1;
+            sm.st.shortl[in ? ps : (uint32_t)(MAX_SLOTS + lane)] = ((uint64_t)(ib + j) << 32) | u[j];
+            ps += in ? 1u : 0u;
+        }
     }
     __syncthreads();
     if (direct)
