@@ -267,29 +267,27 @@ __device__ __forceinline__ uint32_t hist_find(SplitSmem &sm, const uint32_t (&tg
 
 // One wavefront: the r-th largest (1-based, r <= n) of the n <= 64 keys in
 // sm.lk, and how many of them are strictly larger. Wave-uniform results.
+// Lane i counts the keys above and at or above its own, one broadcast key
+// per step (n steps; the bins ranked here hold a few keys); key i is the
+// r-th largest iff fewer than r keys exceed it and at least r reach it.
+// A bit-serial radix over the keys' differing bits took ~1 us for a
+// three-key bin, its ~24 ballot steps being one long dependency chain.
 __device__ __forceinline__ void list_rank(const SplitSmem &sm, uint32_t n, uint32_t r, uint32_t &kth,
                                           uint32_t &gt_out)
 {
-    // Bit by bit from the highest bit in which the keys differ: among the
-    // keys that match the bits chosen so far, those with the next bit set are
-    // the larger; one ballot counts them.
     const int lane = threadIdx.x & 63;
     const bool live = lane < (int)n;
     const uint32_t mine = live ? sm.lk[lane] : 0u;
-    const uint32_t a = wave_and(live ? mine : ~0u), o = wave_or(mine);
-    const uint32_t diff = a ^ o;
-    const int hb = diff ? 31 - __builtin_clz(diff) : -1;
-    const uint32_t low = hb < 0 ? 0u : (hb == 31 ? ~0u : (2u << hb) - 1u);  // bits still open
-    uint32_t prefix = a & ~low, pmask = ~low, rem = r;
-    for (int b = hb; b >= 0; --b) {
-        const uint32_t bit = 1u << b;
-        const uint32_t c = (uint32_t)__builtin_popcountll(wave_ballot(live && (mine & pmask) == prefix && (mine & bit)));
-        if (c >= rem) prefix |= bit;
-        else rem -= c;
-        pmask |= bit;
+    uint32_t gt = 0, ge = 0;
+    for (int j = 0; j < (int)n; ++j) {
+        const uint32_t kj = (uint32_t)__builtin_amdgcn_readlane((int)mine, j);
+        gt += kj > mine ? 1u : 0u;
+        ge += kj >= mine ? 1u : 0u;
     }
-    kth = prefix;
-    gt_out = (uint32_t)__builtin_popcountll(wave_ballot(live && mine > prefix));
+    const uint64_t m = wave_ballot(live && gt < r && r <= ge);
+    const int src = m ? __builtin_ctzll(m) : 0;
+    kth = (uint32_t)__builtin_amdgcn_readlane((int)mine, src);
+    gt_out = (uint32_t)__builtin_amdgcn_readlane((int)gt, src);
 }
 
 // Appends the calling wavefront's keys that satisfy `in` to sm.lk (order
