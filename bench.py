@@ -38,6 +38,7 @@ core count, CPU model and a one-thread rate.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import os
 import sys
@@ -153,6 +154,21 @@ def _to_device(wl, dev):
         return t.to(dev)
     ks = None if wl.k_scale is None else torch.from_numpy(wl.k_scale).to(dev)
     return cv(wl.q, wl.q_dtype), cv(wl.k, wl.k_dtype), ks, torch.from_numpy(wl.w).to(dev)
+
+
+def _probe_lib():
+    """The ceiling probes' own library (outside the indexer's C ABI), or None
+    if it was not built."""
+    plib = os.path.join(os.path.dirname(CSRC), "libds4probe.so")
+    if not os.path.exists(plib):
+        return None
+    probe = ctypes.CDLL(plib)
+    probe.ds4probe_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_longlong, ctypes.c_void_p, ctypes.c_int,
+                                        ctypes.c_void_p]
+    probe.ds4probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    probe.ds4probe_gather.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_longlong, ctypes.c_void_p,
+                                      ctypes.c_longlong, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    return probe
 
 
 def _time_calls(call, n: int, stream, warm_ms: float = 30.0):
@@ -440,6 +456,28 @@ def main():
         nsel = int((at.idx >= 0).sum())
         aflop = 2 * 64 * nsel * (at.q.shape[-1] + at.d_v)
         amed = aus[len(aus) // 2]
+        row_bytes = at.q.shape[-1] * 2  # the gathered key rows (576 bf16; values are their first 512)
+        # The gather probe: the same selected rows of the same cache, read
+        # into registers with nothing else done (1024 workgroups, four rows
+        # in flight per wavefront): what this GPU sustains on this gather.
+        gprobe = _probe_lib()
+        gather = {}
+        if gprobe is not None:
+            gsink = torch.empty(1024 * 512, dtype=torch.int32, device=dev)
+            gst = ctypes.c_void_p(stream.cuda_stream)
+            nidx = int(aidx.numel())
+
+            def gpstep(i):
+                st = gprobe.ds4probe_gather(akv.data_ptr(), row_bytes, int(akv.shape[-2]), aidx.data_ptr(), nidx,
+                                            gsink.data_ptr(), 1024, gst)
+                assert st == 0, st
+
+            gus = _time_calls(gpstep, 20, stream, args.warm_ms)
+            gpmed = gus[len(gus) // 2]
+            gp_rate = nsel * row_bytes / (gpmed * 1e-6) / 1e9
+            gather = {"gather_probe_us": round(gpmed, 2), "gather_probe_GB_s": round(gp_rate, 1),
+                      "gather_frac": round(nsel * row_bytes / (amed * 1e-6) / 1e9 / gp_rate, 4)}
+            del gsink
         extra["sparse_attention_4096"] = {
             "workload": "4096 queries x 64 heads, 512 selected rows each of a 65536-row bf16 latent cache "
                         "(key 576, value 512), bf16 out + fp32 lse",
@@ -447,7 +485,7 @@ def main():
             "query_tok_s": round(4096 / (amed * 1e-6), 1), "flop": aflop,
             "tflops": round(aflop / (amed * 1e-6) / 1e12, 1),
             "mfma_frac": round(aflop / (amed * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4),
-            "gathered_GB_s": round(nsel * at.q.shape[-1] * 2 / (amed * 1e-6) / 1e9, 1),
+            "gathered_GB_s": round(nsel * row_bytes / (amed * 1e-6) / 1e9, 1), **gather,
             "traffic": measured_traffic("sparse_attention_4096_traffic.txt", "sparse_attention.hip")}
         del aq, akv, aidx, aout
 
@@ -547,14 +585,8 @@ def main():
         # rotated bytes (256 x 512 threads, four 16-byte loads in flight per
         # lane) and back-to-back 32x32x16 bf16 MFMAs (four chains per
         # wavefront, two wavefronts per SIMD).
-        probe = None
-        plib = os.path.join(os.path.dirname(CSRC), "libds4probe.so")
-        if os.path.exists(plib):
-            import ctypes
-            probe = ctypes.CDLL(plib)
-            probe.ds4probe_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_longlong, ctypes.c_void_p, ctypes.c_int,
-                                                ctypes.c_void_p]
-            probe.ds4probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+        probe = _probe_lib()
+        if probe is not None:
             sink = torch.empty(256 * 512, dtype=torch.int32, device=dev)
             sst = ctypes.c_void_p(stream.cuda_stream)
 

@@ -1,12 +1,17 @@
 // Measurement probes, kept out of the indexer's C ABI (their own library,
 // loaded by the benchmark only): what this GPU sustains on a plain read of
-// device memory and on back-to-back matrix-core instructions, as measured
-// ceilings beside the datasheet peaks the kernels' roofline fractions use.
+// device memory, on a gather of scattered rows and on back-to-back
+// matrix-core instructions, as measured ceilings beside the datasheet peaks
+// the kernels' roofline fractions use.
 #include <hip/hip_runtime.h>
+
+#include "device_common.h"
 
 #include <cstdint>
 
 namespace {
+
+using namespace ds4idx;
 
 // Every 16-byte word of p read once, grid-stride, four loads in flight per
 // lane; each thread XOR-folds what it read into sink[thread], so no load can
@@ -27,6 +32,55 @@ __global__ __launch_bounds__(512) void read_kernel(const uint4 *__restrict__ p, 
         acc ^= a.x ^ a.y ^ a.z ^ a.w;
     }
     sink[t] = acc;
+}
+
+// rows[idx[i]] (row16 16-byte pieces, at most 128) for every i < n with
+// 0 <= idx[i] < nrows, gathered the way the sparse attention gathers its
+// rows: straight into LDS (global_load_lds_dwordx4), one instruction per
+// 1 KB of a row, from a wavefront-uniform row base. Block b takes the
+// indices [b n / grid, (b + 1) n / grid); each wavefront loads 64 of them at
+// once (one per lane) and gathers their rows eight at a time into its own
+// LDS slots, then reads its pieces back and XOR-folds them into
+// sink[thread], so every gathered word is counted once.
+constexpr int GROWS = 8;  // rows in flight per wavefront
+__global__ __launch_bounds__(512) void gather_kernel(const uint4 *__restrict__ rows, int row16, long long nrows,
+                                                     const int *__restrict__ idx, long long n,
+                                                     uint32_t *__restrict__ sink)
+{
+    __shared__ uint4 slot[8][GROWS][128];
+    const long long lo = (long long)blockIdx.x * n / gridDim.x, hi = (long long)(blockIdx.x + 1) * n / gridDim.x;
+    const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    uint32_t acc = 0;
+    for (long long g0 = lo + 64 * wid; g0 < hi; g0 += 64 * 8) {
+        const int mine = g0 + lane < hi ? idx[g0 + lane] : -1;
+        const int cnt = hi - g0 < 64 ? (int)(hi - g0) : 64;
+        for (int u = 0; u < cnt; u += GROWS) {
+            bool okj[GROWS];
+#pragma unroll
+            for (int j = 0; j < GROWS; ++j) {
+                const int r = u + j < cnt ? __builtin_amdgcn_readlane(mine, u + j) : -1;
+                okj[j] = r >= 0 && r < nrows;
+                if (okj[j]) {
+                    const uint4 *rb = uniform_ptr(rows + (long long)r * row16);
+                    const uint32_t l0 = __builtin_amdgcn_readfirstlane(lds_addr(&slot[wid][j][0]));
+                    if (lane < row16) gather16_at(rb, (uint32_t)lane * 16, l0);
+                    if (64 + lane < row16) gather16_at(rb, (uint32_t)(64 + lane) * 16, l0 + 1024);
+                }
+            }
+            wait_vm<0>();
+#pragma unroll
+            for (int j = 0; j < GROWS; ++j) {
+                if (okj[j]) {
+                    uint4 a = lane < row16 ? slot[wid][j][lane] : make_uint4(0, 0, 0, 0);
+                    uint4 c = 64 + lane < row16 ? slot[wid][j][64 + lane] : make_uint4(0, 0, 0, 0);
+                    acc ^= a.x ^ a.y ^ a.z ^ a.w ^ c.x ^ c.y ^ c.z ^ c.w;
+                }
+            }
+            // the slots are refilled only after these reads
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        }
+    }
+    sink[blockIdx.x * blockDim.x + threadIdx.x] = acc;
 }
 
 typedef __attribute__((__vector_size__(8 * sizeof(short)))) short bf16x8;
@@ -69,6 +123,21 @@ int ds4probe_hbm_read(const void *buf, long long bytes, uint32_t *sink, int bloc
         return (int)hipErrorInvalidValue;
     hipLaunchKernelGGL(read_kernel, dim3(blocks), dim3(512), 0, static_cast<hipStream_t>(stream),
                        static_cast<const uint4 *>(buf), bytes / 16, sink);
+    return (int)hipGetLastError();
+}
+
+// Gathers rows[idx[i]] (row_bytes each: a multiple of 16, at most 2048;
+// rows 16-byte aligned) for the n indices at idx, skipping those outside
+// [0, nrows), with `blocks` workgroups of 512 threads; sink holds
+// blocks * 512 words. Returns a hipError_t value (0 = launched).
+int ds4probe_gather(const void *rows, int row_bytes, long long nrows, const int *idx, long long n, uint32_t *sink,
+                    int blocks, void *stream)
+{
+    if (!rows || !idx || !sink || row_bytes < 16 || row_bytes > 2048 || (row_bytes & 15) || ((uintptr_t)rows & 15) ||
+        nrows < 1 || n < 1 || blocks < 1)
+        return (int)hipErrorInvalidValue;
+    hipLaunchKernelGGL(gather_kernel, dim3(blocks), dim3(512), 0, static_cast<hipStream_t>(stream),
+                       static_cast<const uint4 *>(rows), row_bytes / 16, nrows, idx, n, sink);
     return (int)hipGetLastError();
 }
 

@@ -65,14 +65,21 @@ def test_digest_ignores_comments_and_layout_only():
     assert bench._code_only(src) != bench._code_only(literal)   # inside a literal, text counts
 
 
-def test_probe_library_exports_its_two_kernels():
+def test_probe_library_exports_its_kernels():
     # the ceiling probes bench.py times live in their own library, outside
     # the indexer's C ABI
     import ctypes
     path = os.path.join(ROOT, "sparse_attention_token_lightning_amd", "libds4probe.so")
     assert os.path.exists(path), "built by __graft_entry__.build()"
     lib = ctypes.CDLL(path)
-    assert hasattr(lib, "ds4probe_hbm_read") and hasattr(lib, "ds4probe_mfma")
+    assert hasattr(lib, "ds4probe_hbm_read") and hasattr(lib, "ds4probe_mfma") and hasattr(lib, "ds4probe_gather")
+    lib.ds4probe_gather.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_longlong, ctypes.c_void_p,
+                                    ctypes.c_longlong, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    ok = (ctypes.c_void_p(0x1000), 1152, 10, ctypes.c_void_p(0x2000), 5, ctypes.c_void_p(0x3000), 1, None)
+    for i, bad in [(1, 1000), (1, 4096), (2, 0), (4, 0), (6, 0), (0, None), (0, ctypes.c_void_p(0x1008))]:
+        args = list(ok)
+        args[i] = bad
+        assert lib.ds4probe_gather(*args) != 0, (i, bad)
     # argument checks come before any HIP call
     lib.ds4probe_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_longlong, ctypes.c_void_p, ctypes.c_int,
                                       ctypes.c_void_p]
