@@ -1057,33 +1057,24 @@ __global__ __launch_bounds__(THREADS, 1) void split_indexer_kernel(
 
     uint32_t m_out;
     if (use_short && G1 <= NW * GB) {
-        // Select straight from the loaded short lists, transposed through
-        // LDS so that thread t owns slots 16t .. 16t+15 (index order). Every
-        // key in play lies in [bound, row maximum], so they share the bits
-        // above the highest bit in which those two differ: the 12 bits below
-        // it are the first digit, with no reduction pass.
-        const int nslot = G1 * 64;
-#pragma unroll
-        for (int i = 0; i < GB; ++i) {
-            const int g = wid + NW * i;
-            if (g < G1) {
-                const uint32_t key = (uint32_t)v0[i];
-                sm.sv.key[scx(g * 64 + lane)] = key >= bound ? key : 0u;
-                sm.sv.idx[g * 64 + lane] = (int)(v0[i] >> 32);
-            }
-        }
-        __syncthreads();
-        constexpr int KPT = MSURV / THREADS;  // 16 slots per thread
-        uint32_t kk[KPT];
-#pragma unroll
-        for (int j = 0; j < KPT; ++j) kk[j] = KPT * tid + j < nslot ? sm.sv.key[KPT * tid + tid + j] : 0u;
+        // Select straight from the loaded short lists, in the order they
+        // were loaded: thread t holds slots 512 i + t (i < GB), so chunk
+        // (i, wavefront) holds slots 512 i + 64 w .. +63, and chunks taken in
+        // (i, w) order run through the slots in index order. Every key in play
+        // lies in [bound, row maximum], so they share the bits above the
+        // highest bit in which those two differ: the 12 bits below it are the
+        // first digit, with no reduction pass.
         const int hb = 31 - __builtin_clz((bound ^ kmax_row) | 1u);
         const int lo = hb >= HBITS - 1 ? hb - (HBITS - 1) : 0;
         const uint32_t dmask = (2u << (hb - lo)) - 1u;
         const uint32_t prefix = hb == 31 ? 0u : (bound & (~0u << (hb + 1)));
+        uint32_t kk[GB];  // slots past the lists were loaded as 0 (no key)
 #pragma unroll
-        for (int j = 0; j < KPT; ++j)
-            if (kk[j] != 0u) atomicAdd(&sm.hist[hidx((kk[j] >> lo) & dmask)], 1u);
+        for (int i = 0; i < GB; ++i) {
+            const uint32_t key = (uint32_t)v0[i];
+            kk[i] = key >= bound ? key : 0u;
+            if (kk[i] != 0u) atomicAdd(&sm.hist[hidx((kk[i] >> lo) & dmask)], 1u);
+        }
         __syncthreads();
         Found fd[1];
         const uint32_t total = hist_find<1>(sm, {(uint32_t)topk}, fd);
@@ -1097,12 +1088,12 @@ __global__ __launch_bounds__(THREADS, 1) void split_indexer_kernel(
             } else if (f.cnt <= (uint32_t)NLIST) {
                 uint32_t cm = 0;
 #pragma unroll
-                for (int j = 0; j < KPT; ++j) cm += (kk[j] != 0u && ((kk[j] >> lo) & dmask) == f.bin) ? 1u : 0u;
+                for (int i = 0; i < GB; ++i) cm += (kk[i] != 0u && ((kk[i] >> lo) & dmask) == f.bin) ? 1u : 0u;
                 if (cm != 0u) {
                     uint32_t pm = atomicAdd(&sm.nl, cm);
 #pragma unroll
-                    for (int j = 0; j < KPT; ++j)
-                        if (kk[j] != 0u && ((kk[j] >> lo) & dmask) == f.bin) sm.lk[pm++] = kk[j];
+                    for (int i = 0; i < GB; ++i)
+                        if (kk[i] != 0u && ((kk[i] >> lo) & dmask) == f.bin) sm.lk[pm++] = kk[i];
                 }
                 __syncthreads();
                 if (wid == 0) {
@@ -1120,33 +1111,41 @@ __global__ __launch_bounds__(THREADS, 1) void split_indexer_kernel(
                 block_kth(
                     [&](auto fn) {
 #pragma unroll
-                        for (int j = 0; j < KPT; ++j)
-                            if (kk[j] != 0u) fn(kk[j]);
+                        for (int i = 0; i < GB; ++i)
+                            if (kk[i] != 0u) fn(kk[i]);
                     },
                     (uint32_t)topk, sm, tau, ties);
             }
         }
-        // Ordered output: each thread's kept keys at their places in the row.
-        uint32_t ngt = 0, neq = 0;
+        // Ordered output. Each chunk counts its keys above tau and equal to
+        // it (ballots); every wavefront scans the 128 chunk counts itself, so
+        // one barrier serves. A key's place is the keys above tau before it
+        // plus the ties before it, capped at the ties kept (the lowest
+        // indices); the stores come straight from the loaded lists.
+        uint32_t mycnt = 0;
 #pragma unroll
-        for (int j = 0; j < KPT; ++j) {
-            ngt += kk[j] > tau ? 1u : 0u;
-            neq += (kk[j] != 0u && kk[j] == tau) ? 1u : 0u;
+        for (int i = 0; i < GB; ++i) {
+            const uint32_t ng = (uint32_t)__builtin_popcountll(wave_ballot(kk[i] > tau));
+            const uint32_t ne = (uint32_t)__builtin_popcountll(wave_ballot(kk[i] != 0u && kk[i] == tau));
+            mycnt = lane == i ? ng | (ne << 16) : mycnt;  // counts <= 64
         }
-        uint32_t tot;
-        const uint32_t ex = block_excl_scan(ngt | (neq << 16), sm, tot);  // counts < 2^14
-        uint32_t eqb = ex >> 16;
-        uint32_t pos = (ex & 0xffffu) + (eqb < ties ? eqb : ties);
-        // Written in place: consecutive threads hold consecutive positions,
-        // so each store instruction covers a short run of the row.
+        if (lane < GB) sm.gcnt[NW * lane + wid] = mycnt;
+        __syncthreads();
+        // lane l: chunks 2l and 2l + 1, i.e. (i, w) = (l / 4, 2 (l % 4)) and the next
+        const uint32_t c0 = sm.gcnt[2 * lane], c1 = sm.gcnt[2 * lane + 1];
+        const uint32_t inc = wave_scan_incl(c0 + c1, 0u, OpAdd{});  // packed: each half < 2^14
+        const uint32_t ex0 = inc - c0 - c1, ex1 = inc - c1;
 #pragma unroll
-        for (int j = 0; j < KPT; ++j) {
-            bool keep = kk[j] > tau;
-            if (kk[j] != 0u && kk[j] == tau) keep = eqb++ < ties;
-            if (keep) {
-                io[pos] = sm.sv.idx[KPT * tid + j];
-                if (vo) vo[pos] = key_float(kk[j]);
-                ++pos;
+        for (int i = 0; i < GB; ++i) {
+            const int e = NW * i + wid;  // this wavefront's chunk of slot row i
+            const uint32_t base = (uint32_t)__builtin_amdgcn_readlane((int)((e & 1) ? ex1 : ex0), e >> 1);
+            const bool gt = kk[i] > tau, eq = kk[i] != 0u && kk[i] == tau;
+            const uint32_t gb = (base & 0xffffu) + lanes_below(wave_ballot(gt));
+            const uint32_t eb = (base >> 16) + lanes_below(wave_ballot(eq));
+            if (gt || (eq && eb < ties)) {
+                const uint32_t pos = gb + (eb < ties ? eb : ties);
+                io[pos] = (int)(v0[i] >> 32);
+                if (vo) vo[pos] = key_float(kk[i]);
             }
         }
         m_out = total < (uint32_t)topk ? total : (uint32_t)topk;
