@@ -32,10 +32,12 @@
 //  * Streaming top-k per token. A candidate buffer of CAP (score, index)
 //    slots per token lives in LDS. A score enters only if it reaches the
 //    token's running threshold (ballot + mbcnt place it in ascending key
-//    order). When the buffer is nearly full, the wavefront raises the
-//    threshold to the highest 8-bit histogram edge that keeps k entries at
-//    or above it, and compacts the buffer stably; nothing that can still
-//    reach the top k is dropped. If that frees too little, the exact k-th
+//    order). At a tile's end, when some token's buffer is nearly full, every
+//    wavefront whose buffer holds more than RAISE_LO entries raises its
+//    threshold, all in the same tile, so the workgroup stalls at one barrier
+//    for all of them: to the highest 8-bit histogram edge that keeps k
+//    entries at or above it, compacting the buffer stably; nothing that can
+//    still reach the top k is dropped. If that frees too little, the exact k-th
 //    key is found by radix selection and the buffer cut to exactly k
 //    entries; later keys, all with higher indices, must then beat it
 //    strictly, so equal scores keep going to the lower index. At the end the
@@ -58,6 +60,12 @@ constexpr int TQ = NWAVE;
 constexpr int KT = 128;     // keys per LDS tile
 constexpr int KROW = D + 8; // bf16 per LDS key row: 272 B keeps 16-byte reads conflict-free
 constexpr int CAP = 1280;   // candidate slots per token
+// A tile adds at most 2 pairs (128 entries) to a buffer between two tile
+// ends: a raise is called for above RAISE_HI, and every buffer above
+// RAISE_LO (> k, so a raise is possible) takes part.
+constexpr int RAISE_HI = CAP - 64 - 128;
+constexpr int RAISE_LO = 768;
+static_assert(kMfmaMaxK < RAISE_LO && RAISE_LO < RAISE_HI, "a raise keeps k of more than k entries");
 constexpr int THREADS = NWAVE * 64;
 
 typedef __attribute__((__vector_size__(8 * sizeof(short)))) short bf16x8;
@@ -72,6 +80,7 @@ struct alignas(16) Smem {
     float cs[TQ][CAP];
     int ci[TQ][CAP];
     uint32_t hist[NWAVE][256];
+    alignas(8) uint8_t rneed[2][NWAVE];  // per tile parity: this wavefront's buffer is above RAISE_HI
     int last;  // split parts: this block arrived last for its 8 tokens
 };
 
@@ -580,21 +589,22 @@ __global__ __launch_bounds__(THREADS, 1) void mfma_indexer_kernel(
                     cs[pos] = sc;
                     ci[pos] = (int)key;
                 }
-                cnt += __builtin_popcountll(m);
-                if (cnt > CAP - 64) {
-                    wave_lds_sync();
-                    uint32_t edge = 0;
-                    const int kept = wave_raise_threshold(cs, ci, cnt, topk, sm.hist[wid], lane, edge);
-                    if (kept <= CAP - 256) {
-                        cnt = kept;
-                        thr = key_float(edge);
-                    } else {  // too little freed: exact k-th, admit strictly above it
-                        const float kth = wave_keep_topk(cs, ci, kept, topk, sm.hist[wid], lane);
-                        cnt = topk;
-                        thr = key_float(ord_key(kth) + 1u);
-                    }
-                }
+                cnt += __builtin_popcountll(m);  // at most RAISE_HI + 128 <= CAP (see the tile loop)
             }
+        }
+    };
+    // Raise this token's threshold (cnt > RAISE_LO > topk entries).
+    auto raise_now = [&]() {
+        wave_lds_sync();
+        uint32_t edge = 0;
+        const int kept = wave_raise_threshold(cs, ci, cnt, topk, sm.hist[wid], lane, edge);
+        if (kept < cnt && kept <= CAP - 256) {
+            cnt = kept;
+            thr = key_float(edge);
+        } else {  // too little freed (or all entries equal): exact k-th, admit strictly above it
+            const float kth = wave_keep_topk(cs, ci, kept, topk, sm.hist[wid], lane);
+            cnt = topk;
+            thr = key_float(ord_key(kth) + 1u);
         }
     };
 
@@ -604,6 +614,7 @@ __global__ __launch_bounds__(THREADS, 1) void mfma_indexer_kernel(
     // barrier: by that finish, other wavefronts may already be staging the
     // tile after next into the same scale buffer.
     float pend_scale = 1.0f;
+    bool raise_pending = false;
     for (int it = 0; it < ntiles; ++it) {
         const int tile = tlo + it;
         const int cur = it & 1;
@@ -613,6 +624,7 @@ __global__ __launch_bounds__(THREADS, 1) void mfma_indexer_kernel(
         for (int pp = 0; pp < KT / 64; ++pp) {
             float h1[2], h0[2];
             phase(0, cur, pp, h1);  // MFMAs of this pair's first half; previous pair's second half reduced
+            if (!SCORE && pp == 0 && raise_pending) raise_now();
             if (pp > 0)
                 finish_pair(prev0, h1, kbase + pp * 64 - 64, KFP8 ? sm.scale[cur][(pp - 1) * 64 + lane] : 1.0f);
             else if (it > 0)
@@ -626,7 +638,18 @@ __global__ __launch_bounds__(THREADS, 1) void mfma_indexer_kernel(
             if constexpr (QFP8) store_tile_raw(sm, cur ^ 1, tr, tsc, tid);
             else store_tile<KFP8>(sm, cur ^ 1, tr, tsc, tid);
         }
+        if (!SCORE && lane == 0) sm.rneed[cur][wid] = cnt > RAISE_HI ? 1 : 0;
         __syncthreads();
+        // Raises are taken together: when some buffer is above RAISE_HI, every
+        // buffer above RAISE_LO is raised in the next tile, after its first
+        // MFMAs are issued and before its first insert. Until the next tile's
+        // end, at most 128 more entries arrive (this tile's last pair and the
+        // next tile's first); after the last tile only its last pair, so a
+        // raise asked for there is not needed. The flags alternate between two
+        // rows, so a wavefront already writing the next tile's cannot
+        // overwrite these.
+        if constexpr (!SCORE)
+            raise_pending = *reinterpret_cast<const uint64_t *>(sm.rneed[cur]) != 0 && cnt > RAISE_LO;
     }
     if (ntiles > 0) {  // the last pair's second half
         float h1[2];
