@@ -291,6 +291,21 @@ def test_split_int_exact():
     compare_rows(wl, np.arange(6), gi, gv, exact=True)
 
 
+@pytest.mark.parametrize("lo,hi,kind", [(-4, 4, "fp8"), (-1, 1, "fp8"), (-1, 1, "bf16")])
+def test_split_int_decode_ties_exact(lo, hi, kind):
+    # Decode shape (one query per stream, 262144 keys: 32 partitions whose
+    # short lists are merged). Integer values make every fp32 sum exact, so
+    # the oracle's indices are the answer bit for bit. Values in [-1, 1] leave
+    # few distinct scores, so the k-th score is shared by many keys spread
+    # over many 64-slot chunks of the merge, and the ties kept must be the
+    # lowest indices.
+    wl = W.int_decode(seed=80 + hi, B=2, S=262144, lo=lo, hi=hi, kind=kind)
+    _say(f"split integer decode ties [{lo}, {hi}] {kind}")
+    gi, gv = run_select(wl, poison=True)
+    check_invariants(wl, gi)
+    compare_rows(wl, np.arange(2), gi, gv, exact=True)
+
+
 @pytest.mark.parametrize("S", [100000, 300000])
 def test_split_all_equal_scores(S):
     # K = 0 on a long cache with few rows (the split-key kernel): every score

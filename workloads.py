@@ -202,6 +202,24 @@ def long_prefill(seed: int = 5, T: int = 2048, S: int = 1048576, H: int = 64, D:
                     [(0, T, S, off)])
 
 
+def int_decode(seed: int = 80, B: int = 2, S: int = 262144, H: int = 64, D: int = 128, topk: int = 512,
+               lo: int = -4, hi: int = 4, kind: str = "fp8", name: str = "int-decode") -> Workload:
+    """One query per stream against S cached keys, with integer values in
+    [lo, hi]: bf16 queries, keys as exact E4M3 codes with scale 1 (kind "fp8")
+    or as bf16, and w in {0.5, 1, 2}, so every fp32 sum is exact. A narrow
+    range leaves few distinct scores: the k-th score is shared by many keys."""
+    gq, gk, gw = _streams(seed, 3)
+    q = to_bf16_bits(_int_uniform(gq, (B, 1, H, D), lo, hi))
+    kv = _int_uniform(gk, (B, S, D), lo, hi)
+    w = _pick_weights(gw, (B, 1, H))
+    if kind == "fp8":
+        codes = torch.from_numpy(kv).to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
+        return Workload(name, q, codes, np.ones((B, S), np.float32), w, B, 1, S, H, D, S - 1, topk, BF16, FP8,
+                        [(0, 1, S, S - 1)], integer_valued=True)
+    return Workload(name, q, to_bf16_bits(kv), None, w, B, 1, S, H, D, S - 1, topk, BF16, BF16,
+                    [(0, 1, S, S - 1)], integer_valued=True)
+
+
 CONFIGS = {
     "tiny": tiny,
     "8k": prefill_bf16,
