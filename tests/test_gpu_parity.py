@@ -395,3 +395,41 @@ def test_split_partition_lengths_identical(keys):
                 compare_rows(wl, np.arange(wl.B * wl.T), gi, gv, exact=False)
     finally:
         ds.set_split(prev)
+
+
+# ------------------------------------------------------------------ randomised shapes
+
+def _random_case(g, case):
+    kind = g.choice(["prefill", "long", "decode", "decode"])
+    kdt = g.choice(["fp8", "bf16", "int"])
+    topk = int(g.choice([1, 5, 64, 100, 257, 512, 512, 1024, 2048]))
+    B = int(g.integers(1, 4))
+    if kind == "prefill":
+        T, offset = int(g.integers(1, 300)), int(g.integers(0, 20000 // B))
+    elif kind == "long":  # long rows: several threshold raises per token
+        T, offset = int(g.integers(1, 40)), int(g.integers(20000, 90000 // B))
+    else:
+        T, offset = int(g.integers(1, 4)), int(g.integers(500, 300000 // B))
+    S, seed = offset + T, 5000 + case
+    if kdt == "fp8":
+        wl = W.prefill_fp8(seed=seed, T=T, S=S, offset=offset, topk=topk, B=B, chunk=T)
+    elif kdt == "bf16":
+        wl = W.prefill_bf16(seed=seed, T=T, S=S, offset=offset, topk=topk, B=B)
+    else:
+        wl = W.prefill_bf16_int(seed=seed, T=T, S=S, offset=offset, topk=topk, B=B)
+    wl.chunks = [(0, T, S, offset)]
+    return wl, f"{kind} {kdt} B={B} T={T} S={S} offset={offset} k={topk} seed={seed}"
+
+
+@pytest.mark.parametrize("group", range(4))
+def test_randomised_shapes(group):
+    # 12 seeded cases per group: prefill-, long-row- and decode-shaped problems
+    # (both hot kernels and every k path), E4M3, bf16 and integer keys; every
+    # row against the oracle (bit for bit on integers).
+    g = np.random.Generator(np.random.PCG64(900 + group))
+    for case in range(12):
+        wl, desc = _random_case(g, 12 * group + case)
+        _say("random", desc)
+        gi, gv = run_select(wl, poison=True)
+        check_invariants(wl, gi)
+        compare_rows(wl, np.arange(wl.B * wl.T), gi, gv, exact=wl.integer_valued)
