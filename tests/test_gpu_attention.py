@@ -192,3 +192,23 @@ def test_many_items_per_workgroup(seed, B, T, S, H, k, pad, sample):
         g = np.random.Generator(np.random.PCG64(seed))
         rows = np.unique(np.concatenate([[0, B * T - 1], g.integers(0, B * T, sample - 2)]))
     check(a, go, glse, rows=rows)
+
+
+@pytest.mark.parametrize("group", range(2))
+def test_randomised_attention(group):
+    # 10 seeded random shapes per group: 1-3 streams, 1-119 queries, 64, 128 or
+    # 192 heads, caches of 40 to 70000 rows, k from 1 to 2048 (odd counts and
+    # ragged last chunks included), with and without padded entries; every row
+    # (or 32 sampled rows with both ends) against the oracle.
+    g = np.random.Generator(np.random.PCG64(800 + group))
+    for case in range(10):
+        B, T, H = int(g.integers(1, 4)), int(g.integers(1, 120)), int(g.choice([64, 128, 192]))
+        S = int(g.integers(40, 70000))
+        topk = min(int(g.choice([1, 17, 32, 33, 64, 96, 97, 128, 500, 512, 2048])), S)
+        pad = float(g.choice([0.0, 0.0, 0.3]))
+        a = W.attention(seed=8100 + 10 * group + case, B=B, T=T, S=S, H=H, topk=topk, pad_frac=pad)
+        _say(f"random attention B={B} T={T} S={S} H={H} k={topk} pad={pad}")
+        go, glse = run_attention(a)
+        rows = None if B * T <= 64 else np.unique(np.concatenate([[0, B * T - 1], g.integers(0, B * T, 30)]))
+        check(a, go, glse, rows=rows)
+

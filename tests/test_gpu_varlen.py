@@ -285,3 +285,28 @@ def test_planned_parts_match_fixed_length(name, mix, topk, seed):
     assert np.array_equal(ai, gi), f"{name}: indices differ from the fixed length"
     assert np.array_equal(av.view(np.uint32), gv.view(np.uint32)), f"{name}: values differ"
     check_against_oracle(rg, ai, av, exact=False, topk=topk, n=4)
+
+
+@pytest.mark.parametrize("group", range(2))
+def test_randomised_ragged_batches(group):
+    # 10 seeded random stream mixes per group: empty streams, single tokens on
+    # long caches and prefill-like streams in one batch; E4M3, bf16 and integer
+    # keys; k from 1 to 2048. Every stream's invariants, and up to 24 rows per
+    # stream against the oracle (bit for bit on integers). (A mixed batch runs
+    # on one kernel for all its streams, so its values can differ from a
+    # single-stream call by fp32 rounding: the oracle is the reference here.)
+    g = np.random.Generator(np.random.PCG64(700 + group))
+    for case in range(10):
+        streams = []
+        for _ in range(int(g.integers(1, 24))):
+            T = int(g.choice([0, 1, 1, 2, int(g.integers(1, 200))]))
+            streams.append((T, T + int(g.integers(0, 90000 if T <= 2 else 30000))))
+        if sum(t for t, _ in streams) == 0:
+            streams[0] = (1, max(1, streams[0][1]))
+        kind = str(g.choice(["fp8", "int", "bf16"]))
+        topk = int(g.choice([1, 64, 300, 512, 512, 2048]))
+        rg = W.ragged(seed=7100 + 10 * group + case, streams=streams, topk=topk, kind=kind)
+        _say(f"random ragged {kind} k={topk} streams={streams}")
+        gi, gv = run_varlen(rg)
+        check_against_oracle(rg, gi, gv, exact=(kind == "int"), n=24)
+
